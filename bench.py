@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the attention layer on one MI355X.
+
+A step is one pass of the whole layer stack of the chosen workload (every
+layer: RMSNorm, Q8_0 quantization, Q/K/V projections, RoPE, KV append,
+split-K GQA attention, O projection + residual) over one token per sequence,
+with every input already resident in HBM. The step is captured once in a HIP
+graph (through torch's CUDA-graph API on the current stream) and replayed; K
+steps are timed with HIP events on that stream. Replicas of the whole stack
+are rotated when one step's bytes would fit the 256 MB last-level cache.
+
+Prints one JSON line: value = achieved GB/s over the algorithmic bytes
+(quantized weight blocks + fp32 K and V of every attended token) of the step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-layer µs/token + achieved HBM GB/s (weights+KV bytes) vs peak"
+PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+DESCRIBE = {
+    "c1": "tiny decode layer: D=256 H=4 KV=2 hd=64, 17 attended tokens, 1 layer",
+    "c2": "Qwen2-0.5B-shaped decode layer: D=896 H=14 KV=2 hd=64, 1025 attended tokens, 24 layers",
+    "c3": "7B-shaped decode layer: D=3584 H=28 KV=4 hd=128, 4097 attended tokens, 28 layers",
+    "c4": "long-context decode layer: D=4096 H=32 KV=8 hd=128, 32769 attended tokens, 1 layer",
+    "c5": "batched paged decode: D=4096 H=32 KV=8 hd=128, m=8, L_s~U[512,8192], pages of 16, 1 layer",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=sorted(DESCRIBE))
+    ap.add_argument("--variant", default="fused", choices=["fused", "chain"])
+    ap.add_argument("--eager", action="store_true", help="launch from Python, no graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle CPU-baseline sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the layer is built and timed on a single MI355X "
+              "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_step_attention_layer_amd import ck, synth
+    from decode_step_attention_layer_amd.workload import DeviceStack
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ck.load()
+    cfg = synth.CONFIGS[args.config]
+    variant = ck.CK_VARIANT_FUSED if args.variant == "fused" else ck.CK_VARIANT_CHAIN
+    t0 = time.time()
+    stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu)
+    log(f"[bench] {args.config}: {stack.nlayers} layers on device in {time.time() - t0:.1f}s")
+    nbytes = synth.algorithmic_bytes(cfg, stack.lens)
+    step_bytes = nbytes["total"] * stack.nlayers
+    replicas = 1
+    if step_bytes < 3 * MALL_BYTES:
+        replicas = min(8, math.ceil(3 * MALL_BYTES / step_bytes))
+    stacks = [stack] + [stack.clone() for _ in range(replicas - 1)]
+    desc = stack.desc(variant)
+    wss = [s.workspace(desc) for s in stacks]
+    stream = torch.cuda.current_stream()
+
+    # ---- eager warm-up (also the reference for the graph replays)
+    for i in range(max(1, args.warmup)):
+        for s, ws in zip(stacks, wss):
+            s.step(desc, ws)
+    torch.cuda.synchronize()
+    ref = stacks[0].bufs[(stack.nlayers - 1) % 2].clone()
+
+    graphs = []
+    if not args.eager:
+        for s, ws in zip(stacks, wss):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s.step(desc, ws)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        out = stacks[0].bufs[(stack.nlayers - 1) % 2]
+        assert torch.equal(out, ref), "graph replay differs from the eager step"
+
+    def run_step(i):
+        if graphs:
+            graphs[i % replicas].replay()
+        else:
+            stacks[i % replicas].step(desc, wss[i % replicas])
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        run_step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_step = ms / args.steps
+    us_layer = ms_step * 1e3 / stack.nlayers
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    out = stacks[0].bufs[(stack.nlayers - 1) % 2]
+    assert torch.isfinite(out).all(), "non-finite layer output"
+    log(f"[bench] step {ms_step * 1e3:.2f} us, {us_layer:.2f} us/layer, {value:.0f} GB/s")
+
+    roof = roofline(args, stack, desc, wss[0], nbytes)
+    cpu = None if args.no_cpu else cpu_baseline(args, stack, nbytes)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-dot/f32",
+        "data": "synthetic (seeded; quantized N(0,0.02) weights, N(0,1) activations and cache)",
+        "config": {
+            "workload": f"{args.config}: {DESCRIBE[args.config]}",
+            "variant": args.variant,
+            "launch": "eager" if args.eager else "hip-graph",
+            "layers": stack.nlayers,
+            "tokens_per_step": cfg.m,
+            "replicas": replicas,
+        },
+        "us_per_layer": round(us_layer, 3),
+        "us_per_token": round(ms_step * 1e3 / cfg.m, 3),
+        "bytes_per_step": step_bytes,
+        "frac_of_peak": round(value / PEAK_GBS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _time_launches(fn, reps):
+    import torch
+
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps     # us per launch
+
+
+def roofline(args, stack, desc, ws, nbytes):
+    """Per-launch timing of the layer's two large steps through their C-ABI
+    entry points on layer 0's data (same stream, same launch configuration as
+    inside the layer): the attention (split-K pass + merge) and the O
+    projection GEMV. The one with the larger share is reported."""
+    import torch
+
+    from decode_step_attention_layer_amd import ck, synth
+
+    cfg = stack.cfg
+    L = stack.layers[0]
+    m, D, H, KV, hd = cfg.m, cfg.D, cfg.H, cfg.KV, cfg.hd
+    off = lambda n: ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, n)
+    base = ws.data_ptr()
+    q, attn, aq = base + off("q"), base + off("attn"), base + off("aq")
+    nws = ck.ck_attn_workspace_size(m, H, KV, hd, stack.max_ctx, desc.attn_chunk)
+    aws = torch.empty(nws, dtype=torch.uint8, device=ws.device)
+    out = torch.empty((m, D), dtype=torch.float32, device=ws.device)
+    scale = 1.0 / math.sqrt(hd)
+
+    attn_us = _time_launches(lambda: ck.ck_attn_decode_gqa(
+        q, L.cache, stack.pos, attn, m, H, scale, desc.attn_chunk, aws, nws), args.kernel_reps)
+    wo_us = _time_launches(lambda: ck.ck_gemv_q5_0_q8_0(
+        L.tensors["wo"], aq, L.tensors["bo"], stack.x0, out, D, H * hd, m), args.kernel_reps)
+    kv_bytes = nbytes["kv"]
+    wo_bytes = D * (H * hd // 32) * synth.Q5_0_BYTES
+    att_gbs = kv_bytes / (attn_us * 1e-6) / 1e9
+    wo_gbs = wo_bytes / (wo_us * 1e-6) / 1e9
+    log(f"[bench] attention {attn_us:.2f} us ({att_gbs:.0f} GB/s), O GEMV {wo_us:.2f} us "
+        f"({wo_gbs:.0f} GB/s)")
+    if attn_us >= wo_us:
+        name, gbs, us, b = "k_attn_partial+k_attn_merge", att_gbs, attn_us, kv_bytes
+    else:
+        name, gbs, us, b = "k_gemv (O projection, Q5_0)", wo_gbs, wo_us, wo_bytes
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_GBS, 4), "traffic": None, "kernel": name,
+            "us_per_launch": round(us, 3), "bytes_per_launch": b,
+            "other": {"attention_us": round(attn_us, 3), "attention_GBs": round(att_gbs, 1),
+                      "o_gemv_us": round(wo_us, 3), "o_gemv_GBs": round(wo_gbs, 1)}}
+
+
+def cpu_baseline(args, stack, nbytes):
+    """The oracle (plain single-threaded C) on the host cores, on a bounded
+    sample of the same workload: whole layers, cycling over the stack's layers
+    with the first layer's input, until the time budget is spent."""
+    import numpy as np
+
+    import oracle
+    from decode_step_attention_layer_amd import synth
+
+    cfg = stack.cfg
+    cos, sin = synth.rope_for(cfg)
+    dims = dict(D=cfg.D, H=cfg.H, KV=cfg.KV, hd=cfg.hd, m=cfg.m, eps=cfg.eps)
+    x = stack.x0_host
+    done, t_spent, li = 0, 0.0, 0
+    while t_spent < args.cpu_seconds and done < 4 * stack.nlayers:
+        L = stack.layers[li % stack.nlayers]
+        h = L.host
+        if cfg.page_size:
+            c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, page_size=cfg.page_size,
+                             page_table=h["table"], max_pages_per_seq=cfg.max_pages_per_seq,
+                             num_pages=h["k"].shape[0])
+        else:
+            c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, capacity=cfg.capacity)
+        w = dict(h, rope_cos=cos, rope_sin=sin)
+        t = time.perf_counter()
+        oracle.decode_layer(dims, w, c, x, x, stack.pos)
+        t_spent += time.perf_counter() - t
+        done += 1
+        li += 1
+    gbs = nbytes["total"] * done / t_spent / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_layer": round(t_spent * 1e6 / done, 1),
+            "sample": f"{done} whole-layer calls of the {args.config} workload "
+                      f"(layers cycled, first-layer input), {t_spent:.1f} s single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,320 @@
+// ck_api.cpp — the C ABI of libck.so (declared in include/ck.h): argument
+// validation on the host, workspace layout, and the launch sequence of the
+// decode layer (C-Kernel-Engine "mega_fused_attention_decode_q5_0.c", MAIN
+// KERNEL steps 1-8). Nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ck.h"
+#include "ck_internal.hpp"
+
+using namespace ck;
+
+namespace {
+
+bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? CK_OK : CK_EHIP; }
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Validates the cache descriptor and builds the kernel view.
+int cache_view(const ck_kv_cache *kv, CacheView *out) {
+    if (!kv || !kv->k || !kv->v || kv->kv_heads <= 0 || kv->head_dim <= 0) return CK_EINVAL;
+    if (!al(kv->k, 16) || !al(kv->v, 16) || kv->head_dim % 4) return CK_EINVAL;
+    if (kv->page_size < 0) return CK_EINVAL;
+    if (kv->page_size == 0) {
+        if (kv->capacity <= 0) return CK_EINVAL;
+    } else {
+        if (!kv->page_table || kv->max_pages_per_seq <= 0 || kv->num_pages <= 0) return CK_EINVAL;
+        if (!al(kv->page_table, 4)) return CK_EINVAL;
+    }
+    out->k = kv->k;
+    out->v = kv->v;
+    out->table = kv->page_table;
+    out->kv_heads = kv->kv_heads;
+    out->head_dim = kv->head_dim;
+    out->capacity = kv->capacity;
+    out->page_size = kv->page_size;
+    out->max_pages = kv->max_pages_per_seq;
+    out->num_pages = kv->num_pages;
+    return CK_OK;
+}
+
+// Token capacity of one sequence of the cache (positions must stay below).
+long long cache_tokens(const ck_kv_cache *kv) {
+    return kv->page_size == 0 ? (long long)kv->capacity
+                              : (long long)kv->page_size * kv->max_pages_per_seq;
+}
+
+int read_positions(const int32_t *pos_host, int m, long long limit, Positions *p, int *max_tokens) {
+    if (!pos_host || m < 1 || m > CK_MAX_SEQS) return CK_EINVAL;
+    int mx = 0;
+    memset(p, 0, sizeof(*p));
+    for (int s = 0; s < m; s++) {
+        if (pos_host[s] < 0 || pos_host[s] >= limit) return CK_EINVAL;
+        p->p[s] = pos_host[s];
+        if (pos_host[s] + 1 > mx) mx = pos_host[s] + 1;
+    }
+    *max_tokens = mx;
+    return CK_OK;
+}
+
+struct WsLayout {
+    size_t xn, xq, q, k, v, attn, aq, part, total;
+    AttnPlan plan;
+};
+
+WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
+    const size_t m = d->m, D = d->D, HD = (size_t)d->H * d->head_dim,
+                 KD = (size_t)d->KV * d->head_dim;
+    WsLayout w;
+    size_t o = 0;
+    w.xn = o; o = up256(o + sizeof(float) * m * D);
+    w.xq = o; o = up256(o + m * (D / CK_QK) * CK_Q8_0_BYTES);
+    w.q = o; o = up256(o + sizeof(float) * m * HD);
+    w.k = o; o = up256(o + sizeof(float) * m * KD);
+    w.v = o; o = up256(o + sizeof(float) * m * KD);
+    w.attn = o; o = up256(o + sizeof(float) * m * HD);
+    w.aq = o; o = up256(o + m * (HD / CK_QK) * CK_Q8_0_BYTES);
+    w.plan = attn_plan(d->m, d->KV, max_ctx, d->attn_chunk);
+    const int maxc = attn_max_chunks(d->m, d->KV, max_ctx, d->attn_chunk);
+    w.part = o; o = up256(o + attn_partials_bytes(d->m, d->H, d->head_dim, maxc));
+    w.total = o;
+    return w;
+}
+
+int check_desc(const ck_layer_desc *d) {
+    if (!d) return CK_EINVAL;
+    if (d->D <= 0 || d->H <= 0 || d->KV <= 0 || d->head_dim <= 0 || d->m < 1 || d->m > CK_MAX_SEQS)
+        return CK_EINVAL;
+    if (d->D % CK_QK || (d->H * d->head_dim) % CK_QK || d->head_dim % 2 || d->H % d->KV)
+        return CK_EINVAL;
+    if (d->variant != CK_VARIANT_CHAIN && d->variant != CK_VARIANT_FUSED) return CK_EINVAL;
+    if (d->attn_chunk < 0 || !(d->eps >= 0.0f)) return CK_EINVAL;
+    if (!attn_shape_supported(d->H / d->KV, d->head_dim)) return CK_EUNSUPPORTED;
+    if (!gemv_shape_supported(d->D) || !gemv_shape_supported(d->H * d->head_dim))
+        return CK_EUNSUPPORTED;
+    return CK_OK;
+}
+
+int gemv_common(const void *W, const void *xq, const float *bias, const float *residual, float *y,
+                int rows, int K, int m, void *stream, int is_q5) {
+    if (!W || !xq || !y || rows <= 0 || K <= 0 || K % CK_QK || m < 1) return CK_EINVAL;
+    if (!al(W, 4) || !al(xq, 2) || !al(y, 4) || (bias && !al(bias, 4)) ||
+        (residual && !al(residual, 4)))
+        return CK_EINVAL;
+    if (!gemv_shape_supported(K)) return CK_EUNSUPPORTED;
+    GemvArgs a;
+    memset(&a, 0, sizeof(a));
+    a.nseg = 1;
+    a.seg[0].W = static_cast<const uint8_t *>(W);
+    a.seg[0].bias = bias;
+    a.seg[0].residual = residual;
+    a.seg[0].y = y;
+    a.seg[0].rows = rows;
+    a.seg[0].is_q5 = is_q5;
+    a.xq = static_cast<const uint8_t *>(xq);
+    a.K = K;
+    a.m = m;
+    return hip_rc(launch_gemv(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ck_strerror(int code) {
+    switch (code) {
+        case CK_OK: return "ok";
+        case CK_EINVAL: return "invalid argument";
+        case CK_ENOSPC: return "workspace too small";
+        case CK_EUNSUPPORTED: return "shape not supported";
+        case CK_EHIP: return "HIP runtime error";
+    }
+    return "unknown error";
+}
+
+int ck_version(void) { return (0 << 16) | 1; }
+
+int ck_rmsnorm(const float *x, const float *gamma, float *y, int m, int D, float eps, void *stream) {
+    if (!x || !gamma || !y || m < 1 || D <= 0 || !(eps >= 0.0f)) return CK_EINVAL;
+    if (!al(x, 4) || !al(gamma, 4) || !al(y, 4)) return CK_EINVAL;
+    return hip_rc(launch_rmsnorm(x, gamma, y, m, D, eps, (hipStream_t)stream));
+}
+
+int ck_quantize_q8_0(const float *x, void *y, int m, int K, void *stream) {
+    if (!x || !y || m < 1 || K <= 0 || K % CK_QK) return CK_EINVAL;
+    if (!al(x, 4) || !al(y, 2)) return CK_EINVAL;
+    return hip_rc(launch_quantize_q8_0(x, static_cast<uint8_t *>(y), (long long)m * (K / CK_QK),
+                                       (hipStream_t)stream));
+}
+
+int ck_gemv_q5_0_q8_0(const void *W, const void *xq, const float *bias, const float *residual,
+                      float *y, int rows, int K, int m, void *stream) {
+    return gemv_common(W, xq, bias, residual, y, rows, K, m, stream, 1);
+}
+
+int ck_gemv_q8_0_q8_0(const void *W, const void *xq, const float *bias, const float *residual,
+                      float *y, int rows, int K, int m, void *stream) {
+    return gemv_common(W, xq, bias, residual, y, rows, K, m, stream, 0);
+}
+
+int ck_rope(float *q, float *k, const float *cos_tab, const float *sin_tab, int tab_rows,
+            const int32_t *pos_host, int m, int H, int KV, int hd, void *stream) {
+    if ((!q && !k) || !cos_tab || !sin_tab || tab_rows <= 0 || hd <= 0 || hd % 2) return CK_EINVAL;
+    if ((q && H <= 0) || (k && KV <= 0)) return CK_EINVAL;
+    Positions p;
+    int mx;
+    int rc = read_positions(pos_host, m, tab_rows, &p, &mx);
+    if (rc) return rc;
+    return hip_rc(launch_rope(q, k, cos_tab, sin_tab, p, m, q ? H : 0, k ? KV : 0, hd,
+                              (hipStream_t)stream));
+}
+
+int ck_kv_append(const ck_kv_cache *kv, const float *k, const float *v, const int32_t *pos_host,
+                 int m, void *stream) {
+    CacheView c;
+    int rc = cache_view(kv, &c);
+    if (rc) return rc;
+    if (!k || !v) return CK_EINVAL;
+    Positions p;
+    int mx;
+    rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
+    if (rc) return rc;
+    return hip_rc(launch_kv_append(c, k, v, p, m, (hipStream_t)stream));
+}
+
+size_t ck_attn_workspace_size(int m, int H, int KV, int hd, int max_tokens, int chunk) {
+    if (m < 1 || H <= 0 || KV <= 0 || hd <= 0 || max_tokens < 1 || chunk < 0) return 0;
+    return attn_partials_bytes(m, H, hd, attn_max_chunks(m, KV, max_tokens, chunk));
+}
+
+int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, float *out,
+                       int m, int H, float scale, int chunk, void *ws, size_t ws_bytes,
+                       void *stream) {
+    CacheView c;
+    int rc = cache_view(kv, &c);
+    if (rc) return rc;
+    if (!q || !out || !ws || H <= 0 || chunk < 0 || H % c.kv_heads) return CK_EINVAL;
+    if (!al(q, 16) || !al(out, 4) || !al(ws, 16)) return CK_EINVAL;
+    if (!attn_shape_supported(H / c.kv_heads, c.head_dim)) return CK_EUNSUPPORTED;
+    Positions p;
+    int mx;
+    rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
+    if (rc) return rc;
+    AttnPlan pl = attn_plan(m, c.kv_heads, mx, chunk);
+    if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
+    return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream));
+}
+
+size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx) {
+    if (check_desc(desc) != CK_OK || max_ctx < 1) return 0;
+    return ws_layout(desc, max_ctx).total;
+}
+
+long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const char *name) {
+    if (check_desc(desc) != CK_OK || max_ctx < 1 || !name) return -1;
+    WsLayout w = ws_layout(desc, max_ctx);
+    if (!strcmp(name, "xn")) return (long)w.xn;
+    if (!strcmp(name, "xq")) return (long)w.xq;
+    if (!strcmp(name, "q")) return (long)w.q;
+    if (!strcmp(name, "k")) return (long)w.k;
+    if (!strcmp(name, "v")) return (long)w.v;
+    if (!strcmp(name, "attn")) return (long)w.attn;
+    if (!strcmp(name, "aq")) return (long)w.aq;
+    return -1;
+}
+
+int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                    const float *x, const float *residual, const int32_t *pos_host, float *out,
+                    void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    const ck_layer_desc &d = *desc;
+    if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->gamma || !w->rope_cos || !w->rope_sin)
+        return CK_EINVAL;
+    if (!al(w->wq, 4) || !al(w->wk, 4) || !al(w->wv, 4) || !al(w->wo, 4)) return CK_EINVAL;
+    if (!x || !out || !ws || !al(x, 4) || !al(out, 4) || !al(ws, 256)) return CK_EINVAL;
+    if (residual && !al(residual, 4)) return CK_EINVAL;
+    if (x == out) return CK_EINVAL;
+    CacheView c;
+    rc = cache_view(kv, &c);
+    if (rc) return rc;
+    if (c.kv_heads != d.KV || c.head_dim != d.head_dim) return CK_EINVAL;
+    Positions p;
+    int mx;
+    long long limit = cache_tokens(kv);
+    if (w->rope_rows < limit) limit = w->rope_rows;
+    rc = read_positions(pos_host, d.m, limit, &p, &mx);
+    if (rc) return rc;
+    WsLayout L = ws_layout(desc, mx);
+    if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, L.plan.nchunks))
+        return CK_ENOSPC;
+
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    float *xn = reinterpret_cast<float *>(base + L.xn);
+    uint8_t *xq = base + L.xq;
+    float *q = reinterpret_cast<float *>(base + L.q);
+    float *k = reinterpret_cast<float *>(base + L.k);
+    float *v = reinterpret_cast<float *>(base + L.v);
+    float *attn = reinterpret_cast<float *>(base + L.attn);
+    uint8_t *aq = base + L.aq;
+    void *part = base + L.part;
+    const int HD = d.H * d.head_dim, KD = d.KV * d.head_dim;
+    const bool fused = d.variant == CK_VARIANT_FUSED;
+
+    // steps 1-2: RMSNorm and the one Q8_0 quantization shared by Q, K and V
+    hipError_t e;
+    if (fused) {
+        e = launch_rmsnorm_quant(x, w->gamma, xn, xq, d.m, d.D, d.eps, st);
+    } else {
+        e = launch_rmsnorm(x, w->gamma, xn, d.m, d.D, d.eps, st);
+        if (e == hipSuccess) e = launch_quantize_q8_0(xn, xq, (long long)d.m * (d.D / CK_QK), st);
+    }
+    if (e != hipSuccess) return CK_EHIP;
+
+    // steps 2-4: Q, K (Q5_0) and V (Q8_0) projections with bias, one launch
+    GemvArgs g;
+    memset(&g, 0, sizeof(g));
+    g.nseg = 3;
+    g.seg[0] = GemvSeg{static_cast<const uint8_t *>(w->wq), w->bq, nullptr, q, HD, 1, 0, 0};
+    g.seg[1] = GemvSeg{static_cast<const uint8_t *>(w->wk), w->bk, nullptr, k, KD, 1, 0, 0};
+    g.seg[2] = GemvSeg{static_cast<const uint8_t *>(w->wv), w->bv, nullptr, v, KD, 0, 0, 0};
+    g.xq = xq;
+    g.K = d.D;
+    g.m = d.m;
+    if ((e = launch_gemv(g, st)) != hipSuccess) return CK_EHIP;
+
+    // steps 5-6: RoPE on q and k, then the append of (k, v) at pos
+    if (fused) {
+        e = launch_rope_append(q, k, v, w->rope_cos, w->rope_sin, c, p, d.m, d.H, st);
+    } else {
+        e = launch_rope(q, k, w->rope_cos, w->rope_sin, p, d.m, d.H, d.KV, d.head_dim, st);
+        if (e == hipSuccess) e = launch_kv_append(c, k, v, p, d.m, st);
+    }
+    if (e != hipSuccess) return CK_EHIP;
+
+    // step 7: attention over pos + 1 tokens (fused: the merge also quantizes)
+    const float scale = 1.0f / sqrtf((float)d.head_dim);
+    e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, L.plan, part, st);
+    if (e != hipSuccess) return CK_EHIP;
+    if (!fused) {
+        e = launch_quantize_q8_0(attn, aq, (long long)d.m * (HD / CK_QK), st);
+        if (e != hipSuccess) return CK_EHIP;
+    }
+
+    // step 8: O projection (Q5_0) + bo + residual
+    GemvArgs o;
+    memset(&o, 0, sizeof(o));
+    o.nseg = 1;
+    o.seg[0] = GemvSeg{static_cast<const uint8_t *>(w->wo), w->bo, residual, out, d.D, 1, 0, 0};
+    o.xq = aq;
+    o.K = HD;
+    o.m = d.m;
+    return hip_rc(launch_gemv(o, st));
+}
+
+}  // extern "C"

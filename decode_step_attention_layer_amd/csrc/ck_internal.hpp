@@ -1,0 +1,88 @@
+// ck_internal.hpp — argument structs and launchers shared between the kernel
+// translation units and the C-ABI entry points (ck_api.cpp). Host-side only
+// declarations plus the by-value kernel argument structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ck.h"
+
+namespace ck {
+
+constexpr int kMaxSeqs = CK_MAX_SEQS;
+
+struct Positions {
+    int32_t p[kMaxSeqs];
+};
+
+// Cache view passed by value to kernels (mirrors ck_kv_cache).
+struct CacheView {
+    float *k;
+    float *v;
+    const int32_t *table;
+    int kv_heads, head_dim, capacity, page_size, max_pages, num_pages;
+};
+
+// Element offset of (seq, kv head, token) in the K (or V) buffer, or -1 if the
+// token's page is unmapped or out of range. Shared by the kernels.
+__device__ __forceinline__ long long cache_row(const CacheView &c, int s, int g, int t) {
+    if (c.page_size == 0)
+        return (((long long)s * c.kv_heads + g) * c.capacity + t) * (long long)c.head_dim;
+    int page = c.table[(long long)s * c.max_pages + t / c.page_size];
+    if (page < 0 || page >= c.num_pages) return -1;
+    return (((long long)page * c.kv_heads + g) * c.page_size + t % c.page_size) *
+           (long long)c.head_dim;
+}
+
+// One GEMV output segment: rows [0, rows) of a weight matrix.
+struct GemvSeg {
+    const uint8_t *W;
+    const float *bias;      // nullable
+    const float *residual;  // nullable, [m][rows]
+    float *y;               // [m][rows]
+    int rows;
+    int is_q5;              // 1: Q5_0 weights, 0: Q8_0 weights
+    int wg_begin;           // first workgroup of this segment
+    int pad;
+};
+
+struct GemvArgs {
+    GemvSeg seg[3];
+    int nseg;
+    const uint8_t *xq;      // [m][K/32] Q8_0 blocks
+    int K;
+    int m;
+};
+
+// Launchers. Each returns hipSuccess or the launch error.
+hipError_t launch_rmsnorm(const float *x, const float *gamma, float *y, int m, int D,
+                          float eps, hipStream_t st);
+hipError_t launch_quantize_q8_0(const float *x, uint8_t *y, long long nblocks, hipStream_t st);
+hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float *xn, uint8_t *xq,
+                                int m, int D, float eps, hipStream_t st);
+bool gemv_shape_supported(int K);
+hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
+hipError_t launch_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
+                       const Positions &pos, int m, int H, int KV, int hd, hipStream_t st);
+hipError_t launch_kv_append(const CacheView &c, const float *k, const float *v,
+                            const Positions &pos, int m, hipStream_t st);
+hipError_t launch_rope_append(float *q, float *k, const float *v, const float *cos_tab,
+                              const float *sin_tab, const CacheView &c, const Positions &pos, int m,
+                              int H, hipStream_t st);
+
+// Attention geometry: tokens per chunk and chunks per (sequence, KV head).
+struct AttnPlan {
+    int chunk;
+    int nchunks;
+};
+AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req);
+int attn_max_chunks(int m, int KV, int max_tokens, int chunk_req);
+bool attn_shape_supported(int G, int hd);
+size_t attn_partials_bytes(int m, int H, int hd, int nchunks);
+hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
+                            uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
+                            void *partials, hipStream_t st);
+
+}  // namespace ck

@@ -1,0 +1,273 @@
+// k_gemv.hip — Q5_0 / Q8_0 weight x Q8_0 activation GEMV for gfx950.
+//
+// Computes, for every token s and output row r of up to three weight
+// segments in one launch (Q, K and V share one quantized input, as the page's
+// helper "Q5_0 GEMV with inline processing" feeds each projection the same
+// quantized row):
+//   y[s][r] = sum_b d_w(r,b) * d_x(s,b) * S(r,s,b) + bias[r] (+ residual[s][r])
+// with S the exact integer dot of block b (v_dot4_i32_i8 over int8 lanes).
+//
+// Mapping: a row is owned by LPR lanes of one wavefront (LPR = 64 for long
+// rows: one row per wavefront; fewer for short rows, several rows per wave).
+// A lane owns "units" of the row: pairs of consecutive blocks (44 B of Q5_0
+// or 68 B of Q8_0, dword aligned whenever K/32 is even) read with dwordx4
+// loads straight from the canonical block layout, or single blocks read with
+// 16-bit loads when K/32 is odd. Each wavefront loads the weights of its R
+// rows before any arithmetic, keeps them in registers and reuses them for all
+// m tokens. The quantized activations are staged once per workgroup into LDS
+// in a dword-aligned form (codes, scale as fp32, code sum for the Q5_0 offset).
+// Partial sums are reduced across the LPR lanes with DPP / ds_swizzle.
+#include "ck_device.hpp"
+#include "ck_internal.hpp"
+
+namespace ck {
+
+namespace {
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = kGemvThreads / kWave;
+
+// Words of register storage for one unit of each format.
+template <bool Q5, bool PAIRED>
+struct Fmt {
+    static constexpr int blocks = PAIRED ? 2 : 1;
+    static constexpr int bytes = (Q5 ? kQ5Bytes : kQ8Bytes) * blocks;
+    static constexpr int words = PAIRED ? (Q5 ? 11 : 17) : (Q5 ? 6 : 9);
+};
+
+template <bool Q5, bool PAIRED>
+__device__ __forceinline__ void load_unit(const uint8_t *p, uint32_t *w) {
+    if constexpr (PAIRED) {
+        const uint32_t *p32 = reinterpret_cast<const uint32_t *>(p);
+        if constexpr (Q5) {
+            u32x4a4 a = *reinterpret_cast<const u32x4a4 *>(p32);
+            u32x4a4 b = *reinterpret_cast<const u32x4a4 *>(p32 + 4);
+            u32x3a4 c = *reinterpret_cast<const u32x3a4 *>(p32 + 8);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+            w[8] = c.x; w[9] = c.y; w[10] = c.z;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                u32x4a4 a = *reinterpret_cast<const u32x4a4 *>(p32 + 4 * i);
+                w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
+            }
+            w[16] = p32[16];
+        }
+    } else {
+        const uint16_t *p16 = reinterpret_cast<const uint16_t *>(p);
+        w[0] = p16[0];
+        if constexpr (Q5) {
+            w[1] = (uint32_t)p16[1] | ((uint32_t)p16[2] << 16);
+#pragma unroll
+            for (int i = 0; i < 4; i++) w[2 + i] = (uint32_t)p16[3 + 2 * i] | ((uint32_t)p16[4 + 2 * i] << 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) w[1 + i] = (uint32_t)p16[1 + 2 * i] | ((uint32_t)p16[2 + 2 * i] << 16);
+        }
+    }
+}
+
+// Activation block staged in LDS / registers.
+struct alignas(16) XBlock {
+    int c[8];     // 32 int8 codes, 4 per dword
+    float d;      // scale
+    int sum;      // sum of the 32 codes
+    int pad[2];
+};
+
+// Dot of one weight unit with its activation blocks.
+template <bool Q5, bool PAIRED>
+__device__ __forceinline__ float unit_dot(const uint32_t *w, const XBlock *x, float acc) {
+    if constexpr (PAIRED && Q5) {
+        int s0 = q5_codes_dot(align2(w[1], w[0]), align2(w[2], w[1]), align2(w[3], w[2]),
+                              align2(w[4], w[3]), align2(w[5], w[4]), x[0].c) - 16 * x[0].sum;
+        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
+        int s1 = q5_codes_dot(w[6], w[7], w[8], w[9], w[10], x[1].c) - 16 * x[1].sum;
+        acc = fmaf((float)s1, half_bits_to_float(w[5] >> 16) * x[1].d, acc);
+    } else if constexpr (PAIRED) {
+        uint32_t c0[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) c0[i] = align2(w[i + 1], w[i]);
+        int s0 = q8_codes_dot(c0, x[0].c);
+        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
+        int s1 = q8_codes_dot(w + 9, x[1].c);
+        acc = fmaf((float)s1, half_bits_to_float(w[8] >> 16) * x[1].d, acc);
+    } else if constexpr (Q5) {
+        int s0 = q5_codes_dot(w[1], w[2], w[3], w[4], w[5], x[0].c) - 16 * x[0].sum;
+        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
+    } else {
+        int s0 = q8_codes_dot(w + 1, x[0].c);
+        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
+    }
+    return acc;
+}
+
+template <int LPR>
+__device__ __forceinline__ float row_reduce(float v) {
+    if constexpr (LPR == 64) {
+        v = group_sum<32>(v);
+        return readlane_f(v, 0) + readlane_f(v, 32);
+    } else {
+        return group_sum<LPR>(v);
+    }
+}
+
+template <bool Q5, int LPR, int UPL, int R, bool PAIRED>
+__device__ __forceinline__ void gemv_body(const GemvSeg &sg, int wg_in_seg, const XBlock *xs,
+                                          int nb, int m) {
+    using F = Fmt<Q5, PAIRED>;
+    constexpr int RPW = kWave / LPR;  // rows per wave per iteration
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % LPR, rsel = lane / LPR;
+    const int nunits = nb / F::blocks;
+    const size_t row_bytes = (size_t)nb * (Q5 ? kQ5Bytes : kQ8Bytes);
+    const int row0 = (wg_in_seg * kGemvWaves + wave) * (RPW * R);
+
+    // 1. weights of all R rows into registers (all loads issued up front)
+    uint32_t wr[R][UPL][F::words];
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        const int row = row0 + it * RPW + rsel;
+        const uint8_t *rp = sg.W + (size_t)row * row_bytes;
+#pragma unroll
+        for (int u = 0; u < UPL; u++) {
+            const int unit = sub + u * LPR;
+            if (row < sg.rows && unit < nunits) {
+                load_unit<Q5, PAIRED>(rp + (size_t)unit * F::bytes, wr[it][u]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < F::words; i++) wr[it][u][i] = 0;
+            }
+        }
+    }
+
+    // 2. per token: activation blocks of this lane's units, dots, reduction
+    for (int s = 0; s < m; s++) {
+        XBlock xb[UPL][F::blocks];
+#pragma unroll
+        for (int u = 0; u < UPL; u++) {
+            const int unit = sub + u * LPR;
+#pragma unroll
+            for (int b = 0; b < F::blocks; b++) {
+                if (unit < nunits) {
+                    xb[u][b] = xs[(size_t)s * nb + unit * F::blocks + b];
+                } else {
+                    xb[u][b] = XBlock{{0, 0, 0, 0, 0, 0, 0, 0}, 0.0f, 0, {0, 0}};
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < R; it++) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int u = 0; u < UPL; u++) acc = unit_dot<Q5, PAIRED>(wr[it][u], xb[u], acc);
+            acc = row_reduce<LPR>(acc);
+            const int row = row0 + it * RPW + rsel;
+            if (sub == 0 && row < sg.rows) {
+                float o = acc + (sg.bias ? sg.bias[row] : 0.0f);
+                if (sg.residual) o = o + sg.residual[(size_t)s * sg.rows + row];
+                sg.y[(size_t)s * sg.rows + row] = o;
+            }
+        }
+    }
+}
+
+template <int LPR, int UPL, int R, bool PAIRED>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
+    extern __shared__ XBlock xs[];
+    const int wg = blockIdx.x;
+    const int si = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2
+                   : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
+    const GemvSeg sg = si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]);
+    const int nb = a.K / kQK;
+
+    // stage the quantized activations: dword-aligned codes, fp32 scale, code sum
+    const int nxb = a.m * nb;
+    for (int b = threadIdx.x; b < nxb; b += kGemvThreads) {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(a.xq + (size_t)b * kQ8Bytes);
+        XBlock xb;
+        xb.d = half_bits_to_float(src[0]);
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t c = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+            xb.c[i] = (int)c;
+            sum = __builtin_amdgcn_sdot4((int)c, 0x01010101, sum, false);
+        }
+        xb.sum = sum;
+        xb.pad[0] = xb.pad[1] = 0;
+        xs[b] = xb;
+    }
+    __syncthreads();
+
+    const int wg_in_seg = wg - sg.wg_begin;
+    if (sg.is_q5)
+        gemv_body<true, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, nb, a.m);
+    else
+        gemv_body<false, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, nb, a.m);
+}
+
+constexpr int kRowsIter = 2;
+
+template <int LPR, int UPL, bool PAIRED>
+hipError_t launch_t(GemvArgs a, hipStream_t st) {
+    const int rows_per_wg = kGemvWaves * (kWave / LPR) * kRowsIter;
+    int total = 0;
+    for (int i = 0; i < a.nseg; i++) {
+        a.seg[i].wg_begin = total;
+        total += (a.seg[i].rows + rows_per_wg - 1) / rows_per_wg;
+    }
+    for (int i = a.nseg; i < 3; i++) a.seg[i] = a.seg[0], a.seg[i].wg_begin = 1 << 30;
+    const size_t lds = sizeof(XBlock) * (size_t)a.m * (a.K / kQK);
+    hipLaunchKernelGGL((k_gemv<LPR, UPL, kRowsIter, PAIRED>), dim3(total), dim3(kGemvThreads), lds,
+                       st, a);
+    return hipGetLastError();
+}
+
+template <int LPR, bool PAIRED>
+hipError_t launch_upl(const GemvArgs &a, int upl, hipStream_t st) {
+    if (upl <= 1) return launch_t<LPR, 1, PAIRED>(a, st);
+    if (upl <= 2) return launch_t<LPR, 2, PAIRED>(a, st);
+    return launch_t<LPR, 4, PAIRED>(a, st);
+}
+
+template <bool PAIRED>
+hipError_t launch_lpr(const GemvArgs &a, int nunits, hipStream_t st) {
+    if (nunits <= 4) return launch_upl<4, PAIRED>(a, 1, st);
+    if (nunits <= 8) return launch_upl<8, PAIRED>(a, 1, st);
+    if (nunits <= 16) return launch_upl<16, PAIRED>(a, 1, st);
+    if (nunits <= 32) return launch_upl<32, PAIRED>(a, 1, st);
+    return launch_upl<64, PAIRED>(a, (nunits + 63) / 64, st);
+}
+
+constexpr size_t kGemvLds = 64 * 1024;
+
+}  // namespace
+
+bool gemv_shape_supported(int K) {
+    const int nb = K / kQK;
+    const int nunits = (nb % 2 == 0) ? nb / 2 : nb;
+    return nunits <= 64 * 4 && sizeof(XBlock) * (size_t)nb <= kGemvLds;
+}
+
+// Tokens are processed in slices whose staged activations fit the LDS budget;
+// each slice re-reads the weights, so a slice holds as many tokens as fit.
+hipError_t launch_gemv(const GemvArgs &a, hipStream_t st) {
+    const int nb = a.K / kQK;
+    const int per = (int)(kGemvLds / (sizeof(XBlock) * (size_t)nb));
+    for (int s0 = 0; s0 < a.m; s0 += per) {
+        GemvArgs b = a;
+        b.m = a.m - s0 < per ? a.m - s0 : per;
+        b.xq = a.xq + (size_t)s0 * nb * kQ8Bytes;
+        for (int i = 0; i < a.nseg; i++) {
+            b.seg[i].y = a.seg[i].y + (size_t)s0 * a.seg[i].rows;
+            if (a.seg[i].residual) b.seg[i].residual = a.seg[i].residual + (size_t)s0 * a.seg[i].rows;
+        }
+        hipError_t e = (nb % 2 == 0) ? launch_lpr<true>(b, nb / 2, st) : launch_lpr<false>(b, nb, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace ck

@@ -1,0 +1,127 @@
+"""Device-resident workloads for the decode layer: upload seeded inputs, wire
+them into the C-ABI structs and run decode steps through libck.
+
+Plumbing only (torch provides device memory and the stream); every step of
+the layer runs in libck's kernels. A "step" runs every layer of the
+configuration once, chaining x_{l+1} = out_l with residual_l = x_l.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import ck, synth
+
+
+def to_dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+@dataclass
+class DeviceLayer:
+    tensors: dict
+    weights: ck.CkLayerWeights
+    cache: ck.CkKVCache
+    host: dict = field(default_factory=dict)
+
+
+class DeviceStack:
+    """All layers of one configuration on one GPU, plus x, outputs and workspace."""
+
+    def __init__(self, cfg: synth.Config, device="cuda", poison: float = float("nan"),
+                 keep_host: bool = False, spare_pages: int = 0, layers: int | None = None,
+                 threads: int = 8):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.nlayers = cfg.layers if layers is None else layers
+        cos, sin = synth.rope_for(cfg)
+        self.rope = (to_dev(cos, self.device), to_dev(sin, self.device))
+        self.rope_rows = cos.shape[0]
+        x = synth.token_input(cfg)
+        self.x0_host = x
+        self.x0 = to_dev(x, self.device)
+        self.lens = synth.context_lengths(cfg)
+        self.pos = [int(p) for p in self.lens]
+
+        def make(layer):
+            w = synth.layer_weights(cfg, layer)
+            if cfg.page_size:
+                k, v, table, lens = synth.paged_cache(cfg, layer, poison, spare_pages)
+                assert np.array_equal(lens, self.lens)
+                c = dict(k=k, v=v, table=table)
+            else:
+                k, v = synth.contiguous_cache(cfg, layer, poison)
+                c = dict(k=k, v=v)
+            return layer, w, c
+
+        self.layers: list[DeviceLayer] = []
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            for layer, w, c in ex.map(make, range(self.nlayers)):
+                self.layers.append(self._upload(w, c, keep_host))
+        D = cfg.D
+        self.bufs = [torch.empty((cfg.m, D), dtype=torch.float32, device=self.device)
+                     for _ in range(2)]
+        self.max_ctx = max(self.pos) + 1
+
+    def clone(self) -> "DeviceStack":
+        """A second copy of every device tensor (same values, new memory), for
+        benchmarks that rotate replicas to keep the working set out of the
+        last-level cache."""
+        twin = object.__new__(DeviceStack)
+        twin.__dict__.update(self.__dict__)
+        twin.layers = []
+        cfg = self.cfg
+        for L in self.layers:
+            t = {n: v.clone() for n, v in L.tensors.items()}
+            if cfg.page_size:
+                cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, 0, cfg.page_size, t["table"],
+                                    cfg.max_pages_per_seq, L.cache.num_pages)
+            else:
+                cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity)
+            weights = ck.layer_weights(t["wq"], t["wk"], t["wv"], t["wo"], t["bq"], t["bk"],
+                                       t["bv"], t["bo"], t["gamma"], self.rope[0], self.rope[1],
+                                       self.rope_rows)
+            twin.layers.append(DeviceLayer(t, weights, cache, L.host))
+        twin.bufs = [b.clone() for b in self.bufs]
+        twin.x0 = self.x0.clone()
+        return twin
+
+    def _upload(self, w, c, keep_host):
+        dev = self.device
+        t = {n: to_dev(w[n], dev) for n in ("wq", "wk", "wv", "wo", "bq", "bk", "bv", "bo", "gamma")}
+        t["k"] = to_dev(c["k"], dev)
+        t["v"] = to_dev(c["v"], dev)
+        cfg = self.cfg
+        if cfg.page_size:
+            t["table"] = to_dev(c["table"], dev)
+            cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, 0, cfg.page_size, t["table"],
+                                cfg.max_pages_per_seq, c["k"].shape[0])
+        else:
+            cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity)
+        weights = ck.layer_weights(t["wq"], t["wk"], t["wv"], t["wo"], t["bq"], t["bk"], t["bv"],
+                                   t["bo"], t["gamma"], self.rope[0], self.rope[1], self.rope_rows)
+        host = dict(w, **{"k": c["k"], "v": c["v"]}, **({"table": c["table"]} if "table" in c else {})) \
+            if keep_host else {}
+        return DeviceLayer(t, weights, cache, host)
+
+    def desc(self, variant=ck.CK_VARIANT_FUSED, attn_chunk=0) -> ck.CkLayerDesc:
+        c = self.cfg
+        return ck.layer_desc(c.D, c.H, c.KV, c.hd, c.m, c.eps, variant, attn_chunk)
+
+    def workspace(self, desc: ck.CkLayerDesc) -> torch.Tensor:
+        n = ck.ck_decode_layer_workspace_size(desc, self.max_ctx)
+        assert n > 0, "layer shape rejected by libck"
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def step(self, desc: ck.CkLayerDesc, ws: torch.Tensor, stream=None, x=None) -> torch.Tensor:
+        """One decode step through every layer; returns the last layer's output."""
+        cur = self.x0 if x is None else x
+        for i, L in enumerate(self.layers):
+            out = self.bufs[i % 2]
+            ck.ck_decode_layer(desc, L.weights, L.cache, cur, cur, self.pos, out, ws,
+                               ws.numel(), stream)
+            cur = out
+        return cur

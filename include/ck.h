@@ -1,0 +1,179 @@
+/*
+ * ck.h — C ABI of libck.so, the MI355X (gfx950) decode-step attention layer.
+ *
+ * The layer is the one on the C-Kernel-Engine page
+ * "mega_fused_attention_decode_q5_0.c" (MAIN KERNEL, steps 1-8): RMSNorm,
+ * Q8_0 activation quantization, Q/K/O projections with Q5_0 weights and the V
+ * projection with Q8_0 weights (each plus bias), RoPE, KV-cache append,
+ * grouped-query decode attention, O projection, residual add. The paged cache
+ * follows the metrale page "prefill_attn_a.rs" (paged_decode_attn_*: block
+ * tables, block size); the attention is split over tokens and merged with a
+ * log-sum-exp pass.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_host are host memory; every other pointer is device
+ *    memory (hipMalloc'd or a torch CUDA tensor), 16-byte aligned.
+ *  - The caller owns every buffer: weights, cache, inputs, outputs and the
+ *    workspace. The library never allocates, frees or synchronizes.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; results are valid after the stream is synchronized.
+ *  - Arguments are validated on the host before anything is launched. The
+ *    return value is CK_OK or a negative CK_E* code; on an error nothing has
+ *    been enqueued. A launch failure reported by the runtime returns CK_EHIP.
+ *  - The library keeps no state between calls and is safe to call from
+ *    several host threads on different streams.
+ *  - m, the number of tokens (one per sequence), is at most CK_MAX_SEQS.
+ *
+ * Block layouts (little-endian, packed, no padding), 32 values per block:
+ *   Q8_0, 34 B: fp16 d | int8 q[32]                 value_j = d * q_j
+ *   Q5_0, 22 B: fp16 d | uint8 qh[4] | uint8 qs[16] value_j = d * (code_j - 16)
+ *     code_j = (j < 16 ? qs[j] & 15 : qs[j-16] >> 4) | ((qh32 >> j) & 1) << 4
+ *   A weight matrix [rows][K] is rows * K/32 blocks, row-major (row = output).
+ */
+#ifndef CK_H
+#define CK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CK_OK 0
+#define CK_EINVAL (-1)        /* bad pointer, size, position or alignment */
+#define CK_ENOSPC (-2)        /* workspace too small */
+#define CK_EUNSUPPORTED (-3)  /* shape not built into this library */
+#define CK_EHIP (-4)          /* the HIP runtime reported an error */
+
+#define CK_MAX_SEQS 16
+#define CK_QK 32
+#define CK_Q8_0_BYTES 34
+#define CK_Q5_0_BYTES 22
+
+/* KV cache, fp32.
+ * page_size == 0: contiguous, k/v are [m][kv_heads][capacity][head_dim]
+ *   (the page's [KV][capacity][head_dim] per sequence, sequences stacked).
+ * page_size  > 0: paged, k/v are pools [num_pages][kv_heads][page_size][head_dim];
+ *   token t of sequence s is in page page_table[s*max_pages_per_seq + t/page_size]
+ *   (device int32, -1 = unmapped) at slot t % page_size. A page id outside
+ *   [0, num_pages) is never dereferenced: the attention of that sequence
+ *   returns NaN. */
+typedef struct ck_kv_cache {
+    float *k;
+    float *v;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t capacity;            /* contiguous: tokens per sequence */
+    int32_t page_size;           /* 0 = contiguous */
+    const int32_t *page_table;   /* device, [m][max_pages_per_seq] */
+    int32_t max_pages_per_seq;
+    int32_t num_pages;
+} ck_kv_cache;
+
+#define CK_VARIANT_CHAIN 0   /* one kernel per step (the unfused chain) */
+#define CK_VARIANT_FUSED 1   /* steps fused, intermediates kept on chip */
+
+typedef struct ck_layer_desc {
+    int32_t D;          /* model width (RMSNorm, Q/K/V input, O output) */
+    int32_t H;          /* query heads */
+    int32_t KV;         /* KV heads; H % KV == 0, query head h reads KV head h*KV/H */
+    int32_t head_dim;   /* even; H*head_dim and D multiples of 32 */
+    int32_t m;          /* tokens, one per sequence, 1..CK_MAX_SEQS */
+    float eps;          /* RMSNorm epsilon */
+    int32_t variant;    /* CK_VARIANT_* */
+    int32_t attn_chunk; /* tokens per attention split; 0 = choose for the GPU */
+} ck_layer_desc;
+
+typedef struct ck_layer_weights {
+    const void *wq;            /* Q5_0 [H*hd][D] */
+    const void *wk;            /* Q5_0 [KV*hd][D] */
+    const void *wv;            /* Q8_0 [KV*hd][D] */
+    const void *wo;            /* Q5_0 [D][H*hd] */
+    const float *bq, *bk, *bv, *bo;   /* biases, each nullable (= no bias) */
+    const float *gamma;        /* RMSNorm weight [D] */
+    const float *rope_cos;     /* [rope_rows][hd/2]: cos of the angle of (position, pair) */
+    const float *rope_sin;     /* [rope_rows][hd/2] */
+    int32_t rope_rows;         /* every position must be < rope_rows */
+} ck_layer_weights;
+
+/* Human-readable name of a return code. */
+const char *ck_strerror(int code);
+
+/* Library version, (major << 16) | minor. */
+int ck_version(void);
+
+/* Step 1 — RMSNorm of m rows of D fp32: y = x * gamma / sqrt(mean(x^2) + eps).
+ * x, y: [m][D]; gamma: [D]. y may alias x. */
+int ck_rmsnorm(const float *x, const float *gamma, float *y, int m, int D,
+               float eps, void *stream);
+
+/* Q8_0 quantization of m rows of K fp32 (K % 32 == 0) into m*K/32 blocks
+ * (the quantization done before every projection; MAIN KERNEL, steps 2-4 and
+ * 8). Per block: d = amax/127, q = round-half-away-from-zero(x * (1/d)) with
+ * fp32 operations, stored scale = binary16(d) rounded to nearest even. */
+int ck_quantize_q8_0(const float *x, void *y, int m, int K, void *stream);
+
+/* Block GEMV (helper "Q5_0 GEMV with inline processing"; step 8 for the O
+ * projection): for each token s < m and row r < rows,
+ *   y[s][r] = sum_b d_w * d_x * (integer block dot) + bias[r] (+ residual[s][r]).
+ * W: [rows][K/32] blocks; xq: [m][K/32] Q8_0 blocks; bias [rows] and residual
+ * [m][rows] nullable; y: [m][rows]; y may alias residual. K % 32 == 0. */
+int ck_gemv_q5_0_q8_0(const void *W, const void *xq, const float *bias,
+                      const float *residual, float *y, int rows, int K, int m,
+                      void *stream);
+int ck_gemv_q8_0_q8_0(const void *W, const void *xq, const float *bias,
+                      const float *residual, float *y, int rows, int K, int m,
+                      void *stream);
+
+/* Step 5 — rotate-half RoPE in place (helper "RoPE application (inline)"):
+ * within every head of q ([m][H][hd]) and k ([m][KV][hd]), element i and
+ * element i + hd/2 are rotated by row pos_host[s] of the tables. q or k may
+ * be NULL. Every pos_host[s] must lie in [0, tab_rows). */
+int ck_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
+            int tab_rows, const int32_t *pos_host, int m, int H, int KV, int hd,
+            void *stream);
+
+/* Step 6 — KV append: the new token's k and v ([m][KV][hd], k already
+ * rotated) are written at position pos_host[s] of sequence s. */
+int ck_kv_append(const ck_kv_cache *kv, const float *k, const float *v,
+                 const int32_t *pos_host, int m, void *stream);
+
+/* Workspace bytes ck_attn_decode_gqa needs for m sequences of at most
+ * max_tokens attended tokens each, with the given split (0 = automatic). */
+size_t ck_attn_workspace_size(int m, int H, int KV, int hd, int max_tokens, int chunk);
+
+/* Step 7 — grouped-query decode attention: for each sequence s and query head
+ * h, softmax(scale * q_h . K_g[t]) . V_g over tokens t <= pos_host[s], with
+ * g = h*KV/H. q, out: [m][H][hd]. Tokens are split into chunks of `chunk`
+ * tokens (0 = automatic), each chunk's online-softmax partial is written to
+ * the workspace and a second pass merges them by log-sum-exp. */
+int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos_host,
+                       float *out, int m, int H, float scale, int chunk,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes ck_decode_layer needs when every position is < max_ctx. */
+size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx);
+
+/* The whole layer, steps 1-8, for m tokens sharing the weights:
+ *   xn = RMSNorm(x); xq = Q8_0(xn); q = Wq xq + bq; k = Wk xq + bk; v = Wv xq + bv
+ *   RoPE(q, k, pos); cache[pos] = (k, v); a = attention over pos + 1 tokens
+ *   out = Wo Q8_0(a) + bo + residual
+ * x, residual, out: [m][D]; residual nullable; out may alias residual but not
+ * x. pos_host: [m] host positions. ws: at least
+ * ck_decode_layer_workspace_size bytes of device memory. */
+int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w,
+                    const ck_kv_cache *kv, const float *x, const float *residual,
+                    const int32_t *pos_host, float *out, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Workspace layout of ck_decode_layer, so that callers (tests) can read the
+ * intermediates after a call: byte offsets into ws, or -1 if the variant does
+ * not keep that intermediate in the workspace. Names: "xn", "xq", "q", "k",
+ * "v", "attn", "aq". */
+long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const char *name);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

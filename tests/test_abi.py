@@ -1,0 +1,135 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/ck.h declares, and its host-side validation rejects bad arguments
+before anything is launched (no GPU needed for any of these calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ck.h")
+
+
+@pytest.fixture(scope="module")
+def ck():
+    from decode_step_attention_layer_amd import ck as ckmod
+
+    if not os.path.exists(ckmod.LIB_PATH):
+        from decode_step_attention_layer_amd import build
+
+        build.build()
+    ckmod.load()
+    return ckmod
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ck_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("ck_rmsnorm", "ck_quantize_q8_0", "ck_gemv_q5_0_q8_0", "ck_gemv_q8_0_q8_0",
+              "ck_rope", "ck_kv_append", "ck_attn_decode_gqa", "ck_decode_layer"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(ck):
+    lib = ctypes.CDLL(ck.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), f"libck.so does not export {n}"
+    assert set(_declared()) == set(ck.EXPORTS)
+
+
+def test_strerror_and_version(ck):
+    assert ck.strerror(0) == "ok"
+    assert ck.strerror(-2) == "workspace too small"
+    assert ck.strerror(-99) == "unknown error"
+    assert ck.ck_version() >= 1
+
+
+FAKE = 1 << 20    # an aligned non-null address; validation fails before any use
+
+
+def test_gemv_validation(ck):
+    L = ck.load()
+    st = None
+    assert L.ck_gemv_q5_0_q8_0(None, FAKE, None, None, FAKE, 4, 64, 1, st) == ck.CK_EINVAL
+    assert L.ck_gemv_q5_0_q8_0(FAKE, FAKE, None, None, FAKE, 4, 48, 1, st) == ck.CK_EINVAL
+    assert L.ck_gemv_q8_0_q8_0(FAKE, FAKE, None, None, FAKE, 0, 64, 1, st) == ck.CK_EINVAL
+    assert L.ck_gemv_q8_0_q8_0(FAKE + 2, FAKE, None, None, FAKE, 4, 64, 1, st) == ck.CK_EINVAL
+    assert L.ck_gemv_q5_0_q8_0(FAKE, FAKE, None, None, FAKE, 4, 64 * 32 * 600, 1, st) == \
+        ck.CK_EUNSUPPORTED
+    assert L.ck_quantize_q8_0(FAKE, FAKE, 1, 33, st) == ck.CK_EINVAL
+    assert L.ck_rmsnorm(FAKE, None, FAKE, 1, 64, 1e-6, st) == ck.CK_EINVAL
+
+
+def test_rope_and_append_validation(ck):
+    L = ck.load()
+    pos = (ctypes.c_int32 * 2)(5, 64)
+    assert L.ck_rope(FAKE, FAKE, FAKE, FAKE, 64, pos, 2, 4, 2, 64, None) == ck.CK_EINVAL
+    assert L.ck_rope(FAKE, FAKE, FAKE, FAKE, 65, pos, 2, 4, 2, 63, None) == ck.CK_EINVAL
+    c = ck.CkKVCache(FAKE, FAKE, 2, 64, 64, 0, None, 0, 0)
+    assert L.ck_kv_append(ctypes.byref(c), FAKE, FAKE, pos, 2, None) == ck.CK_EINVAL   # pos 64
+    c2 = ck.CkKVCache(FAKE, FAKE, 2, 64, 0, 16, None, 4, 10)
+    one = (ctypes.c_int32 * 1)(3)
+    assert L.ck_kv_append(ctypes.byref(c2), FAKE, FAKE, one, 1, None) == ck.CK_EINVAL  # no table
+    many = (ctypes.c_int32 * 17)(*range(17))
+    assert L.ck_kv_append(ctypes.byref(c), FAKE, FAKE, many, 17, None) == ck.CK_EINVAL
+
+
+def test_attention_validation(ck):
+    L = ck.load()
+    pos = (ctypes.c_int32 * 1)(10)
+    c = ck.CkKVCache(FAKE, FAKE, 2, 64, 64, 0, None, 0, 0)
+    # H not a multiple of KV
+    assert L.ck_attn_decode_gqa(FAKE, ctypes.byref(c), pos, FAKE, 1, 5, 0.1, 0, FAKE, 1 << 20,
+                                None) == ck.CK_EINVAL
+    # group of 9 query heads per KV head is not built
+    assert L.ck_attn_decode_gqa(FAKE, ctypes.byref(c), pos, FAKE, 1, 18, 0.1, 0, FAKE, 1 << 20,
+                                None) == ck.CK_EUNSUPPORTED
+    # workspace too small
+    assert L.ck_attn_decode_gqa(FAKE, ctypes.byref(c), pos, FAKE, 1, 4, 0.1, 0, FAKE, 16,
+                                None) == ck.CK_ENOSPC
+    assert ck.ck_attn_workspace_size(1, 4, 2, 64, 11, 0) > 16
+
+
+def test_layer_validation_and_workspace(ck):
+    L = ck.load()
+    good = ck.layer_desc(256, 4, 2, 64, 1)
+    assert ck.ck_decode_layer_workspace_size(good, 17) > 0
+    for bad in (ck.layer_desc(250, 4, 2, 64, 1), ck.layer_desc(256, 5, 2, 64, 1),
+                ck.layer_desc(256, 4, 2, 64, 0), ck.layer_desc(256, 4, 2, 64, 17),
+                ck.layer_desc(256, 4, 2, 64, 1, variant=7)):
+        assert ck.ck_decode_layer_workspace_size(bad, 17) == 0
+    # offsets of the intermediates are distinct, aligned and inside the workspace
+    n = ck.ck_decode_layer_workspace_size(good, 17)
+    offs = [ck.ck_decode_layer_ws_offset(good, 17, k) for k in ("xn", "xq", "q", "k", "v", "attn", "aq")]
+    assert len(set(offs)) == len(offs) and all(o % 256 == 0 and 0 <= o < n for o in offs)
+    assert ck.ck_decode_layer_ws_offset(good, 17, "nope") == -1
+    # the workspace bound holds for every context length up to max_ctx
+    for mx in (1, 64, 65, 4097, 8192, 8193):
+        assert ck.ck_decode_layer_workspace_size(ck.layer_desc(3584, 28, 4, 128, 1), mx) > 0
+    w = ck.CkLayerWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, 64)
+    c = ck.CkKVCache(FAKE, FAKE, 2, 64, 64, 0, None, 0, 0)
+    pos = (ctypes.c_int32 * 1)(16)
+    # x aliasing out is rejected; workspace too small is ENOSPC
+    assert L.ck_decode_layer(ctypes.byref(good), ctypes.byref(w), ctypes.byref(c), FAKE, FAKE,
+                             pos, FAKE, FAKE, n, None) == ck.CK_EINVAL
+    assert L.ck_decode_layer(ctypes.byref(good), ctypes.byref(w), ctypes.byref(c), FAKE, FAKE,
+                             pos, FAKE + 4096, FAKE, 256, None) == ck.CK_ENOSPC
+    pos_bad = (ctypes.c_int32 * 1)(64)
+    assert L.ck_decode_layer(ctypes.byref(good), ctypes.byref(w), ctypes.byref(c), FAKE, FAKE,
+                             pos_bad, FAKE + 4096, FAKE, n, None) == ck.CK_EINVAL
+
+
+def test_no_fallback_when_library_missing(tmp_path, monkeypatch):
+    from decode_step_attention_layer_amd import ck as ckmod
+
+    monkeypatch.setattr(ckmod, "_lib", None)
+    monkeypatch.setattr(ckmod, "LIB_PATH", str(tmp_path / "libck.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        ckmod.load()
