@@ -1,14 +1,23 @@
 """GPU parity of the whole decode layer (ck_decode_layer) against the oracle,
 at the five workloads' full sizes and in the configuration the benchmark times.
 
-Per layer the oracle runs on the same input the GPU layer received, and:
-  * out within 2e-3 x RMS(out), and the attention branch (out - residual)
-    within 2e-3 x RMS(branch), so a wrong branch cannot hide behind x;
-  * the Q8_0 bytes of xn and of the attention output are bit-exact with the
-    oracle quantizer applied to the GPU's own fp32 values (identical input);
+Per layer, with the oracle run on the same input the GPU layer received:
+  * out within 2e-3 x RMS(out) (the benchmark spec's bound), and the attention
+    branch (out - residual) within 1e-2 x RMS(branch): two independently
+    rounded pipelines quantize slightly different fp32 values, so an 8-bit
+    activation code can land on the other side of a rounding boundary, and
+    each such code moves the branch by up to ~1.5e-3 of its RMS;
+  * stage by stage on identical inputs (the GPU's own intermediates read back
+    from the workspace): xn within 1e-5, Q8_0 bytes of xn and of the attention
+    output bit-exact, q/k/v within 1e-5, attention within 1e-4, O projection
+    within 1e-5 of the branch RMS;
   * every KV-cache slot except the appended one is byte-identical (NaN poison
-    included) and the appended k, v match within tolerance.
-End to end, the GPU chain of all layers matches the oracle chain.
+    included), and the appended slot holds exactly the k, v the layer computed.
+End to end, the GPU chain of all layers matches the independent oracle chain
+within max(2e-3, 3 x the oracle's own +-1-ulp noise floor) x RMS: chaining
+quantized layers turns last-bit differences into occasional code flips in
+every layer, and the oracle chained against itself with +-1-ulp nudges shows
+how far that alone carries (about 5e-3 after the 28 layers of the 7B shape).
 """
 import numpy as np
 import pytest
@@ -20,6 +29,16 @@ from gpu_helpers import assert_close_rms, cuda, host, rms
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+BRANCH_TOL = 1e-2
+
+
+def gcache_row(cfg, L, s, g, t):
+    """Float offset of (sequence, KV head, token) in the cache layout of ck.h."""
+    hd, KV = cfg.hd, cfg.KV
+    if cfg.page_size:
+        page = int(L.host["table"][s, t // cfg.page_size])
+        return ((page * KV + g) * cfg.page_size + t % cfg.page_size) * hd
+    return ((s * KV + g) * cfg.capacity + t) * hd
 
 
 def _ws_read(ws, off, nbytes, dtype):
@@ -39,7 +58,7 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
     ws = stack.workspace(desc)
     ws.fill_(0xFF)                       # NaN poison for any read of unwritten workspace
     off = {n: ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, n)
-           for n in ("xn", "xq", "attn", "aq")}
+           for n in ("xn", "xq", "q", "k", "v", "attn", "aq")}
     m, D, H, KV, hd = cfg.m, cfg.D, cfg.H, cfg.KV, cfg.hd
     dims = dict(D=D, H=H, KV=KV, hd=hd, m=m, eps=cfg.eps)
     cos, sin = synth.rope_for(cfg)
@@ -63,25 +82,44 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
         got = host(out)
         wts = dict(L.host, rope_cos=cos, rope_sin=sin)
 
-        # oracle on the GPU's own input
+        # oracle on the GPU's own input: spec bound on the output; the
+        # branch bound allows a few 8-bit activation codes that land on the
+        # other side of a rounding boundary (each moves the branch by at most
+        # d_a * max|Wo| ~ 1.5e-3 of its RMS); stage-wise checks below are exact
         oc = ocache(L, L.host["k"].copy(), L.host["v"].copy())
         ref, tr = oracle.decode_layer(dims, wts, oc, x_host, x_host, pos, trace=True)
         tag = f"{name} layer {li}"
         assert_close_rms(got, ref, TOL, tag + " out")
-        assert_close_rms(got - x_host, ref - x_host, TOL, tag + " branch")
+        assert_close_rms(got - x_host, ref - x_host, BRANCH_TOL, tag + " branch")
 
-        # bit-exact quantized activations on identical fp32 input
+        # stage by stage on identical inputs (the GPU's own intermediates)
         xn = _ws_read(ws, off["xn"], 4 * m * D, np.float32).reshape(m, D)
-        xq = _ws_read(ws, off["xq"], m * D // 32 * 34, np.uint8)
+        xq = _ws_read(ws, off["xq"], m * D // 32 * 34, np.uint8).reshape(m, -1)
+        gq = _ws_read(ws, off["q"], 4 * m * H * hd, np.float32).reshape(m, H * hd)
+        gkk = _ws_read(ws, off["k"], 4 * m * KV * hd, np.float32).reshape(m, KV * hd)
+        gvv = _ws_read(ws, off["v"], 4 * m * KV * hd, np.float32).reshape(m, KV * hd)
         at = _ws_read(ws, off["attn"], 4 * m * H * hd, np.float32).reshape(m, H * hd)
-        aq = _ws_read(ws, off["aq"], m * H * hd // 32 * 34, np.uint8)
-        assert np.array_equal(xq, oracle.quantize_q8_0(xn.reshape(-1))), tag + " xq bytes"
-        assert np.array_equal(aq, oracle.quantize_q8_0(at.reshape(-1))), tag + " aq bytes"
-        assert_close_rms(xn, tr["xn"], 1e-5, tag + " xn")
-        assert_close_rms(at, tr["attn"], TOL, tag + " attn")
-
-        # the cache: only the appended slot changed, and it holds k, v
+        aq = _ws_read(ws, off["aq"], m * H * hd // 32 * 34, np.uint8).reshape(m, -1)
         gk, gv = host(L.tensors["k"]), host(L.tensors["v"])
+        gcache = ocache(L, gk, gv)
+        for s in range(m):
+            xs = x_host[s]
+            assert_close_rms(xn[s], oracle.rmsnorm(xs, wts["gamma"], cfg.eps), 1e-5, tag + " xn")
+            assert np.array_equal(xq[s], oracle.quantize_q8_0(xn[s])), tag + " xq bytes"
+            q0 = oracle.gemv_q5_0(wts["wq"], xq[s], wts["bq"], None, H * hd, D)
+            k0 = oracle.gemv_q5_0(wts["wk"], xq[s], wts["bk"], None, KV * hd, D)
+            v0 = oracle.gemv_q8_0(wts["wv"], xq[s], wts["bv"], None, KV * hd, D)
+            q1, k1 = oracle.rope(q0, k0, cos, sin, pos[s], H, KV, hd)
+            assert_close_rms(gq[s], q1, 1e-5, tag + " q")
+            assert_close_rms(gkk[s], k1, 1e-5, tag + " k")
+            assert_close_rms(gvv[s], v0, 1e-5, tag + " v")
+            a0 = oracle.attention(gq[s], gcache, s, pos[s] + 1, H)
+            assert_close_rms(at[s], a0, 1e-4, tag + " attention")
+            assert np.array_equal(aq[s], oracle.quantize_q8_0(at[s])), tag + " aq bytes"
+            o0 = oracle.gemv_q5_0(wts["wo"], aq[s], wts["bo"], xs, D, H * hd)
+            assert_close_rms(got[s] - xs, o0 - xs, 1e-5, tag + " O projection")
+
+        # the cache: only the appended slot changed, and it holds this token's k, v
         for gc, oc_arr, orig in ((gk, oc.k, L.host["k"]), (gv, oc.v, L.host["v"])):
             appended = ~((oc_arr == orig) | (np.isnan(oc_arr) & np.isnan(orig)))
             assert appended.sum() == m * KV * hd, tag + " oracle appended slot count"
@@ -89,15 +127,42 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
                                   orig.view(np.uint32)[~appended]), \
                 tag + " cache: a slot other than the appended one changed"
             assert_close_rms(gc[appended], oc_arr[appended], TOL, tag + " appended k/v")
+        for s in range(m):
+            for g in range(KV):
+                row = gcache_row(cfg, L, s, g, pos[s])
+                assert np.array_equal(gk.reshape(-1)[row:row + hd], gkk[s, g * hd:(g + 1) * hd])
+                assert np.array_equal(gv.reshape(-1)[row:row + hd], gvv[s, g * hd:(g + 1) * hd])
 
         # independent oracle chain for the end-to-end check
         oc2 = ocache(L, L.host["k"].copy(), L.host["v"].copy())
         x_orc = oracle.decode_layer(dims, wts, oc2, x_orc, x_orc, pos)
         x_host = got
         x_gpu_in = out
-    e2e = assert_close_rms(x_host, x_orc, TOL, f"{name} end to end")
+    # End to end over a stack, the bound is the oracle's own rounding-noise
+    # floor: the oracle chained again with every layer input nudged by +-1 ulp
+    # (the size of fp32 reassociation differences) diverges from itself by this
+    # much, because nudged values cross Q8_0 rounding boundaries in every layer.
+    bound = TOL
+    if len(stack.layers) > 1:
+        floor = _noise_floor(stack, dims, cos, sin, ocache, x_orc)
+        bound = max(TOL, 3.0 * floor)
+        print(f"{name}: oracle +-1 ulp noise floor over {len(stack.layers)} layers {floor:.2e}")
+    e2e = assert_close_rms(x_host, x_orc, bound, f"{name} end to end")
     print(f"{name} variant={variant}: layers={len(stack.layers)} e2e rel err {e2e:.2e} "
-          f"(branch RMS {rms(x_orc - stack.x0_host):.3f})")
+          f"(bound {bound:.2e}, branch RMS {rms(x_orc - stack.x0_host):.3f})")
+
+
+def _noise_floor(stack, dims, cos, sin, ocache, x_clean):
+    g = np.random.default_rng(1234)
+    x = stack.x0_host.copy()
+    for L in stack.layers:
+        up = g.random(x.shape) < 0.5
+        x = np.where(up, np.nextafter(x, np.float32(np.inf)),
+                     np.nextafter(x, np.float32(-np.inf))).astype(np.float32)
+        c = ocache(L, L.host["k"].copy(), L.host["v"].copy())
+        x = oracle.decode_layer(dims, dict(L.host, rope_cos=cos, rope_sin=sin), c, x, x,
+                                stack.pos)
+    return float(np.max(np.abs(x.astype(np.float64) - x_clean))) / rms(x_clean)
 
 
 @pytest.mark.parametrize("variant", [0, 1], ids=["chain", "fused"])
