@@ -27,7 +27,8 @@ CK_VARIANT_FUSED = 1
 EXPORTS = (
     "ck_strerror", "ck_version", "ck_rmsnorm", "ck_quantize_q8_0", "ck_gemv_q5_0_q8_0",
     "ck_gemv_q8_0_q8_0", "ck_rope", "ck_kv_append", "ck_attn_workspace_size",
-    "ck_attn_decode_gqa", "ck_decode_layer_workspace_size", "ck_decode_layer",
+    "ck_attn_decode_gqa", "ck_attn_partial", "ck_attn_merge", "ck_decode_layer_workspace_size",
+    "ck_decode_layer",
     "ck_decode_layer_ws_offset",
 )
 
@@ -87,6 +88,8 @@ def load():
         "ck_kv_append": ([ctypes.POINTER(CkKVCache), P, P, IP, I, P], I),
         "ck_attn_workspace_size": ([I, I, I, I, I, I], S),
         "ck_attn_decode_gqa": ([P, ctypes.POINTER(CkKVCache), IP, P, I, I, F, I, P, S, P], I),
+        "ck_attn_partial": ([P, ctypes.POINTER(CkKVCache), IP, I, I, F, I, P, S, P], I),
+        "ck_attn_merge": ([P, S, IP, I, I, I, I, I, P, P, P], I),
         "ck_decode_layer_workspace_size": ([ctypes.POINTER(CkLayerDesc), I], S),
         "ck_decode_layer": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                              ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, P], I),
@@ -185,6 +188,17 @@ def ck_attn_decode_gqa(q, cache: CkKVCache, pos, out, m, H, scale, chunk, ws, ws
     _check(load().ck_attn_decode_gqa(_ptr(q), ctypes.byref(cache), _pos(pos), _ptr(out), m, H,
                                      scale, chunk, _ptr(ws), ws_bytes, _stream(stream)),
            "ck_attn_decode_gqa")
+
+
+def ck_attn_partial(q, cache: CkKVCache, pos, m, H, scale, chunk, partials, nbytes,
+                    stream=None):
+    _check(load().ck_attn_partial(_ptr(q), ctypes.byref(cache), _pos(pos), m, H, scale, chunk,
+                                  _ptr(partials), nbytes, _stream(stream)), "ck_attn_partial")
+
+
+def ck_attn_merge(partials, nbytes, pos, m, H, KV, hd, chunk, out, out_q8=None, stream=None):
+    _check(load().ck_attn_merge(_ptr(partials), nbytes, _pos(pos), m, H, KV, hd, chunk, _ptr(out),
+                                _ptr(out_q8), _stream(stream)), "ck_attn_merge")
 
 
 def layer_desc(D, H, KV, head_dim, m=1, eps=1e-6, variant=CK_VARIANT_FUSED, attn_chunk=0):

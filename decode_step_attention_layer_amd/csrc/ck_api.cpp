@@ -205,8 +205,43 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
     AttnPlan pl = attn_plan(m, c.kv_heads, mx, chunk);
+    if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream));
+}
+
+int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, int m, int H,
+                    float scale, int chunk, void *partials, size_t bytes, void *stream) {
+    CacheView c;
+    int rc = cache_view(kv, &c);
+    if (rc) return rc;
+    if (!q || !partials || H <= 0 || chunk < 0 || H % c.kv_heads) return CK_EINVAL;
+    if (!al(q, 16) || !al(partials, 16)) return CK_EINVAL;
+    if (!attn_shape_supported(H / c.kv_heads, c.head_dim)) return CK_EUNSUPPORTED;
+    Positions p;
+    int mx;
+    rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
+    if (rc) return rc;
+    AttnPlan pl = attn_plan(m, c.kv_heads, mx, chunk);
+    if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
+    if (bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
+    return hip_rc(launch_attn_partial(q, c, p, m, H, scale, pl, partials, (hipStream_t)stream));
+}
+
+int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, int m, int H,
+                  int KV, int hd, int chunk, float *out, void *out_q8, void *stream) {
+    if (!partials || !out || H <= 0 || KV <= 0 || H % KV || chunk < 0) return CK_EINVAL;
+    if (!al(partials, 16) || !al(out, 16) || (out_q8 && !al(out_q8, 2))) return CK_EINVAL;
+    if (!attn_shape_supported(H / KV, hd)) return CK_EUNSUPPORTED;
+    Positions p;
+    int mx;
+    int rc = read_positions(pos_host, m, 1LL << 30, &p, &mx);
+    if (rc) return rc;
+    AttnPlan pl = attn_plan(m, KV, mx, chunk);
+    if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
+    if (bytes < attn_partials_bytes(m, H, hd, pl.nchunks)) return CK_ENOSPC;
+    return hip_rc(launch_attn_merge(partials, p, m, H, KV, hd, pl, out,
+                                    static_cast<uint8_t *>(out_q8), (hipStream_t)stream));
 }
 
 size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx) {
@@ -250,6 +285,7 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
     rc = read_positions(pos_host, d.m, limit, &p, &mx);
     if (rc) return rc;
     WsLayout L = ws_layout(desc, mx);
+    if (!attn_chunks_supported(L.plan.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, L.plan.nchunks))
         return CK_ENOSPC;
 
@@ -266,36 +302,47 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
     const int HD = d.H * d.head_dim, KD = d.KV * d.head_dim;
     const bool fused = d.variant == CK_VARIANT_FUSED;
 
-    // steps 1-2: RMSNorm and the one Q8_0 quantization shared by Q, K and V
     hipError_t e;
-    if (fused) {
-        e = launch_rmsnorm_quant(x, w->gamma, xn, xq, d.m, d.D, d.eps, st);
+    if (fused && qkv_shape_supported(d.D, d.m)) {
+        // steps 1-6 in one kernel: RMSNorm, Q8_0, Q/K/V projections + bias,
+        // RoPE, KV append
+        e = launch_qkv(x, w->gamma, d.eps, d.D, d.H, d.KV, d.head_dim, d.m,
+                       static_cast<const uint8_t *>(w->wq), static_cast<const uint8_t *>(w->wk),
+                       static_cast<const uint8_t *>(w->wv), w->bq, w->bk, w->bv, w->rope_cos,
+                       w->rope_sin, p, c, q, k, v, xn, xq, st);
+        if (e != hipSuccess) return CK_EHIP;
     } else {
-        e = launch_rmsnorm(x, w->gamma, xn, d.m, d.D, d.eps, st);
-        if (e == hipSuccess) e = launch_quantize_q8_0(xn, xq, (long long)d.m * (d.D / CK_QK), st);
-    }
-    if (e != hipSuccess) return CK_EHIP;
+        // steps 1-2: RMSNorm and the one Q8_0 quantization shared by Q, K and V
+        if (fused) {
+            e = launch_rmsnorm_quant(x, w->gamma, xn, xq, d.m, d.D, d.eps, st);
+        } else {
+            e = launch_rmsnorm(x, w->gamma, xn, d.m, d.D, d.eps, st);
+            if (e == hipSuccess)
+                e = launch_quantize_q8_0(xn, xq, (long long)d.m * (d.D / CK_QK), st);
+        }
+        if (e != hipSuccess) return CK_EHIP;
 
-    // steps 2-4: Q, K (Q5_0) and V (Q8_0) projections with bias, one launch
-    GemvArgs g;
-    memset(&g, 0, sizeof(g));
-    g.nseg = 3;
-    g.seg[0] = GemvSeg{static_cast<const uint8_t *>(w->wq), w->bq, nullptr, q, HD, 1, 0, 0};
-    g.seg[1] = GemvSeg{static_cast<const uint8_t *>(w->wk), w->bk, nullptr, k, KD, 1, 0, 0};
-    g.seg[2] = GemvSeg{static_cast<const uint8_t *>(w->wv), w->bv, nullptr, v, KD, 0, 0, 0};
-    g.xq = xq;
-    g.K = d.D;
-    g.m = d.m;
-    if ((e = launch_gemv(g, st)) != hipSuccess) return CK_EHIP;
+        // steps 2-4: Q, K (Q5_0) and V (Q8_0) projections with bias, one launch
+        GemvArgs g;
+        memset(&g, 0, sizeof(g));
+        g.nseg = 3;
+        g.seg[0] = GemvSeg{static_cast<const uint8_t *>(w->wq), w->bq, nullptr, q, HD, 1, 0, 0};
+        g.seg[1] = GemvSeg{static_cast<const uint8_t *>(w->wk), w->bk, nullptr, k, KD, 1, 0, 0};
+        g.seg[2] = GemvSeg{static_cast<const uint8_t *>(w->wv), w->bv, nullptr, v, KD, 0, 0, 0};
+        g.xq = xq;
+        g.K = d.D;
+        g.m = d.m;
+        if ((e = launch_gemv(g, st)) != hipSuccess) return CK_EHIP;
 
-    // steps 5-6: RoPE on q and k, then the append of (k, v) at pos
-    if (fused) {
-        e = launch_rope_append(q, k, v, w->rope_cos, w->rope_sin, c, p, d.m, d.H, st);
-    } else {
-        e = launch_rope(q, k, w->rope_cos, w->rope_sin, p, d.m, d.H, d.KV, d.head_dim, st);
-        if (e == hipSuccess) e = launch_kv_append(c, k, v, p, d.m, st);
+        // steps 5-6: RoPE on q and k, then the append of (k, v) at pos
+        if (fused) {
+            e = launch_rope_append(q, k, v, w->rope_cos, w->rope_sin, c, p, d.m, d.H, st);
+        } else {
+            e = launch_rope(q, k, w->rope_cos, w->rope_sin, p, d.m, d.H, d.KV, d.head_dim, st);
+            if (e == hipSuccess) e = launch_kv_append(c, k, v, p, d.m, st);
+        }
+        if (e != hipSuccess) return CK_EHIP;
     }
-    if (e != hipSuccess) return CK_EHIP;
 
     // step 7: attention over pos + 1 tokens (fused: the merge also quantizes)
     const float scale = 1.0f / sqrtf((float)d.head_dim);

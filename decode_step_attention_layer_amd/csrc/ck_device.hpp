@@ -95,6 +95,40 @@ __device__ __forceinline__ void quantize_q8_0_half(float x, int &code, uint16_t 
     dbits = __half_as_ushort(__float2half_rn(d));
 }
 
+// Q8_0 of one 32-element block held as 4 consecutive values by each of 8
+// lanes (an aligned 8-lane group); the same arithmetic as quantize_q8_0_half.
+// Returns this lane's 4 codes packed in a dword and the block's scale bits.
+__device__ __forceinline__ void quantize_q8_0_x4_codes(float4 v, uint32_t &packed,
+                                                       uint16_t &dbits) {
+#pragma clang fp contract(off)
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = group_max<8>(a);
+    const float d = a / 127.0f;
+    const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    const float xs[4] = {v.x, v.y, v.z, v.w};
+    packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float s = xs[i] * id;
+        float t = truncf(s);
+        if (fabsf(s - t) >= 0.5f) t += copysignf(1.0f, s);
+        packed |= ((uint32_t)(uint8_t)(int8_t)(int)t) << (8 * i);
+    }
+    dbits = __half_as_ushort(__float2half_rn(d));
+}
+
+// The same, stored into the Q8_0 block `blk` (lane `sub` of the 8 writes
+// codes 4*sub..4*sub+3; lane 0 also writes the scale).
+__device__ __forceinline__ void quantize_q8_0_x4(float4 v, uint8_t *blk, int sub) {
+    uint32_t packed;
+    uint16_t dbits;
+    quantize_q8_0_x4_codes(v, packed, dbits);
+    uint16_t *dst = reinterpret_cast<uint16_t *>(blk + 2 + 4 * sub);
+    dst[0] = (uint16_t)(packed & 0xFFFF);
+    dst[1] = (uint16_t)(packed >> 16);
+    if (sub == 0) *reinterpret_cast<uint16_t *>(blk) = dbits;
+}
+
 // -------------------------------------------------------- block fields -----
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));

@@ -63,6 +63,12 @@ hipError_t launch_quantize_q8_0(const float *x, uint8_t *y, long long nblocks, h
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float *xn, uint8_t *xq,
                                 int m, int D, float eps, hipStream_t st);
 bool gemv_shape_supported(int K);
+bool qkv_shape_supported(int D, int m);
+hipError_t launch_qkv(const float *x, const float *gamma, float eps, int D, int H, int KV, int hd,
+                      int m, const uint8_t *wq, const uint8_t *wk, const uint8_t *wv,
+                      const float *bq, const float *bk, const float *bv, const float *cos_tab,
+                      const float *sin_tab, const Positions &pos, const CacheView &c, float *q,
+                      float *k, float *v, float *xn, uint8_t *xq, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
 hipError_t launch_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
                        const Positions &pos, int m, int H, int KV, int hd, hipStream_t st);
@@ -80,7 +86,14 @@ struct AttnPlan {
 AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req);
 int attn_max_chunks(int m, int KV, int max_tokens, int chunk_req);
 bool attn_shape_supported(int G, int hd);
+bool attn_chunks_supported(int nchunks);
 size_t attn_partials_bytes(int m, int H, int hd, int nchunks);
+hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positions &pos, int m,
+                               int H, float scale, const AttnPlan &plan, void *partials,
+                               hipStream_t st);
+hipError_t launch_attn_merge(const void *partials, const Positions &pos, int m, int H, int KV,
+                             int hd, const AttnPlan &plan, float *out, uint8_t *out_q8,
+                             hipStream_t st);
 hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
                             void *partials, hipStream_t st);

@@ -7,16 +7,21 @@
 // "prefill_attn_a.rs" paged decode launchers; the GQA packing (one workgroup
 // serves all query heads of a KV head) follows its paged_decode_attn_*_gqa.
 //
-// Pass 1 (k_attn_partial), grid (chunk, KV head, sequence): a workgroup walks
-// its chunk in tiles of 64 tokens. K and V tiles are staged through LDS with
-// coalesced 16-byte loads (prefetched into registers one tile ahead), so every
-// K/V byte is read from HBM once for the whole query group. Scores: wave w
-// owns heads w and w+4, lane = token, q read through the scalar unit; online
-// softmax keeps a running max per head and per-lane partial sums. P.V: thread
-// = (4 output dims, token subset), p broadcast from LDS. The chunk's
-// (max, sum, unnormalized output) per head goes to the partials buffer.
-// Pass 2 (k_attn_merge), grid (head, sequence): log-sum-exp merge of the
-// chunks, optionally followed by Q8_0 quantization of the head's output.
+// One kernel, grid (chunk, KV head, sequence). A workgroup walks its chunk of
+// tokens in tiles of 64: the K and V tiles are staged through LDS with
+// coalesced 16-byte loads (the next tile's loads are in flight while the
+// current one is computed), so each K/V byte is read from HBM once for the
+// whole query group. Scores: wave j owns query head j of the group, lane =
+// token, q (pre-scaled by scale * log2 e) broadcast from LDS; the online
+// softmax keeps a running max per head (wave-uniform) and per-lane sums.
+// P.V: thread = (4 output dims, token subset), p broadcast from LDS. The
+// chunk's (max, sum, unnormalized output) per head goes to the partials.
+// A second kernel, one workgroup per (head, sequence), merges the chunks by
+// log-sum-exp with all chunks' loads in flight at once, writes the attention
+// output and, optionally, its Q8_0 blocks. (Merging inside the first kernel
+// by the last workgroup to finish needs an agent-scope release per
+// workgroup, an L2 write-back on this GPU; measured, it cost more than the
+// kernel boundary.)
 #include "ck_device.hpp"
 #include "ck_internal.hpp"
 
@@ -24,9 +29,10 @@ namespace ck {
 
 namespace {
 
-constexpr int kAttnThreads = 256;
-constexpr int kTile = 64;  // tokens per tile
+constexpr int kTile = 64;   // tokens per tile
 constexpr int kMaxG = 8;
+constexpr int kMaxChunks = 4096;
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
     const float *q;       // [m][H][HD]
@@ -36,26 +42,28 @@ struct AttnArgs {
     int chunk;            // tokens per chunk, multiple of kTile
     int nchunks;
     int H;
-    float *po;            // [m][KV][nchunks][G][HD]
-    float *pml;           // [m][KV][nchunks][G][2]  (max, sum)
+    float *po;            // [m][KV][nchunks][G][HD]  unnormalized outputs
+    float *pml;           // [m][KV][nchunks][G][2]   (max in log2 units, sum)
 };
 
 template <int HD>
 struct Smem {
     static constexpr int stride = HD + 4;  // padded row: conflict-free b128 reads
-    float kv[2 * kTile * stride];           // K tile, then V tile
+    float kv[2 * kTile * stride];           // K tile, then V tile; reused by reductions
+    float q[kMaxG * HD];
     float p[kTile * kMaxG];
     float alpha[kMaxG];
     int bad;
 };
 
-template <int HD, int G>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
+template <int HD, int G, bool PAGED>
+__global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
     static_assert(HD % 64 == 0 && G >= 1 && G <= kMaxG, "shape");
+    constexpr int NT = G > 4 ? 512 : 256;            // threads
     constexpr int C4 = HD / 4;                       // float4 columns per row
-    constexpr int NLD = kTile * C4 / kAttnThreads;   // float4 loads per thread per tile (K or V)
-    constexpr int ROWS_PER_LD = kAttnThreads / C4;   // rows covered by one load round
-    constexpr int NTG = kAttnThreads / C4;           // token groups in the P.V phase
+    constexpr int NLD = kTile * C4 / NT;             // float4 loads per thread per tile (K or V)
+    constexpr int ROWS_PER_LD = NT / C4;             // rows covered by one load round
+    constexpr int NTG = NT / C4;                     // token groups in the P.V phase
     constexpr int TPG = kTile / NTG;                 // tokens per group per tile
     constexpr int S = Smem<HD>::stride;
     __shared__ Smem<HD> sm;
@@ -63,7 +71,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     const int cidx = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
     const int L = a.pos.p[s] + 1;
     const int t0 = cidx * a.chunk;
-    if (t0 >= L) return;                             // the merge skips this chunk
+    if (t0 >= L) return;                             // beyond this sequence: no chunk
     const int t1 = min(L, t0 + a.chunk);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,12 +80,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     const float *qg = a.q + ((size_t)s * H + (size_t)g * G) * HD;
 
     float *sk = sm.kv;
-    float *sv_ = sm.kv + kTile * S;
+    float *sv = sm.kv + kTile * S;
+    // q of the group into LDS, pre-scaled so that scores are in log2 units
+    const float qs = a.scale * kLog2e;
+    for (int i = tid; i < G * HD; i += NT) sm.q[i] = qg[i] * qs;
     if (tid == 0) sm.bad = 0;
     __syncthreads();
 
     // loader geometry: this thread loads column ld_col of rows ld_row + i*ROWS_PER_LD
     const int ld_col = tid % C4, ld_row = tid / C4;
+    const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
     float4 kreg[NLD], vreg[NLD];
     auto fetch = [&](int st) {
 #pragma unroll
@@ -85,8 +97,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
             const int t = st + ld_row + i * ROWS_PER_LD;
             long long off = -1;
             if (t < t1) {
-                off = cache_row(a.c, s, g, t);
-                if (off < 0) sm.bad = 1;
+                if constexpr (PAGED) {
+                    off = cache_row(a.c, s, g, t);
+                    if (off < 0) sm.bad = 1;
+                } else {
+                    off = (long long)(seq_base + (size_t)t * HD);
+                }
             }
             if (off >= 0) {
                 kreg[i] = *reinterpret_cast<const float4 *>(a.c.k + off + 4 * ld_col);
@@ -97,22 +113,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
             }
         }
     };
-    auto stash = [&]() {
-#pragma unroll
-        for (int i = 0; i < NLD; i++) {
-            const int r = ld_row + i * ROWS_PER_LD;
-            *reinterpret_cast<float4 *>(&sk[r * S + 4 * ld_col]) = kreg[i];
-            *reinterpret_cast<float4 *>(&sv_[r * S + 4 * ld_col]) = vreg[i];
-        }
-    };
 
-    // score-phase state: this wave's heads (w, w+4), running max and per-lane sums
-    constexpr int HPW = (G + 3) / 4;
-    float m_run[HPW], l_lane[HPW];
-#pragma unroll
-    for (int k = 0; k < HPW; k++) { m_run[k] = -INFINITY; l_lane[k] = 0.0f; }
-
-    // P.V state: dims 4*pv_col.., tokens pv_tg + j*NTG of each tile
+    float m_run = -INFINITY, l_lane = 0.0f;          // this wave's head (wave < G)
     const int pv_col = tid % C4, pv_tg = tid / C4;
     float4 o[G];
 #pragma unroll
@@ -120,45 +122,40 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
 
     fetch(t0);
     for (int st = t0; st < t1; st += kTile) {
-        __syncthreads();                 // previous tile fully consumed
-        stash();
-        __syncthreads();
-        if (st + kTile < t1) fetch(st + kTile);   // next tile's loads in flight
-
-        // ---- scores, one token per lane, heads w and w+4
-        const int tok = st + lane;
-        float sc[HPW];
+        __syncthreads();                             // previous tile fully consumed
 #pragma unroll
-        for (int k = 0; k < HPW; k++) sc[k] = 0.0f;
-        const float *krow = &sk[lane * S];
-#pragma unroll 4
-        for (int d = 0; d < HD; d += 4) {
-            const float4 kk = *reinterpret_cast<const float4 *>(krow + d);
-#pragma unroll
-            for (int k = 0; k < HPW; k++) {
-                const int j = wave + 4 * k;
-                if (j < G) {
-                    const float *qj = qg + (size_t)j * HD + d;
-                    sc[k] = fmaf(kk.x, qj[0], sc[k]);
-                    sc[k] = fmaf(kk.y, qj[1], sc[k]);
-                    sc[k] = fmaf(kk.z, qj[2], sc[k]);
-                    sc[k] = fmaf(kk.w, qj[3], sc[k]);
-                }
-            }
+        for (int i = 0; i < NLD; i++) {
+            const int r = ld_row + i * ROWS_PER_LD;
+            *reinterpret_cast<float4 *>(&sk[r * S + 4 * ld_col]) = kreg[i];
+            *reinterpret_cast<float4 *>(&sv[r * S + 4 * ld_col]) = vreg[i];
         }
-#pragma unroll
-        for (int k = 0; k < HPW; k++) {
-            const int j = wave + 4 * k;
-            if (j < G) {
-                const float sv = tok < t1 ? sc[k] * a.scale : -INFINITY;
-                const float m_new = fmaxf(m_run[k], wave_max(sv));
-                const float alpha = __expf(m_run[k] - m_new);
-                const float p = __expf(sv - m_new);
-                l_lane[k] = l_lane[k] * alpha + p;
-                m_run[k] = m_new;
-                sm.p[lane * kMaxG + j] = p;
-                if (lane == 0) sm.alpha[j] = alpha;
+        __syncthreads();
+        if (st + kTile < t1) fetch(st + kTile);      // next tile's loads in flight
+
+        // ---- scores: wave j = head j, lane = token
+        if (wave < G) {
+            const float *krow = &sk[lane * S];
+            const float *qrow = &sm.q[wave * HD];
+            float sc0 = 0.0f, sc1 = 0.0f;
+#pragma unroll 8
+            for (int d = 0; d < HD; d += 8) {
+                const float4 k0 = *reinterpret_cast<const float4 *>(krow + d);
+                const float4 k1 = *reinterpret_cast<const float4 *>(krow + d + 4);
+                const float4 q0 = *reinterpret_cast<const float4 *>(qrow + d);
+                const float4 q1 = *reinterpret_cast<const float4 *>(qrow + d + 4);
+                sc0 = fmaf(k0.x, q0.x, sc0); sc0 = fmaf(k0.y, q0.y, sc0);
+                sc0 = fmaf(k0.z, q0.z, sc0); sc0 = fmaf(k0.w, q0.w, sc0);
+                sc1 = fmaf(k1.x, q1.x, sc1); sc1 = fmaf(k1.y, q1.y, sc1);
+                sc1 = fmaf(k1.z, q1.z, sc1); sc1 = fmaf(k1.w, q1.w, sc1);
             }
+            const float sv2 = (st + lane < t1) ? sc0 + sc1 : -INFINITY;
+            const float m_new = fmaxf(m_run, wave_max(sv2));
+            const float alpha = exp2f(m_run - m_new);
+            const float p = exp2f(sv2 - m_new);
+            l_lane = l_lane * alpha + p;
+            m_run = m_new;
+            sm.p[lane * kMaxG + wave] = p;
+            if (lane == 0) sm.alpha[wave] = alpha;
         }
         __syncthreads();
 
@@ -168,10 +165,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
             const float al = sm.alpha[j];
             o[j].x *= al; o[j].y *= al; o[j].z *= al; o[j].w *= al;
         }
-#pragma unroll 2
+#pragma unroll
         for (int i = 0; i < TPG; i++) {
             const int r = pv_tg + i * NTG;
-            const float4 vv = *reinterpret_cast<const float4 *>(&sv_[r * S + 4 * pv_col]);
+            const float4 vv = *reinterpret_cast<const float4 *>(&sv[r * S + 4 * pv_col]);
             const float4 p0 = *reinterpret_cast<const float4 *>(&sm.p[r * kMaxG]);
             const float4 p1 = *reinterpret_cast<const float4 *>(&sm.p[r * kMaxG + 4]);
             const float pj[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -186,35 +183,39 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a) {
     }
     __syncthreads();
 
-    // ---- reduce the P.V token groups through LDS (reusing the K/V tiles)
-    float *red = sm.kv;   // [NTG][G][HD] floats
-    static_assert(NTG * G * HD <= 2 * kTile * (HD + 4), "reduction buffer");
+    // ---- reduce the P.V token groups: first the groups inside a wave (xor
+    // shuffles over the C4-lane groups), then one group per wave through LDS
+    // (reusing the K/V tiles)
+    constexpr int NW = NT / kWave;
+    float *red = sm.kv;   // [NW][G][HD]
+    static_assert(NW * G * HD <= 2 * kTile * (HD + 4), "reduction buffer");
 #pragma unroll
-    for (int j = 0; j < G; j++)
-        *reinterpret_cast<float4 *>(&red[(pv_tg * G + j) * HD + 4 * pv_col]) = o[j];
-    float lsum[HPW];
+    for (int j = 0; j < G; j++) {
 #pragma unroll
-    for (int k = 0; k < HPW; k++) lsum[k] = wave_sum(l_lane[k]);
+        for (int sh = C4; sh < kWave; sh <<= 1) {
+            o[j].x += __shfl_xor(o[j].x, sh);
+            o[j].y += __shfl_xor(o[j].y, sh);
+            o[j].z += __shfl_xor(o[j].z, sh);
+            o[j].w += __shfl_xor(o[j].w, sh);
+        }
+        if (lane < C4) *reinterpret_cast<float4 *>(&red[(wave * G + j) * HD + 4 * lane]) = o[j];
+    }
+    const float lsum = wave_sum(l_lane);
     __syncthreads();
 
-    const size_t part = ((size_t)s * KV + g) * a.nchunks + cidx;
-    const bool bad = sm.bad != 0;
-    for (int e = tid; e < G * HD; e += kAttnThreads) {
+    const size_t grp = (size_t)s * KV + g;
+    const size_t part = grp * a.nchunks + cidx;
+    for (int e = tid; e < G * HD; e += NT) {
         float acc = 0.0f;
 #pragma unroll
-        for (int tg = 0; tg < NTG; tg++) acc += red[tg * G * HD + e];
+        for (int w = 0; w < NW; w++) acc += red[w * G * HD + e];
         a.po[part * G * HD + e] = acc;
     }
-    if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < HPW; k++) {
-            const int j = wave + 4 * k;
-            if (j < G) {
-                a.pml[(part * G + j) * 2 + 0] = m_run[k];
-                a.pml[(part * G + j) * 2 + 1] = bad ? NAN : lsum[k];
-            }
-        }
+    if (wave < G && lane == 0) {
+        a.pml[(part * G + wave) * 2 + 0] = m_run;
+        a.pml[(part * G + wave) * 2 + 1] = sm.bad ? NAN : lsum;
     }
+
 }
 
 struct MergeArgs {
@@ -226,56 +227,114 @@ struct MergeArgs {
     uint8_t *out_q8;     // nullable: [m][H*HD/32] Q8_0 blocks
 };
 
+constexpr int kMergeThreads = 256;
+
+// One workgroup per (head, sequence). Phase 1: one chunk per thread reads
+// (max, sum), the block reduces the global max M and the denominator, and
+// the weights 2^(m_c - M) go to LDS. Phase 2: thread (4 dims, chunk group)
+// accumulates its chunks' outputs with independent loads in flight; the
+// chunk groups are summed with a shuffle inside the wave and through LDS.
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_merge(MergeArgs a) {
-    const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
+    constexpr int C4 = HD / 4;
+    constexpr int CG = kMergeThreads / C4;        // chunk groups
+    constexpr int NW = kMergeThreads / kWave;
+    __shared__ float w_s[kMaxChunks];
+    __shared__ float red[NW];
+    __shared__ float4 part[NW][C4];
+    const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int G = a.H / a.KV, g = h / G, j = h % G;
     const int L = a.pos.p[s] + 1;
     const int nc = (L + a.chunk - 1) / a.chunk;
     const size_t base = ((size_t)s * a.KV + g) * a.nchunks;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; c++) M = fmaxf(M, a.pml[((base + c) * G + j) * 2]);
-    float num = 0.0f, den = 0.0f;
-    for (int c = 0; c < nc; c++) {
+
+    float mx = -INFINITY;
+    for (int c = tid; c < nc; c += kMergeThreads) mx = fmaxf(mx, a.pml[((base + c) * G + j) * 2]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; i++) M = fmaxf(M, red[i]);
+    __syncthreads();
+    float den = 0.0f;
+    for (int c = tid; c < nc; c += kMergeThreads) {
         const size_t pj = (base + c) * G + j;
-        const float w = __expf(a.pml[pj * 2] - M);
+        const float w = exp2f(a.pml[pj * 2] - M);
+        w_s[c] = w;
         den = fmaf(w, a.pml[pj * 2 + 1], den);
-        num = fmaf(w, a.po[pj * HD + d], num);
     }
-    const float v = num / den;
-    const size_t oi = ((size_t)s * a.H + h) * HD + d;
-    a.out[oi] = v;
-    if (a.out_q8) {
-        int code;
-        uint16_t dbits;
-        quantize_q8_0_half(v, code, dbits);
-        uint8_t *blk = a.out_q8 + (oi / kQK) * kQ8Bytes;
-        blk[2 + (d & 31)] = (uint8_t)(int8_t)code;
-        if ((d & 31) == 0) {
-            blk[0] = (uint8_t)(dbits & 0xFF);
-            blk[1] = (uint8_t)(dbits >> 8);
+    den = wave_sum(den);
+    if (lane == 0) red[wave] = den;
+    __syncthreads();
+    float D = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW; i++) D += red[i];
+
+    const int d4 = tid % C4, cg = tid / C4;
+    float4 n0 = make_float4(0.f, 0.f, 0.f, 0.f), n1 = n0;
+    auto fma4 = [](float w, float4 v, float4 acc) {
+        return make_float4(fmaf(w, v.x, acc.x), fmaf(w, v.y, acc.y), fmaf(w, v.z, acc.z),
+                           fmaf(w, v.w, acc.w));
+    };
+    auto ld = [&](int c) {
+        return *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
+    };
+    int c = cg;
+    for (; c + CG < nc; c += 2 * CG) {
+        const float4 v0 = ld(c), v1 = ld(c + CG);
+        n0 = fma4(w_s[c], v0, n0);
+        n1 = fma4(w_s[c + CG], v1, n1);
+    }
+    if (c < nc) n0 = fma4(w_s[c], ld(c), n0);
+    float4 acc = make_float4(n0.x + n1.x, n0.y + n1.y, n0.z + n1.z, n0.w + n1.w);
+#pragma unroll
+    for (int sh = C4; sh < kWave; sh <<= 1) {
+        acc.x += __shfl_xor(acc.x, sh);
+        acc.y += __shfl_xor(acc.y, sh);
+        acc.z += __shfl_xor(acc.z, sh);
+        acc.w += __shfl_xor(acc.w, sh);
+    }
+    if (lane < C4) part[wave][lane] = acc;
+    __syncthreads();
+    if (tid < C4) {
+        float4 t = part[0][tid];
+#pragma unroll
+        for (int w = 1; w < NW; w++) {
+            const float4 u = part[w][tid];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
         }
+        const float inv = 1.0f / D;
+        const float4 v = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+        const size_t oi = ((size_t)s * a.H + h) * HD + 4 * tid;
+        *reinterpret_cast<float4 *>(&a.out[oi]) = v;
+        if (a.out_q8) quantize_q8_0_x4(v, a.out_q8 + (oi / kQK) * kQ8Bytes, tid & 7);
     }
 }
 
 template <int HD, int G>
-hipError_t launch_partial(const AttnArgs &a, int m, hipStream_t st) {
-    hipLaunchKernelGGL((k_attn_partial<HD, G>), dim3(a.nchunks, a.c.kv_heads, m),
-                       dim3(kAttnThreads), 0, st, a);
+hipError_t launch_t(const AttnArgs &a, int m, bool paged, hipStream_t st) {
+    constexpr int NT = G > 4 ? 512 : 256;
+    const dim3 grid(a.nchunks, a.c.kv_heads, m);
+    if (paged)
+        hipLaunchKernelGGL((k_attn<HD, G, true>), grid, dim3(NT), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_attn<HD, G, false>), grid, dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 
 template <int HD>
-hipError_t launch_partial_g(const AttnArgs &a, int G, int m, hipStream_t st) {
+hipError_t launch_g(const AttnArgs &a, int G, int m, bool paged, hipStream_t st) {
     switch (G) {
-        case 1: return launch_partial<HD, 1>(a, m, st);
-        case 2: return launch_partial<HD, 2>(a, m, st);
-        case 3: return launch_partial<HD, 3>(a, m, st);
-        case 4: return launch_partial<HD, 4>(a, m, st);
-        case 5: return launch_partial<HD, 5>(a, m, st);
-        case 6: return launch_partial<HD, 6>(a, m, st);
-        case 7: return launch_partial<HD, 7>(a, m, st);
-        case 8: return launch_partial<HD, 8>(a, m, st);
+        case 1: return launch_t<HD, 1>(a, m, paged, st);
+        case 2: return launch_t<HD, 2>(a, m, paged, st);
+        case 3: return launch_t<HD, 3>(a, m, paged, st);
+        case 4: return launch_t<HD, 4>(a, m, paged, st);
+        case 5: return launch_t<HD, 5>(a, m, paged, st);
+        case 6: return launch_t<HD, 6>(a, m, paged, st);
+        case 7: return launch_t<HD, 7>(a, m, paged, st);
+        case 8: return launch_t<HD, 8>(a, m, paged, st);
     }
     return hipErrorInvalidValue;
 }
@@ -293,11 +352,15 @@ int num_cus() {
     return n;
 }
 
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
 bool attn_shape_supported(int G, int hd) {
     return G >= 1 && G <= kMaxG && (hd == 64 || hd == 128);
 }
+
+bool attn_chunks_supported(int nchunks) { return nchunks >= 1 && nchunks <= kMaxChunks; }
 
 AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req) {
     AttnPlan p;
@@ -325,14 +388,16 @@ int attn_max_chunks(int m, int KV, int max_tokens, int chunk_req) {
     return by_tile < target ? by_tile : target;
 }
 
+// Workspace of the attention: unnormalized outputs, then (max, sum) per chunk
+// and head; each region 256-byte aligned.
 size_t attn_partials_bytes(int m, int H, int hd, int nchunks) {
-    // o: m*H*nchunks*hd floats, (max, sum): m*H*nchunks*2 floats
-    return sizeof(float) * (size_t)m * H * nchunks * (hd + 2);
+    return up256(sizeof(float) * (size_t)m * H * nchunks * hd) +
+           up256(sizeof(float) * (size_t)m * H * nchunks * 2);
 }
 
-hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
-                            uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
-                            void *partials, hipStream_t st) {
+hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positions &pos, int m,
+                               int H, float scale, const AttnPlan &plan, void *partials,
+                               hipStream_t st) {
     const int G = H / c.kv_heads;
     AttnArgs a;
     a.q = q;
@@ -342,26 +407,42 @@ hipError_t launch_attention(const float *q, const CacheView &c, const Positions 
     a.chunk = plan.chunk;
     a.nchunks = plan.nchunks;
     a.H = H;
-    a.po = reinterpret_cast<float *>(partials);
-    a.pml = a.po + (size_t)m * H * plan.nchunks * c.head_dim;
-    hipError_t e = c.head_dim == 64 ? launch_partial_g<64>(a, G, m, st)
-                                    : launch_partial_g<128>(a, G, m, st);
-    if (e != hipSuccess) return e;
+    uint8_t *base = static_cast<uint8_t *>(partials);
+    a.po = reinterpret_cast<float *>(base);
+    a.pml = reinterpret_cast<float *>(base + up256(sizeof(float) * (size_t)m * H * plan.nchunks *
+                                                   c.head_dim));
+    const bool paged = c.page_size != 0;
+    return c.head_dim == 64 ? launch_g<64>(a, G, m, paged, st) : launch_g<128>(a, G, m, paged, st);
+}
+
+hipError_t launch_attn_merge(const void *partials, const Positions &pos, int m, int H, int KV,
+                             int hd, const AttnPlan &plan, float *out, uint8_t *out_q8,
+                             hipStream_t st) {
+    const uint8_t *base = static_cast<const uint8_t *>(partials);
     MergeArgs b;
-    b.po = a.po;
-    b.pml = a.pml;
+    b.po = reinterpret_cast<const float *>(base);
+    b.pml = reinterpret_cast<const float *>(base + up256(sizeof(float) * (size_t)m * H *
+                                                         plan.nchunks * hd));
     b.pos = pos;
     b.chunk = plan.chunk;
     b.nchunks = plan.nchunks;
     b.H = H;
-    b.KV = c.kv_heads;
+    b.KV = KV;
     b.out = out;
     b.out_q8 = out_q8;
-    if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_merge<64>, dim3(H, m), dim3(64), 0, st, b);
+    if (hd == 64)
+        hipLaunchKernelGGL(k_attn_merge<64>, dim3(H, m), dim3(kMergeThreads), 0, st, b);
     else
-        hipLaunchKernelGGL(k_attn_merge<128>, dim3(H, m), dim3(128), 0, st, b);
+        hipLaunchKernelGGL(k_attn_merge<128>, dim3(H, m), dim3(kMergeThreads), 0, st, b);
     return hipGetLastError();
+}
+
+hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
+                            uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
+                            void *partials, hipStream_t st) {
+    hipError_t e = launch_attn_partial(q, c, pos, m, H, scale, plan, partials, st);
+    if (e != hipSuccess) return e;
+    return launch_attn_merge(partials, pos, m, H, c.kv_heads, c.head_dim, plan, out, out_q8, st);
 }
 
 }  // namespace ck

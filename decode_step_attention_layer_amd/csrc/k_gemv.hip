@@ -15,107 +15,41 @@
 // 16-bit loads when K/32 is odd. Each wavefront loads the weights of its R
 // rows before any arithmetic, keeps them in registers and reuses them for all
 // m tokens. The quantized activations are staged once per workgroup into LDS
-// in a dword-aligned form (codes, scale as fp32, code sum for the Q5_0 offset).
+// in a dword-aligned form (codes, scale as fp32, code sum for the Q5_0 offset)
+// while the weight loads are in flight.
 // Partial sums are reduced across the LPR lanes with DPP / ds_swizzle.
 #include "ck_device.hpp"
+#include "ck_gemv_common.hpp"
 #include "ck_internal.hpp"
 
 namespace ck {
 
 namespace {
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvWaves = kGemvThreads / kWave;
-
-// Words of register storage for one unit of each format.
-template <bool Q5, bool PAIRED>
-struct Fmt {
-    static constexpr int blocks = PAIRED ? 2 : 1;
-    static constexpr int bytes = (Q5 ? kQ5Bytes : kQ8Bytes) * blocks;
-    static constexpr int words = PAIRED ? (Q5 ? 11 : 17) : (Q5 ? 6 : 9);
-};
-
-template <bool Q5, bool PAIRED>
-__device__ __forceinline__ void load_unit(const uint8_t *p, uint32_t *w) {
-    if constexpr (PAIRED) {
-        const uint32_t *p32 = reinterpret_cast<const uint32_t *>(p);
-        if constexpr (Q5) {
-            u32x4a4 a = *reinterpret_cast<const u32x4a4 *>(p32);
-            u32x4a4 b = *reinterpret_cast<const u32x4a4 *>(p32 + 4);
-            u32x3a4 c = *reinterpret_cast<const u32x3a4 *>(p32 + 8);
-            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-            w[8] = c.x; w[9] = c.y; w[10] = c.z;
-        } else {
+// Stages the quantized activations (m * nb Q8_0 blocks) into LDS in a
+// dword-aligned form: codes, fp32 scale, code sum. Ends with a barrier.
+__device__ __forceinline__ void stage_xq(const uint8_t *xq, int nxb, XBlock *xs) {
+    for (int b = threadIdx.x; b < nxb; b += kGemvThreads) {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)b * kQ8Bytes);
+        XBlock xb;
+        xb.d = half_bits_to_float(src[0]);
+        int sum = 0;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                u32x4a4 a = *reinterpret_cast<const u32x4a4 *>(p32 + 4 * i);
-                w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
-            }
-            w[16] = p32[16];
+        for (int i = 0; i < 8; i++) {
+            uint32_t c = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+            xb.c[i] = (int)c;
+            sum = __builtin_amdgcn_sdot4((int)c, 0x01010101, sum, false);
         }
-    } else {
-        const uint16_t *p16 = reinterpret_cast<const uint16_t *>(p);
-        w[0] = p16[0];
-        if constexpr (Q5) {
-            w[1] = (uint32_t)p16[1] | ((uint32_t)p16[2] << 16);
-#pragma unroll
-            for (int i = 0; i < 4; i++) w[2 + i] = (uint32_t)p16[3 + 2 * i] | ((uint32_t)p16[4 + 2 * i] << 16);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; i++) w[1 + i] = (uint32_t)p16[1 + 2 * i] | ((uint32_t)p16[2 + 2 * i] << 16);
-        }
+        xb.sum = sum;
+        xb.pad[0] = xb.pad[1] = 0;
+        xs[b] = xb;
     }
-}
-
-// Activation block staged in LDS / registers.
-struct alignas(16) XBlock {
-    int c[8];     // 32 int8 codes, 4 per dword
-    float d;      // scale
-    int sum;      // sum of the 32 codes
-    int pad[2];
-};
-
-// Dot of one weight unit with its activation blocks.
-template <bool Q5, bool PAIRED>
-__device__ __forceinline__ float unit_dot(const uint32_t *w, const XBlock *x, float acc) {
-    if constexpr (PAIRED && Q5) {
-        int s0 = q5_codes_dot(align2(w[1], w[0]), align2(w[2], w[1]), align2(w[3], w[2]),
-                              align2(w[4], w[3]), align2(w[5], w[4]), x[0].c) - 16 * x[0].sum;
-        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
-        int s1 = q5_codes_dot(w[6], w[7], w[8], w[9], w[10], x[1].c) - 16 * x[1].sum;
-        acc = fmaf((float)s1, half_bits_to_float(w[5] >> 16) * x[1].d, acc);
-    } else if constexpr (PAIRED) {
-        uint32_t c0[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) c0[i] = align2(w[i + 1], w[i]);
-        int s0 = q8_codes_dot(c0, x[0].c);
-        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
-        int s1 = q8_codes_dot(w + 9, x[1].c);
-        acc = fmaf((float)s1, half_bits_to_float(w[8] >> 16) * x[1].d, acc);
-    } else if constexpr (Q5) {
-        int s0 = q5_codes_dot(w[1], w[2], w[3], w[4], w[5], x[0].c) - 16 * x[0].sum;
-        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
-    } else {
-        int s0 = q8_codes_dot(w + 1, x[0].c);
-        acc = fmaf((float)s0, half_bits_to_float(w[0]) * x[0].d, acc);
-    }
-    return acc;
-}
-
-template <int LPR>
-__device__ __forceinline__ float row_reduce(float v) {
-    if constexpr (LPR == 64) {
-        v = group_sum<32>(v);
-        return readlane_f(v, 0) + readlane_f(v, 32);
-    } else {
-        return group_sum<LPR>(v);
-    }
+    __syncthreads();
 }
 
 template <bool Q5, int LPR, int UPL, int R, bool PAIRED>
-__device__ __forceinline__ void gemv_body(const GemvSeg &sg, int wg_in_seg, const XBlock *xs,
-                                          int nb, int m) {
+__device__ __forceinline__ void gemv_body(const GemvSeg &sg, int wg_in_seg, XBlock *xs,
+                                          const uint8_t *xq, int nb, int m) {
     using F = Fmt<Q5, PAIRED>;
     constexpr int RPW = kWave / LPR;  // rows per wave per iteration
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -142,7 +76,10 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int wg_in_seg, cons
         }
     }
 
-    // 2. per token: activation blocks of this lane's units, dots, reduction
+    // 2. the activations into LDS while the weight loads are in flight
+    stage_xq(xq, m * nb, xs);
+
+    // 3. per token: activation blocks of this lane's units, dots, reduction
     for (int s = 0; s < m; s++) {
         XBlock xb[UPL][F::blocks];
 #pragma unroll
@@ -182,30 +119,11 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
     const GemvSeg sg = si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]);
     const int nb = a.K / kQK;
 
-    // stage the quantized activations: dword-aligned codes, fp32 scale, code sum
-    const int nxb = a.m * nb;
-    for (int b = threadIdx.x; b < nxb; b += kGemvThreads) {
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(a.xq + (size_t)b * kQ8Bytes);
-        XBlock xb;
-        xb.d = half_bits_to_float(src[0]);
-        int sum = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            uint32_t c = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
-            xb.c[i] = (int)c;
-            sum = __builtin_amdgcn_sdot4((int)c, 0x01010101, sum, false);
-        }
-        xb.sum = sum;
-        xb.pad[0] = xb.pad[1] = 0;
-        xs[b] = xb;
-    }
-    __syncthreads();
-
     const int wg_in_seg = wg - sg.wg_begin;
     if (sg.is_q5)
-        gemv_body<true, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, nb, a.m);
+        gemv_body<true, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb, a.m);
     else
-        gemv_body<false, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, nb, a.m);
+        gemv_body<false, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb, a.m);
 }
 
 constexpr int kRowsIter = 2;

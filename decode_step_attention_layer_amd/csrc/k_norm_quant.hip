@@ -5,6 +5,7 @@
 // Q8_0 (the quantize_row_q8_0 call before each projection): one 32-element
 // block per half-wave, bit-exact with the fp32 definition (see ck_device.hpp).
 #include "ck_device.hpp"
+#include "ck_gemv_common.hpp"
 #include "ck_internal.hpp"
 
 namespace ck {
@@ -72,28 +73,27 @@ __global__ __launch_bounds__(256) void k_quantize_q8_0(const float *__restrict__
     }
 }
 
-// RMSNorm and quantization of one token per workgroup (used by the layer):
-// the normalized row is written to xn and immediately quantized.
-__global__ __launch_bounds__(kNormThreads) void k_rmsnorm_quant(const float *__restrict__ x,
+// RMSNorm and quantization of one token per workgroup (the layer's fused
+// variant when its single-kernel first half does not fit): the normalized row
+// is written to xn and its Q8_0 blocks to xq, with the same row function as
+// the fused first half.
+__global__ __launch_bounds__(kGemvThreads) void k_rmsnorm_quant(const float *__restrict__ x,
                                                                 const float *__restrict__ gamma,
                                                                 float *__restrict__ xn,
                                                                 uint8_t *__restrict__ xq, int D,
                                                                 float eps) {
-    __shared__ float red[2 * kNormThreads / kWave];
-    const float *xs = x + (size_t)blockIdx.x * D;
-    float *ys = xn + (size_t)blockIdx.x * D;
-    uint8_t *qs = xq + (size_t)blockIdx.x * (D / kQK) * kQ8Bytes;
-    float ss = block_sumsq(xs, D, red);
-    float r = 1.0f / sqrtf(ss / (float)D + eps);
+    __shared__ float red[2 * kGemvThreads / kWave];
+    const size_t s = blockIdx.x;
     const int nb = D / kQK;
-    const int j = threadIdx.x & 31;
-    // every half-wave quantizes whole blocks; D % 32 == 0
-    for (int b = threadIdx.x >> 5; b < nb; b += kNormThreads / 32) {
-        int i = b * kQK + j;
-        float v = xs[i] * r * gamma[i];
-        ys[i] = v;
-        store_q8_0_block(qs + (size_t)b * kQ8Bytes, j, v);
-    }
+    norm_quant_row(x + s * D, gamma, D, eps, red,
+                   [&](int c, float4 v, uint32_t packed, uint16_t dbits, int) {
+                       reinterpret_cast<float4 *>(xn + s * D)[c] = v;
+                       uint8_t *blk = xq + (s * nb + (c >> 3)) * kQ8Bytes;
+                       uint16_t *dst = reinterpret_cast<uint16_t *>(blk + 2 + 4 * (c & 7));
+                       dst[0] = (uint16_t)(packed & 0xFFFF);
+                       dst[1] = (uint16_t)(packed >> 16);
+                       if ((c & 7) == 0) *reinterpret_cast<uint16_t *>(blk) = dbits;
+                   });
 }
 
 }  // namespace
@@ -112,7 +112,7 @@ hipError_t launch_quantize_q8_0(const float *x, uint8_t *y, long long nblocks, h
 
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float *xn, uint8_t *xq, int m,
                                 int D, float eps, hipStream_t st) {
-    hipLaunchKernelGGL(k_rmsnorm_quant, dim3(m), dim3(kNormThreads), 0, st, x, gamma, xn, xq, D,
+    hipLaunchKernelGGL(k_rmsnorm_quant, dim3(m), dim3(kGemvThreads), 0, st, x, gamma, xn, xq, D,
                        eps);
     return hipGetLastError();
 }

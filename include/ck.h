@@ -146,11 +146,29 @@ size_t ck_attn_workspace_size(int m, int H, int KV, int hd, int max_tokens, int 
 /* Step 7 — grouped-query decode attention: for each sequence s and query head
  * h, softmax(scale * q_h . K_g[t]) . V_g over tokens t <= pos_host[s], with
  * g = h*KV/H. q, out: [m][H][hd]. Tokens are split into chunks of `chunk`
- * tokens (0 = automatic), each chunk's online-softmax partial is written to
- * the workspace and a second pass merges them by log-sum-exp. */
+ * tokens (0 = automatic); each chunk's online-softmax partial goes to the
+ * workspace (at least ck_attn_workspace_size bytes, any contents) and a
+ * second kernel merges them by log-sum-exp. Calls that share a workspace must
+ * not overlap in time. */
 int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos_host,
                        float *out, int m, int H, float scale, int chunk,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* The two passes of ck_attn_decode_gqa as separate calls, for callers that
+ * produce or merge partials themselves (e.g. token-sharded caches: partials of
+ * several shards merged in one pass). ck_attn_partial writes, per chunk of
+ * `chunk` tokens and query head, the chunk's running max (log2 units), sum of
+ * exponentials and unnormalized output into `partials` (layout: outputs
+ * [m][KV][nchunks][H/KV][hd] fp32, then (max, sum) pairs, each region
+ * 256-byte aligned; nchunks is fixed by (m, KV, max pos + 1, chunk)).
+ * ck_attn_merge combines them by log-sum-exp into out ([m][H][hd]) and, when
+ * out_q8 is not NULL, also writes the Q8_0 blocks of out (the quantization
+ * done before the O projection). Both validate like ck_attn_decode_gqa; the
+ * merge must see the same pos_host, m, H, KV, hd and chunk as the partial. */
+int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, int m, int H,
+                    float scale, int chunk, void *partials, size_t bytes, void *stream);
+int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, int m, int H,
+                  int KV, int hd, int chunk, float *out, void *out_q8, void *stream);
 
 /* Workspace bytes ck_decode_layer needs when every position is < max_ctx. */
 size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx);

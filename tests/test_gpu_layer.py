@@ -2,15 +2,15 @@
 at the five workloads' full sizes and in the configuration the benchmark times.
 
 Per layer, with the oracle run on the same input the GPU layer received:
-  * out within 2e-3 x RMS(out) (the benchmark spec's bound), and the attention
-    branch (out - residual) within 1e-2 x RMS(branch): two independently
-    rounded pipelines quantize slightly different fp32 values, so an 8-bit
-    activation code can land on the other side of a rounding boundary, and
-    each such code moves the branch by up to ~1.5e-3 of its RMS;
+  * out and the attention output within 2e-3 x RMS (the north-star bound);
+    the normalized input differs from the oracle's only in its last bits, so
+    every Q8_0 code of xq that differs must be a rounding-boundary flip (off
+    by one, both scaled values within 1% of a quantum of the boundary); the
+    branch (out - residual) error is reported;
   * stage by stage on identical inputs (the GPU's own intermediates read back
     from the workspace): xn within 1e-5, Q8_0 bytes of xn and of the attention
     output bit-exact, q/k/v within 1e-5, attention within 1e-4, O projection
-    within 1e-5 of the branch RMS;
+    within 1e-5 of the branch RMS plus two ulps of the output;
   * every KV-cache slot except the appended one is byte-identical (NaN poison
     included), and the appended slot holds exactly the k, v the layer computed.
 End to end, the GPU chain of all layers matches the independent oracle chain
@@ -29,7 +29,6 @@ from gpu_helpers import assert_close_rms, cuda, host, rms
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-BRANCH_TOL = 1e-2
 
 
 def gcache_row(cfg, L, s, g, t):
@@ -82,15 +81,9 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
         got = host(out)
         wts = dict(L.host, rope_cos=cos, rope_sin=sin)
 
-        # oracle on the GPU's own input: spec bound on the output; the
-        # branch bound allows a few 8-bit activation codes that land on the
-        # other side of a rounding boundary (each moves the branch by at most
-        # d_a * max|Wo| ~ 1.5e-3 of its RMS); stage-wise checks below are exact
         oc = ocache(L, L.host["k"].copy(), L.host["v"].copy())
         ref, tr = oracle.decode_layer(dims, wts, oc, x_host, x_host, pos, trace=True)
         tag = f"{name} layer {li}"
-        assert_close_rms(got, ref, TOL, tag + " out")
-        assert_close_rms(got - x_host, ref - x_host, BRANCH_TOL, tag + " branch")
 
         # stage by stage on identical inputs (the GPU's own intermediates)
         xn = _ws_read(ws, off["xn"], 4 * m * D, np.float32).reshape(m, D)
@@ -117,7 +110,25 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
             assert_close_rms(at[s], a0, 1e-4, tag + " attention")
             assert np.array_equal(aq[s], oracle.quantize_q8_0(at[s])), tag + " aq bytes"
             o0 = oracle.gemv_q5_0(wts["wo"], aq[s], wts["bo"], xs, D, H * hd)
-            assert_close_rms(got[s] - xs, o0 - xs, 1e-5, tag + " O projection")
+            # 1e-5 of the branch for the dot, plus the rounding of out = x + branch
+            # at the output's magnitude (two fp32 ulps)
+            bound = 1e-5 * rms(o0.astype(np.float64) - xs) + 2 * np.spacing(np.abs(o0))
+            assert np.all(np.abs(got[s].astype(np.float64) - o0) <= bound), tag + " O projection"
+
+        # oracle on the GPU's own input (an independently rounded pipeline):
+        # the output and the attention output within the benchmark spec's bound;
+        # the normalized input differs only in its last bits, so every xq code
+        # that differs from the oracle's must be a rounding-boundary flip. A
+        # flip shifts q, k, v by about one quantum of one input, so downstream
+        # values (attention, its Q8_0 codes, the branch) legitimately differ by
+        # more than last bits; their exactness is the stage-by-stage check above.
+        assert_close_rms(got, ref, TOL, tag + " out")
+        nflip = 0
+        for s in range(m):
+            nflip += _check_flips(xq[s], tr["xq"][s], xn[s], tr["xn"][s], tag + " xq")
+            assert_close_rms(at[s], tr["attn"][s], TOL, tag + " attention (independent)")
+        br = assert_close_rms(got - x_host, ref - x_host, 1.0, tag + " branch")
+        print(f"{tag}: xq boundary flips {nflip}, branch rel err {br:.2e}")
 
         # the cache: only the appended slot changed, and it holds this token's k, v
         for gc, oc_arr, orig in ((gk, oc.k, L.host["k"]), (gv, oc.v, L.host["v"])):
@@ -150,6 +161,36 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
     e2e = assert_close_rms(x_host, x_orc, bound, f"{name} end to end")
     print(f"{name} variant={variant}: layers={len(stack.layers)} e2e rel err {e2e:.2e} "
           f"(bound {bound:.2e}, branch RMS {rms(x_orc - stack.x0_host):.3f})")
+
+
+def _q8_parts(b):
+    b = np.ascontiguousarray(b).reshape(-1, 34)
+    d = b[:, :2].copy().view("<f2")[:, 0].astype(np.float64)
+    return d, b[:, 2:].view(np.int8).astype(np.int64)
+
+
+def _check_flips(gpu_bytes, orc_bytes, gpu_vals, orc_vals, tag):
+    """Q8_0 blocks from two pipelines whose fp32 inputs differ in the last
+    bits: scales may differ by one binary16 step, codes by one, and only where
+    both pipelines' scaled values sit within 1% of a quantum of the rounding
+    boundary. Returns the number of differing codes."""
+    dg, qg = _q8_parts(gpu_bytes)
+    do, qo = _q8_parts(orc_bytes)
+    step = np.spacing(np.maximum(dg, do).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(dg - do) <= step), tag + ": scale differs by more than one fp16 step"
+    assert np.abs(qg - qo).max(initial=0) <= 1, tag + ": a code differs by more than one"
+    vg = np.asarray(gpu_vals, np.float64).reshape(-1, 32)
+    vo = np.asarray(orc_vals, np.float64).reshape(-1, 32)
+    ag = np.abs(vg).max(axis=1, keepdims=True)
+    ao = np.abs(vo).max(axis=1, keepdims=True)
+    sg = np.where(ag > 0, vg * 127.0 / np.where(ag > 0, ag, 1), 0.0)
+    so = np.where(ao > 0, vo * 127.0 / np.where(ao > 0, ao, 1), 0.0)
+    flip = qg != qo
+    if flip.any():
+        assert np.all(np.abs(sg - so)[flip] < 0.01), tag + ": flip from a large value difference"
+        frac = np.abs(so[flip]) - np.floor(np.abs(so[flip]))
+        assert np.all(np.abs(frac - 0.5) < 0.01), tag + ": flip away from a rounding boundary"
+    return int(flip.sum())
 
 
 def _noise_floor(stack, dims, cos, sin, ocache, x_clean):

@@ -280,7 +280,7 @@ def test_attention(m, H, KV, hd, L, chunk, paged):
 
     out = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
     nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, chunk)
-    ws = torch.full((nws // 4,), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)   # counters start at zero
     ck.ck_attn_decode_gqa(_t(q, dev), c, pos, out, m, H, 1.0 / np.sqrt(hd), chunk, ws, nws)
     _sync()
     got = host(out).reshape(m, H * hd)
@@ -304,12 +304,63 @@ def test_attention_split_count_independent():
     for chunk in (64, 192, 1024, 4160):
         out = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
         nws = ck.ck_attn_workspace_size(m, H, KV, hd, L, chunk)
-        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
         ck.ck_attn_decode_gqa(q, c, pos, out, m, H, 1.0 / np.sqrt(hd), chunk, ws, nws)
         _sync()
         outs.append(host(out))
     for o in outs[1:]:
         assert_close_rms(o, outs[0], 1e-5, "split count")
+
+
+def test_attention_two_pass_entry_points_match():
+    """ck_attn_partial + ck_attn_merge give exactly what ck_attn_decode_gqa
+    gives (same kernels), and the merge's Q8_0 output is the quantizer's."""
+    dev = cuda()
+    ck = _ck()
+    m, H, KV, hd, L = 3, 32, 8, 128, 900
+    cfg, k, v, table, pos, oc = _caches(True, m, KV, hd, L, 6)
+    pos = [p - 1 for p in pos]
+    c, kd, vd, td = _dev_cache(ck, dev, cfg, k, v, table)
+    q = _t(synth.seeded_vector(5, m * H * hd), dev)
+    import torch
+
+    nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, 0)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    a = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    bq = torch.empty(m * H * hd // 32 * 34, dtype=torch.uint8, device=dev)
+    ck.ck_attn_decode_gqa(q, c, pos, a, m, H, 1.0 / np.sqrt(hd), 0, ws, nws)
+    ck.ck_attn_partial(q, c, pos, m, H, 1.0 / np.sqrt(hd), 0, ws, nws)
+    ck.ck_attn_merge(ws, nws, pos, m, H, KV, hd, 0, b, bq)
+    _sync()
+    assert torch.equal(a, b)
+    assert np.array_equal(host(bq), oracle.quantize_q8_0(host(b)))
+
+
+def test_attention_workspace_reuse():
+    """Counters return to zero after every call: ten calls on one workspace
+    give the same result as the first."""
+    dev = cuda()
+    ck = _ck()
+    m, H, KV, hd, L = 2, 32, 8, 128, 3000
+    cfg, k, v, table, pos, oc = _caches(True, m, KV, hd, L, 8)
+    pos = [p - 1 for p in pos]          # attend the filled tokens only
+    c, kd, vd, td = _dev_cache(ck, dev, cfg, k, v, table)
+    q = _t(synth.seeded_vector(4, m * H * hd), dev)
+    import torch
+
+    nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, 128)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    outs = []
+    for _ in range(10):
+        out = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
+        ck.ck_attn_decode_gqa(q, c, pos, out, m, H, 1.0 / np.sqrt(hd), 128, ws, nws)
+        outs.append(out)
+    _sync()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    ref = oracle.attention(host(q)[:H * hd], oc, 0, pos[0] + 1, H)
+    assert_close_rms(host(outs[0])[:H * hd], ref, 1e-4, "attention reuse")
 
 
 def test_attention_unmapped_page_gives_nan():
@@ -324,7 +375,7 @@ def test_attention_unmapped_page_gives_nan():
 
     out = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
     nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, 0)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
     pos = [30] * m
     ck.ck_attn_decode_gqa(_t(synth.seeded_vector(3, m * H * hd), dev), c, pos, out, m, H, 0.125,
                           0, ws, nws)
