@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=sorted(DESCRIBE))
-    ap.add_argument("--variant", default="fused", choices=["fused", "chain"])
+    ap.add_argument("--variant", default="fused", choices=["fused", "chain", "persistent"])
     ap.add_argument("--eager", action="store_true", help="launch from Python, no graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU-baseline sample")
@@ -73,7 +73,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ck.load()
     cfg = synth.CONFIGS[args.config]
-    variant = ck.CK_VARIANT_FUSED if args.variant == "fused" else ck.CK_VARIANT_CHAIN
+    variant = {"fused": ck.CK_VARIANT_FUSED, "chain": ck.CK_VARIANT_CHAIN,
+               "persistent": ck.CK_VARIANT_PERSISTENT}[args.variant]
+    persistent = variant == ck.CK_VARIANT_PERSISTENT
     t0 = time.time()
     stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu)
     log(f"[bench] {args.config}: {stack.nlayers} layers on device in {time.time() - t0:.1f}s")
@@ -84,34 +86,47 @@ def main():
         replicas = min(8, math.ceil(3 * MALL_BYTES / step_bytes))
     stacks = [stack] + [stack.clone() for _ in range(replicas - 1)]
     desc = stack.desc(variant)
-    wss = [s.workspace(desc) for s in stacks]
     stream = torch.cuda.current_stream()
+    if persistent:
+        # every layer of the step in one persistent kernel (ck_decode_step)
+        wss = [s.step_workspace(desc) for s in stacks]
+        outs = [torch.empty((cfg.m, cfg.D), dtype=torch.float32, device="cuda:0")
+                for _ in stacks]
+
+        def one_step(j):
+            return stacks[j].decode_step(desc, wss[j], out=outs[j])
+    else:
+        # one ck_decode_layer call per layer
+        wss = [s.workspace(desc) for s in stacks]
+        outs = [s.bufs[(stack.nlayers - 1) % 2] for s in stacks]
+
+        def one_step(j):
+            return stacks[j].step(desc, wss[j])
 
     # ---- eager warm-up (also the reference for the graph replays)
     for i in range(max(1, args.warmup)):
-        for s, ws in zip(stacks, wss):
-            s.step(desc, ws)
+        for j in range(replicas):
+            one_step(j)
     torch.cuda.synchronize()
-    ref = stacks[0].bufs[(stack.nlayers - 1) % 2].clone()
+    ref = outs[0].clone()
 
     graphs = []
     if not args.eager:
-        for s, ws in zip(stacks, wss):
+        for j in range(replicas):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                s.step(desc, ws)
+                one_step(j)
             graphs.append(g)
         for g in graphs:
             g.replay()
         torch.cuda.synchronize()
-        out = stacks[0].bufs[(stack.nlayers - 1) % 2]
-        assert torch.equal(out, ref), "graph replay differs from the eager step"
+        assert torch.equal(outs[0], ref), "graph replay differs from the eager step"
 
     def run_step(i):
         if graphs:
             graphs[i % replicas].replay()
         else:
-            stacks[i % replicas].step(desc, wss[i % replicas])
+            one_step(i % replicas)
 
     for i in range(args.warmup):
         run_step(i)
@@ -126,11 +141,20 @@ def main():
     ms_step = ms / args.steps
     us_layer = ms_step * 1e3 / stack.nlayers
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    out = stacks[0].bufs[(stack.nlayers - 1) % 2]
-    assert torch.isfinite(out).all(), "non-finite layer output"
+    assert torch.isfinite(outs[0]).all(), "non-finite layer output"
+    if persistent:
+        for s, ws in zip(stacks, wss):
+            assert s.step_status(desc, ws) == 0, "a persistent step timed out"
     log(f"[bench] step {ms_step * 1e3:.2f} us, {us_layer:.2f} us/layer, {value:.0f} GB/s")
 
-    roof = roofline(args, stack, desc, wss[0], nbytes)
+    if persistent:
+        # the step is one kernel (k_step, after a counter-clearing kernel of
+        # about a microsecond): its launches are the timed region itself
+        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / PEAK_GBS, 4), "traffic": None, "kernel": "k_step",
+                "us_per_launch": round(ms_step * 1e3, 3), "bytes_per_launch": step_bytes}
+    else:
+        roof = roofline(args, stack, desc, wss[0], nbytes)
     cpu = None if args.no_cpu else cpu_baseline(args, stack, nbytes)
 
     line = {

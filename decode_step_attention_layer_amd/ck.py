@@ -23,13 +23,16 @@ CK_EHIP = -4
 CK_MAX_SEQS = 16
 CK_VARIANT_CHAIN = 0
 CK_VARIANT_FUSED = 1
+CK_VARIANT_PERSISTENT = 2
+CK_MAX_STEP_LAYERS = 32
 
 EXPORTS = (
     "ck_strerror", "ck_version", "ck_rmsnorm", "ck_quantize_q8_0", "ck_gemv_q5_0_q8_0",
     "ck_gemv_q8_0_q8_0", "ck_rope", "ck_kv_append", "ck_attn_workspace_size",
     "ck_attn_decode_gqa", "ck_attn_partial", "ck_attn_merge", "ck_decode_layer_workspace_size",
     "ck_decode_layer",
-    "ck_decode_layer_ws_offset",
+    "ck_decode_layer_ws_offset", "ck_decode_step_workspace_size", "ck_decode_step",
+    "ck_decode_step_status_offset",
 )
 
 
@@ -74,6 +77,9 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"libck.so not built: {LIB_PATH} is missing "
                            "(run python -m decode_step_attention_layer_amd.build)")
+    # torch first: libck.so then binds to the HIP runtime torch loaded, so that
+    # both share one runtime (devices, streams, graph capture)
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     IP = ctypes.POINTER(ctypes.c_int32)
@@ -95,6 +101,10 @@ def load():
                              ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, P], I),
         "ck_decode_layer_ws_offset": ([ctypes.POINTER(CkLayerDesc), I, ctypes.c_char_p],
                                       ctypes.c_long),
+        "ck_decode_step_workspace_size": ([ctypes.POINTER(CkLayerDesc), I, I], S),
+        "ck_decode_step": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
+                            ctypes.POINTER(CkKVCache), I, P, IP, P, P, S, P], I),
+        "ck_decode_step_status_offset": ([ctypes.POINTER(CkLayerDesc), I], ctypes.c_long),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -223,3 +233,23 @@ def ck_decode_layer(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache
     _check(load().ck_decode_layer(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(cache),
                                   _ptr(x), _ptr(residual), _pos(pos), _ptr(out), _ptr(ws),
                                   ws_bytes, _stream(stream)), "ck_decode_layer")
+
+
+def ck_decode_step_workspace_size(desc: CkLayerDesc, layers: int, max_ctx: int) -> int:
+    return int(load().ck_decode_step_workspace_size(ctypes.byref(desc), layers, max_ctx))
+
+
+def ck_decode_step_status_offset(desc: CkLayerDesc, layers: int) -> int:
+    return int(load().ck_decode_step_status_offset(ctypes.byref(desc), layers))
+
+
+def ck_decode_step(desc: CkLayerDesc, weights, caches, x, pos, out, ws, ws_bytes, stream=None):
+    """weights, caches: sequences of CkLayerWeights / CkKVCache, one per layer
+    (or ctypes arrays of them)."""
+    n = len(weights)
+    if len(caches) != n:
+        raise ValueError("one cache per layer")
+    wa = weights if isinstance(weights, ctypes.Array) else (CkLayerWeights * n)(*weights)
+    ca = caches if isinstance(caches, ctypes.Array) else (CkKVCache * n)(*caches)
+    _check(load().ck_decode_step(ctypes.byref(desc), wa, ca, n, _ptr(x), _pos(pos), _ptr(out),
+                                 _ptr(ws), ws_bytes, _stream(stream)), "ck_decode_step")

@@ -91,7 +91,9 @@ int check_desc(const ck_layer_desc *d) {
         return CK_EINVAL;
     if (d->D % CK_QK || (d->H * d->head_dim) % CK_QK || d->head_dim % 2 || d->H % d->KV)
         return CK_EINVAL;
-    if (d->variant != CK_VARIANT_CHAIN && d->variant != CK_VARIANT_FUSED) return CK_EINVAL;
+    if (d->variant != CK_VARIANT_CHAIN && d->variant != CK_VARIANT_FUSED &&
+        d->variant != CK_VARIANT_PERSISTENT)
+        return CK_EINVAL;
     if (d->attn_chunk < 0 || !(d->eps >= 0.0f)) return CK_EINVAL;
     if (!attn_shape_supported(d->H / d->KV, d->head_dim)) return CK_EUNSUPPORTED;
     if (!gemv_shape_supported(d->D) || !gemv_shape_supported(d->H * d->head_dim))
@@ -119,6 +121,45 @@ int gemv_common(const void *W, const void *xq, const float *bias, const float *r
     a.K = K;
     a.m = m;
     return hip_rc(launch_gemv(a, (hipStream_t)stream));
+}
+
+// Workspace of a whole step: the ping-pong layer outputs, then either the
+// persistent kernel's buffers or one ck_decode_layer workspace.
+struct StepWs {
+    size_t xbuf, xn, xq, q, k, v, attn, aqx, aq, po, pml, cnt, layer, total;
+    AttnPlan plan;
+    int maxc;
+};
+
+StepWs step_layout(const ck_layer_desc *d, int layers, int max_ctx) {
+    const size_t m = d->m, D = d->D, HD = (size_t)d->H * d->head_dim,
+                 KD = (size_t)d->KV * d->head_dim;
+    StepWs w;
+    memset(&w, 0, sizeof(w));
+    size_t o = 0;
+    w.xbuf = o; o = up256(o + sizeof(float) * 2 * m * D);
+    w.plan = attn_plan(d->m, d->KV, max_ctx, d->attn_chunk);
+    w.maxc = attn_max_chunks(d->m, d->KV, max_ctx, d->attn_chunk);
+    if (d->variant == CK_VARIANT_PERSISTENT) {
+        // intermediates (offsets independent of the layer count and the
+        // context), then the counters (the status word's offset does not
+        // depend on the context), then the partials
+        w.xn = o; o = up256(o + sizeof(float) * m * D);
+        w.xq = o; o = up256(o + m * (D / CK_QK) * CK_Q8_0_BYTES);
+        w.q = o; o = up256(o + sizeof(float) * m * HD);
+        w.k = o; o = up256(o + sizeof(float) * m * KD);
+        w.v = o; o = up256(o + sizeof(float) * m * KD);
+        w.attn = o; o = up256(o + sizeof(float) * m * HD);
+        w.aqx = o; o = up256(o + sizeof(unsigned) * 10 * m * (HD / CK_QK));
+        w.aq = o; o = up256(o + m * (HD / CK_QK) * CK_Q8_0_BYTES);
+        w.cnt = o; o = up256(o + sizeof(unsigned) * step_counter_words(layers, d->m, d->KV));
+        w.po = o; o = up256(o + sizeof(float) * m * d->H * (size_t)w.maxc * d->head_dim);
+        w.pml = o; o = up256(o + sizeof(float) * m * d->H * (size_t)w.maxc * 2);
+    } else {
+        w.layer = o; o = up256(o + ws_layout(d, max_ctx).total);
+    }
+    w.total = o;
+    return w;
 }
 
 }  // namespace
@@ -244,13 +285,148 @@ int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, i
                                     static_cast<uint8_t *>(out_q8), (hipStream_t)stream));
 }
 
+size_t ck_decode_step_workspace_size(const ck_layer_desc *desc, int layers, int max_ctx) {
+    if (check_desc(desc) != CK_OK || max_ctx < 1 || layers < 1 || layers > CK_MAX_STEP_LAYERS)
+        return 0;
+    return step_layout(desc, layers, max_ctx).total;
+}
+
+long ck_decode_step_status_offset(const ck_layer_desc *desc, int layers) {
+    if (check_desc(desc) != CK_OK || layers < 1 || layers > CK_MAX_STEP_LAYERS ||
+        desc->variant != CK_VARIANT_PERSISTENT)
+        return -1;
+    StepWs w = step_layout(desc, layers, 1);
+    return (long)(w.cnt + sizeof(unsigned) * (step_counter_words(layers, desc->m, desc->KV) - 1));
+}
+
+int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                   int layers, const float *x, const int32_t *pos_host, float *out, void *ws,
+                   size_t ws_bytes, void *stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    const ck_layer_desc &d = *desc;
+    if (!w || !kv || layers < 1 || layers > CK_MAX_STEP_LAYERS) return CK_EINVAL;
+    if (!x || !out || !ws || x == out || !al(x, 16) || !al(out, 16) || !al(ws, 256))
+        return CK_EINVAL;
+    CacheView c0;
+    rc = cache_view(&kv[0], &c0);
+    if (rc) return rc;
+    if (c0.kv_heads != d.KV || c0.head_dim != d.head_dim) return CK_EINVAL;
+    for (int l = 0; l < layers; l++) {
+        const ck_layer_weights &wl = w[l];
+        if (!wl.wq || !wl.wk || !wl.wv || !wl.wo || !wl.gamma) return CK_EINVAL;
+        if (!al(wl.wq, 4) || !al(wl.wk, 4) || !al(wl.wv, 4) || !al(wl.wo, 4) || !al(wl.gamma, 16))
+            return CK_EINVAL;
+        CacheView cl;
+        rc = cache_view(&kv[l], &cl);
+        if (rc) return rc;
+        if (cl.kv_heads != c0.kv_heads || cl.head_dim != c0.head_dim ||
+            cl.capacity != c0.capacity || cl.page_size != c0.page_size ||
+            cl.max_pages != c0.max_pages || cl.num_pages != c0.num_pages)
+            return CK_EINVAL;
+    }
+    if (!w[0].rope_cos || !w[0].rope_sin) return CK_EINVAL;
+    Positions p;
+    int mx;
+    long long limit = cache_tokens(&kv[0]);
+    if (w[0].rope_rows < limit) limit = w[0].rope_rows;
+    rc = read_positions(pos_host, d.m, limit, &p, &mx);
+    if (rc) return rc;
+    StepWs L = step_layout(desc, layers, mx);
+    if (ws_bytes < L.total) return CK_ENOSPC;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    float *xbuf = reinterpret_cast<float *>(base + L.xbuf);
+    const size_t md = (size_t)d.m * d.D;
+
+    if (d.variant != CK_VARIANT_PERSISTENT) {
+        const float *cur = x;
+        for (int l = 0; l < layers; l++) {
+            float *dst = (l == layers - 1) ? out : xbuf + (size_t)(l & 1) * md;
+            ck_layer_weights wl = w[l];
+            wl.rope_cos = w[0].rope_cos;
+            wl.rope_sin = w[0].rope_sin;
+            wl.rope_rows = w[0].rope_rows;
+            rc = ck_decode_layer(desc, &wl, &kv[l], cur, cur, pos_host, dst, base + L.layer,
+                                 ws_bytes - L.layer, stream);
+            if (rc) return rc;
+            cur = dst;
+        }
+        return CK_OK;
+    }
+
+    if (!step_supported(d.D, d.H, d.KV, d.head_dim, d.m, L.plan.nchunks)) return CK_EUNSUPPORTED;
+    StepLaunch sl;
+    memset(&sl, 0, sizeof(sl));
+    sl.L = layers;
+    sl.D = d.D;
+    sl.H = d.H;
+    sl.KV = d.KV;
+    sl.hd = d.head_dim;
+    sl.m = d.m;
+    sl.eps = d.eps;
+    sl.scale = 1.0f / sqrtf((float)d.head_dim);
+    sl.cos_tab = w[0].rope_cos;
+    sl.sin_tab = w[0].rope_sin;
+    sl.pos = p;
+    sl.capacity = c0.capacity;
+    sl.page_size = c0.page_size;
+    sl.max_pages = c0.max_pages;
+    sl.num_pages = c0.num_pages;
+    sl.plan = L.plan;
+    sl.x = x;
+    sl.out = out;
+    sl.xbuf = xbuf;
+    sl.q = reinterpret_cast<float *>(base + L.q);
+    sl.k = reinterpret_cast<float *>(base + L.k);
+    sl.v = reinterpret_cast<float *>(base + L.v);
+    sl.attn = reinterpret_cast<float *>(base + L.attn);
+    sl.xn = reinterpret_cast<float *>(base + L.xn);
+    sl.xq = base + L.xq;
+    sl.aqx = reinterpret_cast<unsigned *>(base + L.aqx);
+    sl.aq = base + L.aq;
+    sl.po = reinterpret_cast<float *>(base + L.po);
+    sl.pml = reinterpret_cast<float *>(base + L.pml);
+    sl.cnt = reinterpret_cast<unsigned *>(base + L.cnt);
+    sl.num_cus = num_cus();
+    for (int l = 0; l < layers; l++) {
+        StepLayer &s = sl.layers[l];
+        s.wq = static_cast<const uint8_t *>(w[l].wq);
+        s.wk = static_cast<const uint8_t *>(w[l].wk);
+        s.wv = static_cast<const uint8_t *>(w[l].wv);
+        s.wo = static_cast<const uint8_t *>(w[l].wo);
+        s.bq = w[l].bq;
+        s.bk = w[l].bk;
+        s.bv = w[l].bv;
+        s.bo = w[l].bo;
+        s.gamma = w[l].gamma;
+        s.kc = kv[l].k;
+        s.vc = kv[l].v;
+        s.table = kv[l].page_table;
+    }
+    return hip_rc(launch_step(sl, st));
+}
+
 size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx) {
     if (check_desc(desc) != CK_OK || max_ctx < 1) return 0;
+    if (desc->variant == CK_VARIANT_PERSISTENT) return step_layout(desc, 1, max_ctx).total;
     return ws_layout(desc, max_ctx).total;
 }
 
 long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const char *name) {
     if (check_desc(desc) != CK_OK || max_ctx < 1 || !name) return -1;
+    if (desc->variant == CK_VARIANT_PERSISTENT) {
+        // a one-layer step's workspace
+        StepWs sw = step_layout(desc, 1, max_ctx);
+        if (!strcmp(name, "xn")) return (long)sw.xn;
+        if (!strcmp(name, "xq")) return (long)sw.xq;
+        if (!strcmp(name, "q")) return (long)sw.q;
+        if (!strcmp(name, "k")) return (long)sw.k;
+        if (!strcmp(name, "v")) return (long)sw.v;
+        if (!strcmp(name, "attn")) return (long)sw.attn;
+        if (!strcmp(name, "aq")) return (long)sw.aq;
+        return -1;
+    }
     WsLayout w = ws_layout(desc, max_ctx);
     if (!strcmp(name, "xn")) return (long)w.xn;
     if (!strcmp(name, "xq")) return (long)w.xq;
@@ -267,6 +443,11 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
                     void *ws, size_t ws_bytes, void *stream) {
     int rc = check_desc(desc);
     if (rc) return rc;
+    if (desc->variant == CK_VARIANT_PERSISTENT) {
+        // a one-layer persistent step; its residual is its input
+        if (residual != x) return CK_EINVAL;
+        return ck_decode_step(desc, w, kv, 1, x, pos_host, out, ws, ws_bytes, stream);
+    }
     const ck_layer_desc &d = *desc;
     if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->gamma || !w->rope_cos || !w->rope_sin)
         return CK_EINVAL;

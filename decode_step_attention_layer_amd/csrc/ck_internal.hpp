@@ -98,4 +98,34 @@ hipError_t launch_attention(const float *q, const CacheView &c, const Positions 
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
                             void *partials, hipStream_t st);
 
+// Persistent decode step (k_step.hip): every layer of a step in one launch.
+struct StepLayer {
+    const uint8_t *wq, *wk, *wv, *wo;
+    const float *bq, *bk, *bv, *bo, *gamma;
+    float *kc, *vc;
+    const int32_t *table;
+};
+
+struct StepLaunch {
+    int L, D, H, KV, hd, m;
+    float eps, scale;
+    const float *cos_tab, *sin_tab;
+    Positions pos;
+    int capacity, page_size, max_pages, num_pages;
+    AttnPlan plan;
+    const float *x;
+    float *out;
+    float *xbuf, *q, *k, *v, *po, *pml, *attn, *xn;
+    unsigned *aqx;
+    uint8_t *aq, *xq;
+    unsigned *cnt;
+    int num_cus;
+    StepLayer layers[CK_MAX_STEP_LAYERS];
+};
+
+bool step_supported(int D, int H, int KV, int hd, int m, int nchunks);
+size_t step_counter_words(int L, int m, int KV);
+hipError_t launch_step(const StepLaunch &sl, hipStream_t st);
+int num_cus();
+
 }  // namespace ck

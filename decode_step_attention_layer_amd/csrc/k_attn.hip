@@ -341,7 +341,7 @@ hipError_t launch_g(const AttnArgs &a, int G, int m, bool paged, hipStream_t st)
 
 // Compute units of the current device, queried once per device (the value
 // cannot change; a racing first query writes the same number).
-int num_cus() {
+int cus_of_current_device() {
     static int cached[64];
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
@@ -356,6 +356,8 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+int num_cus() { return cus_of_current_device(); }
+
 bool attn_shape_supported(int G, int hd) {
     return G >= 1 && G <= kMaxG && (hd == 64 || hd == 128);
 }
@@ -368,7 +370,7 @@ AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req) {
         p.chunk = (chunk_req + kTile - 1) / kTile * kTile;
     } else {
         // about two workgroups per compute unit over all (sequence, KV head) pairs
-        int target = 2 * num_cus() / (m * KV);
+        int target = 2 * cus_of_current_device() / (m * KV);
         if (target < 1) target = 1;
         int c = (max_tokens + target - 1) / target;
         p.chunk = (c + kTile - 1) / kTile * kTile;
@@ -382,7 +384,7 @@ AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req) {
 int attn_max_chunks(int m, int KV, int max_tokens, int chunk_req) {
     // the largest nchunks attn_plan returns for any token count <= max_tokens
     if (chunk_req > 0) return attn_plan(m, KV, max_tokens, chunk_req).nchunks;
-    int target = 2 * num_cus() / (m * KV);
+    int target = 2 * cus_of_current_device() / (m * KV);
     if (target < 1) target = 1;
     int by_tile = (max_tokens + kTile - 1) / kTile;
     return by_tile < target ? by_tile : target;

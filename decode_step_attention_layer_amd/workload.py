@@ -87,6 +87,8 @@ class DeviceStack:
             twin.layers.append(DeviceLayer(t, weights, cache, L.host))
         twin.bufs = [b.clone() for b in self.bufs]
         twin.x0 = self.x0.clone()
+        twin._arrays = None
+        twin.step_out = None
         return twin
 
     def _upload(self, w, c, keep_host):
@@ -125,3 +127,36 @@ class DeviceStack:
                                ws.numel(), stream)
             cur = out
         return cur
+
+    # ----------------------------------------------------- whole-step entry --
+    def step_workspace(self, desc: ck.CkLayerDesc) -> torch.Tensor:
+        n = ck.ck_decode_step_workspace_size(desc, self.nlayers, self.max_ctx)
+        assert n > 0, "step shape rejected by libck"
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def step_arrays(self):
+        """ctypes arrays of the layers' weight and cache structs (built once)."""
+        if getattr(self, "_arrays", None) is None:
+            n = self.nlayers
+            self._arrays = ((ck.CkLayerWeights * n)(*[L.weights for L in self.layers]),
+                            (ck.CkKVCache * n)(*[L.cache for L in self.layers]))
+        return self._arrays
+
+    def decode_step(self, desc: ck.CkLayerDesc, ws: torch.Tensor, out: torch.Tensor | None = None,
+                    stream=None, x=None) -> torch.Tensor:
+        """One decode step through every layer with a single ck_decode_step call."""
+        if out is None:
+            if getattr(self, "step_out", None) is None:
+                self.step_out = torch.empty((self.cfg.m, self.cfg.D), dtype=torch.float32,
+                                            device=self.device)
+            out = self.step_out
+        w, c = self.step_arrays()
+        ck.ck_decode_step(desc, w, c, self.x0 if x is None else x, self.pos, out, ws, ws.numel(),
+                          stream)
+        return out
+
+    def step_status(self, desc: ck.CkLayerDesc, ws: torch.Tensor) -> int:
+        """The persistent step's status word (0: completed)."""
+        off = ck.ck_decode_step_status_offset(desc, self.nlayers)
+        assert off >= 0
+        return int(ws[off:off + 4].view(torch.int32).item())

@@ -71,8 +71,11 @@ typedef struct ck_kv_cache {
     int32_t num_pages;
 } ck_kv_cache;
 
-#define CK_VARIANT_CHAIN 0   /* one kernel per step (the unfused chain) */
-#define CK_VARIANT_FUSED 1   /* steps fused, intermediates kept on chip */
+#define CK_VARIANT_CHAIN 0       /* one kernel per step (the unfused chain) */
+#define CK_VARIANT_FUSED 1       /* steps fused into four kernels per layer */
+#define CK_VARIANT_PERSISTENT 2  /* every layer of a step in one persistent kernel */
+
+#define CK_MAX_STEP_LAYERS 32
 
 typedef struct ck_layer_desc {
     int32_t D;          /* model width (RMSNorm, Q/K/V input, O output) */
@@ -179,16 +182,44 @@ size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx);
  *   out = Wo Q8_0(a) + bo + residual
  * x, residual, out: [m][D]; residual nullable; out may alias residual but not
  * x. pos_host: [m] host positions. ws: at least
- * ck_decode_layer_workspace_size bytes of device memory. */
+ * ck_decode_layer_workspace_size bytes of device memory. With
+ * CK_VARIANT_PERSISTENT the layer runs as a one-layer ck_decode_step, which
+ * requires residual == x (else CK_EINVAL). */
 int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w,
                     const ck_kv_cache *kv, const float *x, const float *residual,
                     const int32_t *pos_host, float *out, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* A whole decode step: `layers` layers of the same shape, layer l reading the
+ * previous layer's output (x for layer 0) with that input as its residual:
+ *   x_{l+1} = ck_decode_layer(layer l, x_l, residual = x_l),  out = x_layers.
+ * w and kv are arrays of `layers` entries (1..CK_MAX_STEP_LAYERS); every
+ * layer's cache has the same geometry and every layer uses the RoPE tables of
+ * w[0]. With desc->variant == CK_VARIANT_PERSISTENT the step runs as one
+ * persistent kernel (plus a counter-clearing kernel) in which HBM streams
+ * continue across layer and phase boundaries; it requires H*head_dim == D <=
+ * 4096, D % 64 == 0, head_dim 64 or 128 and H/KV <= 8 (else CK_EUNSUPPORTED).
+ * The other variants run ck_decode_layer per layer. If a persistent step
+ * cannot complete (its bounded waits time out), the launch still ends, out
+ * is undefined, and the status word (ck_decode_step_status_offset) is set.
+ * ws: at least ck_decode_step_workspace_size bytes, 256-byte aligned; out
+ * must not alias x. Calls that share a workspace must not overlap. */
+size_t ck_decode_step_workspace_size(const ck_layer_desc *desc, int layers, int max_ctx);
+int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                   int layers, const float *x, const int32_t *pos_host, float *out,
+                   void *ws, size_t ws_bytes, void *stream);
+/* Byte offset in the step workspace of the uint32 status word: zero after
+ * a persistent step that completed, non-zero after one whose waits timed out
+ * (read it after synchronizing). -1 for an invalid desc or a variant other
+ * than CK_VARIANT_PERSISTENT. */
+long ck_decode_step_status_offset(const ck_layer_desc *desc, int layers);
+
 /* Workspace layout of ck_decode_layer, so that callers (tests) can read the
  * intermediates after a call: byte offsets into ws, or -1 if the variant does
  * not keep that intermediate in the workspace. Names: "xn", "xq", "q", "k",
- * "v", "attn", "aq". */
+ * "v", "attn", "aq". For CK_VARIANT_PERSISTENT they are the offsets in the
+ * workspace of a step (they do not depend on the number of layers), where
+ * the intermediates of the step's last layer remain. */
 long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const char *name);
 
 #ifdef __cplusplus

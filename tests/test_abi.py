@@ -133,3 +133,54 @@ def test_no_fallback_when_library_missing(tmp_path, monkeypatch):
     monkeypatch.setattr(ckmod, "LIB_PATH", str(tmp_path / "libck.so"))
     with pytest.raises(RuntimeError, match="not built"):
         ckmod.load()
+
+
+def test_step_validation_and_workspace(ck):
+    L = ck.load()
+    for variant in (ck.CK_VARIANT_CHAIN, ck.CK_VARIANT_FUSED, ck.CK_VARIANT_PERSISTENT):
+        d = ck.layer_desc(256, 4, 2, 64, 1, variant=variant)
+        n1 = ck.ck_decode_step_workspace_size(d, 1, 17)
+        n4 = ck.ck_decode_step_workspace_size(d, 4, 17)
+        assert 0 < n1 <= n4
+        assert ck.ck_decode_step_workspace_size(d, 0, 17) == 0
+        assert ck.ck_decode_step_workspace_size(d, ck.CK_MAX_STEP_LAYERS + 1, 17) == 0
+        off = ck.ck_decode_step_status_offset(d, 4)
+        if variant == ck.CK_VARIANT_PERSISTENT:
+            # the status word lies inside the workspace at any context length
+            assert off >= 0 and off % 4 == 0 and off + 4 <= n4
+            assert off + 4 <= ck.ck_decode_step_workspace_size(d, 4, 1)
+            # the one-layer persistent workspace of ck_decode_layer is the step's
+            assert ck.ck_decode_layer_workspace_size(d, 17) == n1
+            offs = [ck.ck_decode_layer_ws_offset(d, 17, k)
+                    for k in ("xn", "xq", "q", "k", "v", "attn", "aq")]
+            assert len(set(offs)) == len(offs) and all(o % 256 == 0 and 0 <= o < n1 for o in offs)
+            # the intermediates precede the counters at any layer count
+            for layers in (1, 4, ck.CK_MAX_STEP_LAYERS):
+                assert max(offs) < ck.ck_decode_step_status_offset(d, layers)
+        else:
+            assert off == -1
+    d = ck.layer_desc(256, 4, 2, 64, 1, variant=ck.CK_VARIANT_PERSISTENT)
+    n = ck.ck_decode_step_workspace_size(d, 2, 17)
+    w = ck.CkLayerWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, 64)
+    c = ck.CkKVCache(FAKE, FAKE, 2, 64, 64, 0, None, 0, 0)
+    ws = (ck.CkLayerWeights * 2)(w, w)
+    pos = (ctypes.c_int32 * 1)(16)
+
+    def call(caches, x=FAKE, out=FAKE + 4096, nbytes=n, layers=2, p=pos):
+        cs = (ck.CkKVCache * len(caches))(*caches)
+        return L.ck_decode_step(ctypes.byref(d), ws, cs, layers, x, p, out, FAKE, nbytes, None)
+
+    assert call([c, c], out=FAKE) == ck.CK_EINVAL                   # out aliases x
+    assert call([c, c], nbytes=256) == ck.CK_ENOSPC
+    assert call([c, c], layers=0) == ck.CK_EINVAL
+    assert call([c, ck.CkKVCache(FAKE, FAKE, 2, 64, 128, 0, None, 0, 0)]) == ck.CK_EINVAL
+    assert call([c, c], p=(ctypes.c_int32 * 1)(64)) == ck.CK_EINVAL  # position past the cache
+    # residual other than x is rejected for a one-layer persistent ck_decode_layer
+    assert L.ck_decode_layer(ctypes.byref(d), ctypes.byref(w), ctypes.byref(c), FAKE, None, pos,
+                             FAKE + 4096, FAKE, n, None) == ck.CK_EINVAL
+    # shapes the persistent kernel is not built for
+    big = ck.layer_desc(8192, 64, 8, 128, 1, variant=ck.CK_VARIANT_PERSISTENT)
+    nb = ck.ck_decode_step_workspace_size(big, 1, 17)
+    cb = ck.CkKVCache(FAKE, FAKE, 8, 128, 64, 0, None, 0, 0)
+    assert L.ck_decode_step(ctypes.byref(big), ws, (ck.CkKVCache * 1)(cb), 1, FAKE, pos,
+                            FAKE + 4096, FAKE, nb, None) == ck.CK_EUNSUPPORTED

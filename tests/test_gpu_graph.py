@@ -33,3 +33,33 @@ def test_graph_replay_equals_eager(name, variant):
         again = stack.step(desc, ws)
         torch.cuda.synchronize()
         assert torch.equal(again, eager)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c5"])
+def test_graph_replay_persistent_step(name):
+    """The whole-step persistent kernel (and its counter-clearing kernel)
+    captured once and replayed: every replay equals the eager step."""
+    import torch
+    from decode_step_attention_layer_amd import ck, synth
+    from decode_step_attention_layer_amd.workload import DeviceStack
+
+    dev = cuda()
+    stack = DeviceStack(synth.CONFIGS[name], dev, layers=4 if name == "c2" else None)
+    desc = stack.desc(ck.CK_VARIANT_PERSISTENT)
+    ws = stack.step_workspace(desc)
+    eager = stack.decode_step(desc, ws).clone()
+    torch.cuda.synchronize()
+    assert stack.step_status(desc, ws) == 0
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stack.decode_step(desc, ws, out=out)
+    for i in range(5):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert stack.step_status(desc, ws) == 0
+        assert torch.equal(out, eager), f"replay {i} differs"
+        again = stack.decode_step(desc, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager)
