@@ -49,7 +49,24 @@ def parse():
                     help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (the known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 256 MiB read and 256 MiB written per
+    dispatch (torch's device-to-device copy kernel)."""
+    import torch
+
+    n = 256 * 2 ** 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}), flush=True)
 
 
 def log(msg):
@@ -58,6 +75,9 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X "
@@ -240,10 +260,42 @@ def roofline(args, stack, desc, ws, nbytes):
     else:
         name, gbs, us, b = "k_gemv", wo_gbs, wo_us, wo_bytes
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / PEAK_GBS, 4), "traffic": None, "kernel": name,
+            "frac": round(gbs / PEAK_GBS, 4),
+            "traffic": recorded_traffic(name, args.config), "traffic_unit": "bytes per launch",
+            "kernel": name,
             "us_per_launch": round(us, 3), "bytes_per_launch": b,
             "other": {"k_attn_us": round(attn_us, 3), "k_attn_GBs": round(att_gbs, 1),
                       "o_gemv_us": round(wo_us, 3), "o_gemv_GBs": round(wo_gbs, 1)}}
+
+
+def recorded_traffic(kernel: str, workload: str, launches_bytes=None):
+    """HBM bytes per dispatch of `kernel` on `workload` from the FETCH_SIZE /
+    WRITE_SIZE counter runs recorded in profiles/hbm_traffic_counters.md
+    (each counter scaled by its reading for a copy of known size), or None if
+    there is no record or the kernel's source changed since it was taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    mt = re.search(r"```json\n(.*?)```", text, re.S)
+    if not mt:
+        return None
+    rec = json.loads(mt.group(1))
+    csrc = os.path.join(ROOT, "decode_step_attention_layer_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (kernel + ".hip", "ck_device.hpp", "ck_internal.hpp", "ck_gemv_common.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    src = h.hexdigest()[:16]
+    for r in rec["records"]:
+        if r["kernel"] == kernel and r["workload"] == workload and r["src"] == src:
+            return round(r["fetch_kib"] * 1024 * rec["fetch_scale"] +
+                         r["write_kib"] * 1024 * rec["write_scale"])
+    return None
 
 
 def cpu_baseline(args, stack, nbytes):

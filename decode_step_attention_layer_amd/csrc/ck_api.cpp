@@ -61,9 +61,20 @@ int read_positions(const int32_t *pos_host, int m, long long limit, Positions *p
     return CK_OK;
 }
 
+}  // namespace
+
+namespace ck {
+long long total_tokens(const Positions &p, int m) {
+    long long t = 0;
+    for (int s = 0; s < m; s++) t += (long long)p.p[s] + 1;
+    return t;
+}
+}  // namespace ck
+
+namespace {
+
 struct WsLayout {
     size_t xn, xq, q, k, v, attn, aq, part, total;
-    AttnPlan plan;
 };
 
 WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
@@ -78,8 +89,7 @@ WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
     w.v = o; o = up256(o + sizeof(float) * m * KD);
     w.attn = o; o = up256(o + sizeof(float) * m * HD);
     w.aq = o; o = up256(o + m * (HD / CK_QK) * CK_Q8_0_BYTES);
-    w.plan = attn_plan(d->m, d->KV, max_ctx, d->attn_chunk);
-    const int maxc = attn_max_chunks(d->m, d->KV, max_ctx, d->attn_chunk);
+    const int maxc = attn_max_chunks(d->KV, max_ctx, d->attn_chunk);
     w.part = o; o = up256(o + attn_partials_bytes(d->m, d->H, d->head_dim, maxc));
     w.total = o;
     return w;
@@ -127,7 +137,6 @@ int gemv_common(const void *W, const void *xq, const float *bias, const float *r
 // persistent kernel's buffers or one ck_decode_layer workspace.
 struct StepWs {
     size_t xbuf, xn, xq, q, k, v, attn, aqx, aq, po, pml, cnt, layer, total;
-    AttnPlan plan;
     int maxc;
 };
 
@@ -138,8 +147,7 @@ StepWs step_layout(const ck_layer_desc *d, int layers, int max_ctx) {
     memset(&w, 0, sizeof(w));
     size_t o = 0;
     w.xbuf = o; o = up256(o + sizeof(float) * 2 * m * D);
-    w.plan = attn_plan(d->m, d->KV, max_ctx, d->attn_chunk);
-    w.maxc = attn_max_chunks(d->m, d->KV, max_ctx, d->attn_chunk);
+    w.maxc = attn_max_chunks(d->KV, max_ctx, d->attn_chunk);
     if (d->variant == CK_VARIANT_PERSISTENT) {
         // intermediates (offsets independent of the layer count and the
         // context), then the counters (the status word's offset does not
@@ -229,7 +237,7 @@ int ck_kv_append(const ck_kv_cache *kv, const float *k, const float *v, const in
 
 size_t ck_attn_workspace_size(int m, int H, int KV, int hd, int max_tokens, int chunk) {
     if (m < 1 || H <= 0 || KV <= 0 || hd <= 0 || max_tokens < 1 || chunk < 0) return 0;
-    return attn_partials_bytes(m, H, hd, attn_max_chunks(m, KV, max_tokens, chunk));
+    return attn_partials_bytes(m, H, hd, attn_max_chunks(KV, max_tokens, chunk));
 }
 
 int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, float *out,
@@ -245,7 +253,7 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(m, c.kv_heads, mx, chunk);
+    AttnPlan pl = attn_plan(c.kv_heads, mx, total_tokens(p, m), chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream));
@@ -263,7 +271,7 @@ int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_ho
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(m, c.kv_heads, mx, chunk);
+    AttnPlan pl = attn_plan(c.kv_heads, mx, total_tokens(p, m), chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attn_partial(q, c, p, m, H, scale, pl, partials, (hipStream_t)stream));
@@ -278,7 +286,7 @@ int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, i
     int mx;
     int rc = read_positions(pos_host, m, 1LL << 30, &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(m, KV, mx, chunk);
+    AttnPlan pl = attn_plan(KV, mx, total_tokens(p, m), chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, hd, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attn_merge(partials, p, m, H, KV, hd, pl, out,
@@ -333,6 +341,7 @@ int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const c
     rc = read_positions(pos_host, d.m, limit, &p, &mx);
     if (rc) return rc;
     StepWs L = step_layout(desc, layers, mx);
+    const AttnPlan plan = attn_plan(d.KV, mx, total_tokens(p, d.m), d.attn_chunk);
     if (ws_bytes < L.total) return CK_ENOSPC;
     hipStream_t st = (hipStream_t)stream;
     uint8_t *base = static_cast<uint8_t *>(ws);
@@ -355,7 +364,7 @@ int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const c
         return CK_OK;
     }
 
-    if (!step_supported(d.D, d.H, d.KV, d.head_dim, d.m, L.plan.nchunks)) return CK_EUNSUPPORTED;
+    if (!step_supported(d.D, d.H, d.KV, d.head_dim, d.m, plan.nchunks)) return CK_EUNSUPPORTED;
     StepLaunch sl;
     memset(&sl, 0, sizeof(sl));
     sl.L = layers;
@@ -373,7 +382,7 @@ int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const c
     sl.page_size = c0.page_size;
     sl.max_pages = c0.max_pages;
     sl.num_pages = c0.num_pages;
-    sl.plan = L.plan;
+    sl.plan = plan;
     sl.x = x;
     sl.out = out;
     sl.xbuf = xbuf;
@@ -466,8 +475,9 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
     rc = read_positions(pos_host, d.m, limit, &p, &mx);
     if (rc) return rc;
     WsLayout L = ws_layout(desc, mx);
-    if (!attn_chunks_supported(L.plan.nchunks)) return CK_EUNSUPPORTED;
-    if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, L.plan.nchunks))
+    const AttnPlan plan = attn_plan(d.KV, mx, total_tokens(p, d.m), d.attn_chunk);
+    if (!attn_chunks_supported(plan.nchunks)) return CK_EUNSUPPORTED;
+    if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, plan.nchunks))
         return CK_ENOSPC;
 
     hipStream_t st = (hipStream_t)stream;
@@ -527,7 +537,7 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
 
     // step 7: attention over pos + 1 tokens (fused: the merge also quantizes)
     const float scale = 1.0f / sqrtf((float)d.head_dim);
-    e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, L.plan, part, st);
+    e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, plan, part, st);
     if (e != hipSuccess) return CK_EHIP;
     if (!fused) {
         e = launch_quantize_q8_0(attn, aq, (long long)d.m * (HD / CK_QK), st);

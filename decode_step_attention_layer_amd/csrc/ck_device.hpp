@@ -177,4 +177,33 @@ __device__ __forceinline__ uint32_t align2(uint32_t hi, uint32_t lo) {
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x3a4 __attribute__((ext_vector_type(3), aligned(4)));
 
+// Device-coherent accesses between workgroups of one launch: relaxed
+// agent-scope atomic loads and stores, which gfx950 issues as ordinary vector
+// loads/stores with device-scope coherence (no L2 write-back or invalidate).
+// A producer completes its stores (s_waitcnt) before it signals; a consumer
+// reads the signal before it issues these loads.
+__device__ __forceinline__ float ld_c(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_cu(const unsigned *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_c(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_cu(unsigned *p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// two floats (8-byte aligned) in one coherent 64-bit load
+__device__ __forceinline__ float2 ld_c2(const float *p) {
+    const unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((unsigned)u), __uint_as_float((unsigned)(u >> 32)));
+}
+// four floats (8-byte aligned) in two coherent 64-bit loads
+__device__ __forceinline__ float4 ld_c4(const float *p) {
+    const float2 a = ld_c2(p), b = ld_c2(p + 2);
+    return make_float4(a.x, a.y, b.x, b.y);
+}
+
 }  // namespace ck

@@ -106,25 +106,40 @@ __device__ __forceinline__ float row_reduce(float v) {
 // block (quantize_q8_0_x4_codes). For each chunk c the sink receives
 // (c, normalized float4, packed codes of the chunk, scale bits, code sum of
 // the chunk's block, valid on the block's first lane). red: 8 floats of LDS.
+// The first KEEP float4 chunks of x and gamma per thread, loaded by
+// norm_load so that a caller can issue them before other loads.
+struct NormIn {
+    static constexpr int KEEP = 4;
+    float4 xv[KEEP], gv[KEEP];
+};
+
+__device__ __forceinline__ void norm_load(const float *x, const float *gamma, int D, NormIn &in) {
+    constexpr int NT = kGemvThreads;
+    const int tid = threadIdx.x, n4 = D / 4;
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
+#pragma unroll
+    for (int i = 0; i < NormIn::KEEP; i++) {
+        const int c = tid + i * NT;
+        in.xv[i] = c < n4 ? x4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        in.gv[i] = c < n4 ? g4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
 template <class Sink>
-__device__ __forceinline__ void norm_quant_row(const float *x, const float *gamma, int D,
-                                               float eps, float *red, Sink sink) {
-    constexpr int NT = kGemvThreads, KEEP = 4;
+__device__ __forceinline__ void norm_quant_finish(const NormIn &in, const float *x,
+                                                  const float *gamma, int D, float eps, float *red,
+                                                  Sink sink) {
+    constexpr int NT = kGemvThreads, KEEP = NormIn::KEEP;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n4 = D / 4;
     const float4 *x4 = reinterpret_cast<const float4 *>(x);
     const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
-    float4 xv[KEEP], gv[KEEP];
-#pragma unroll
-    for (int i = 0; i < KEEP; i++) {
-        const int c = tid + i * NT;
-        xv[i] = c < n4 ? x4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        gv[i] = c < n4 ? g4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < KEEP; i++)
-        ss += (xv[i].x * xv[i].x + xv[i].y * xv[i].y) + (xv[i].z * xv[i].z + xv[i].w * xv[i].w);
+        ss += (in.xv[i].x * in.xv[i].x + in.xv[i].y * in.xv[i].y) +
+              (in.xv[i].z * in.xv[i].z + in.xv[i].w * in.xv[i].w);
     for (int c = tid + KEEP * NT; c < n4; c += NT) {
         const float4 t = x4[c];
         ss += (t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w);
@@ -151,10 +166,18 @@ __device__ __forceinline__ void norm_quant_row(const float *x, const float *gamm
 #pragma unroll
     for (int i = 0; i < KEEP; i++) {
         const int c = tid + i * NT;
-        if (c < n4) emit(c, xv[i], gv[i]);
+        if (c < n4) emit(c, in.xv[i], in.gv[i]);
     }
     for (int c = tid + KEEP * NT; c < n4; c += NT) emit(c, x4[c], g4[c]);
     __syncthreads();   // red is free again
+}
+
+template <class Sink>
+__device__ __forceinline__ void norm_quant_row(const float *x, const float *gamma, int D,
+                                               float eps, float *red, Sink sink) {
+    NormIn in;
+    norm_load(x, gamma, D, in);
+    norm_quant_finish(in, x, gamma, D, eps, red, sink);
 }
 
 }  // namespace ck

@@ -83,8 +83,9 @@ struct AttnPlan {
     int chunk;
     int nchunks;
 };
-AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req);
-int attn_max_chunks(int m, int KV, int max_tokens, int chunk_req);
+AttnPlan attn_plan(int KV, int max_tokens, long long total_tokens, int chunk_req);
+int attn_max_chunks(int KV, int max_tokens, int chunk_req);
+long long total_tokens(const Positions &p, int m);
 bool attn_shape_supported(int G, int hd);
 bool attn_chunks_supported(int nchunks);
 size_t attn_partials_bytes(int m, int H, int hd, int nchunks);

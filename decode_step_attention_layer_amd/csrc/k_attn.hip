@@ -44,7 +44,11 @@ struct AttnArgs {
     int H;
     float *po;            // [m][KV][nchunks][G][HD]  unnormalized outputs
     float *pml;           // [m][KV][nchunks][G][2]   (max in log2 units, sum)
+    int m;
+    int first[kMaxSeqs + 1];  // first work item of each sequence; first[m] = items
 };
+
+constexpr int kPagesLds = 512;   // page ids of a chunk staged in LDS
 
 template <int HD>
 struct Smem {
@@ -53,6 +57,7 @@ struct Smem {
     float q[kMaxG * HD];
     float p[kTile * kMaxG];
     float alpha[kMaxG];
+    int pages[kPagesLds];                   // paged caches: the chunk's page ids
     int bad;
 };
 
@@ -68,10 +73,15 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
     constexpr int S = Smem<HD>::stride;
     __shared__ Smem<HD> sm;
 
-    const int cidx = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+    // grid: (work item, KV head); the items are the chunks of every sequence
+    // back to back, so a batch of unequal lengths launches no idle workgroups
+    const int item = blockIdx.x, g = blockIdx.y;
+    int s = 0;
+    while (s + 1 < a.m && item >= a.first[s + 1]) s++;
+    const int cidx = item - a.first[s];
     const int L = a.pos.p[s] + 1;
     const int t0 = cidx * a.chunk;
-    if (t0 >= L) return;                             // beyond this sequence: no chunk
+    if (t0 >= L) return;                             // (never: items cover [0, L) only)
     const int t1 = min(L, t0 + a.chunk);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -81,11 +91,22 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
 
     float *sk = sm.kv;
     float *sv = sm.kv + kTile * S;
-    // q of the group into LDS, pre-scaled so that scores are in log2 units
-    const float qs = a.scale * kLog2e;
-    for (int i = tid; i < G * HD; i += NT) sm.q[i] = qg[i] * qs;
     if (tid == 0) sm.bad = 0;
-    __syncthreads();
+    // paged: the chunk's page ids in one batch of loads, so that a tile's K/V
+    // addresses do not wait on table reads (chunks with more pages than the
+    // LDS slots read the table per row)
+    int pg0 = 0;
+    bool pages_in_lds = false;
+    if constexpr (PAGED) {
+        const int ps = a.c.page_size;
+        pg0 = t0 / ps;
+        const int npg = (t1 - 1) / ps - pg0 + 1;
+        pages_in_lds = npg <= kPagesLds;
+        if (pages_in_lds)
+            for (int i = tid; i < npg; i += NT)
+                sm.pages[i] = a.c.table[(long long)s * a.c.max_pages + pg0 + i];
+        __syncthreads();
+    }
 
     // loader geometry: this thread loads column ld_col of rows ld_row + i*ROWS_PER_LD
     const int ld_col = tid % C4, ld_row = tid / C4;
@@ -98,7 +119,14 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
             long long off = -1;
             if (t < t1) {
                 if constexpr (PAGED) {
-                    off = cache_row(a.c, s, g, t);
+                    if (pages_in_lds) {
+                        const int ps = a.c.page_size;
+                        const int page = sm.pages[t / ps - pg0];
+                        if (page >= 0 && page < a.c.num_pages)
+                            off = (((long long)page * KV + g) * ps + t % ps) * (long long)HD;
+                    } else {
+                        off = cache_row(a.c, s, g, t);
+                    }
                     if (off < 0) sm.bad = 1;
                 } else {
                     off = (long long)(seq_base + (size_t)t * HD);
@@ -120,7 +148,11 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < G; j++) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
 
+    // the first tile's K/V loads, then q's, in flight together
     fetch(t0);
+    // q of the group into LDS, pre-scaled so that scores are in log2 units
+    const float qs = a.scale * kLog2e;
+    for (int i = tid; i < G * HD; i += NT) sm.q[i] = qg[i] * qs;
     for (int st = t0; st < t1; st += kTile) {
         __syncthreads();                             // previous tile fully consumed
 #pragma unroll
@@ -215,7 +247,6 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
         a.pml[(part * G + wave) * 2 + 0] = m_run;
         a.pml[(part * G + wave) * 2 + 1] = sm.bad ? NAN : lsum;
     }
-
 }
 
 struct MergeArgs {
@@ -240,6 +271,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     constexpr int CG = kMergeThreads / C4;        // chunk groups
     constexpr int NW = kMergeThreads / kWave;
     __shared__ float w_s[kMaxChunks];
+    __shared__ float l_s[kMaxChunks];
     __shared__ float red[NW];
     __shared__ float4 part[NW][C4];
     const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
@@ -249,8 +281,27 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     const int nc = (L + a.chunk - 1) / a.chunk;
     const size_t base = ((size_t)s * a.KV + g) * a.nchunks;
 
+    // Every load that does not depend on another goes out first: the (max,
+    // sum) pairs of this thread's chunks and the outputs of its first kPre
+    // chunk slots, so that the merge costs one memory round trip.
+    constexpr int kPre = 8;
+    const int d4 = tid % C4, cg = tid / C4;
+    auto ld = [&](int c) {
+        return *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
+    };
+    float4 pre[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; i++) {
+        const int c = cg + i * CG;
+        pre[i] = c < nc ? ld(c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float mx = -INFINITY;
-    for (int c = tid; c < nc; c += kMergeThreads) mx = fmaxf(mx, a.pml[((base + c) * G + j) * 2]);
+    for (int c = tid; c < nc; c += kMergeThreads) {
+        const float2 ml = *reinterpret_cast<const float2 *>(&a.pml[((base + c) * G + j) * 2]);
+        w_s[c] = ml.x;
+        l_s[c] = ml.y;
+        mx = fmaxf(mx, ml.x);
+    }
     mx = wave_max(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
@@ -260,10 +311,9 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     __syncthreads();
     float den = 0.0f;
     for (int c = tid; c < nc; c += kMergeThreads) {
-        const size_t pj = (base + c) * G + j;
-        const float w = exp2f(a.pml[pj * 2] - M);
+        const float w = exp2f(w_s[c] - M);
         w_s[c] = w;
-        den = fmaf(w, a.pml[pj * 2 + 1], den);
+        den = fmaf(w, l_s[c], den);
     }
     den = wave_sum(den);
     if (lane == 0) red[wave] = den;
@@ -272,16 +322,20 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < NW; i++) D += red[i];
 
-    const int d4 = tid % C4, cg = tid / C4;
     float4 n0 = make_float4(0.f, 0.f, 0.f, 0.f), n1 = n0;
     auto fma4 = [](float w, float4 v, float4 acc) {
         return make_float4(fmaf(w, v.x, acc.x), fmaf(w, v.y, acc.y), fmaf(w, v.z, acc.z),
                            fmaf(w, v.w, acc.w));
     };
-    auto ld = [&](int c) {
-        return *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
-    };
-    int c = cg;
+#pragma unroll
+    for (int i = 0; i < kPre; i++) {
+        const int c = cg + i * CG;
+        if (c < nc) {
+            if (i & 1) n1 = fma4(w_s[c], pre[i], n1);
+            else n0 = fma4(w_s[c], pre[i], n0);
+        }
+    }
+    int c = cg + kPre * CG;
     for (; c + CG < nc; c += 2 * CG) {
         const float4 v0 = ld(c), v1 = ld(c + CG);
         n0 = fma4(w_s[c], v0, n0);
@@ -316,7 +370,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
 template <int HD, int G>
 hipError_t launch_t(const AttnArgs &a, int m, bool paged, hipStream_t st) {
     constexpr int NT = G > 4 ? 512 : 256;
-    const dim3 grid(a.nchunks, a.c.kv_heads, m);
+    const dim3 grid(a.first[m], a.c.kv_heads);
     if (paged)
         hipLaunchKernelGGL((k_attn<HD, G, true>), grid, dim3(NT), 0, st, a);
     else
@@ -364,16 +418,18 @@ bool attn_shape_supported(int G, int hd) {
 
 bool attn_chunks_supported(int nchunks) { return nchunks >= 1 && nchunks <= kMaxChunks; }
 
-AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req) {
+AttnPlan attn_plan(int KV, int max_tokens, long long total_tokens, int chunk_req) {
     AttnPlan p;
     if (chunk_req > 0) {
         p.chunk = (chunk_req + kTile - 1) / kTile * kTile;
     } else {
-        // about two workgroups per compute unit over all (sequence, KV head) pairs
-        int target = 2 * cus_of_current_device() / (m * KV);
-        if (target < 1) target = 1;
-        int c = (max_tokens + target - 1) / target;
-        p.chunk = (c + kTile - 1) / kTile * kTile;
+        // about two workgroups per compute unit over all (sequence, KV head,
+        // chunk) items: chunks are sized from the tokens of every sequence,
+        // so that a batch of unequal lengths still fills the GPU
+        const long long target = 2LL * cus_of_current_device();
+        if (total_tokens < max_tokens) total_tokens = max_tokens;
+        const long long c = (total_tokens * KV + target - 1) / target;
+        p.chunk = (int)((c + kTile - 1) / kTile * kTile);
     }
     if (p.chunk < kTile) p.chunk = kTile;
     p.nchunks = (max_tokens + p.chunk - 1) / p.chunk;
@@ -381,13 +437,15 @@ AttnPlan attn_plan(int m, int KV, int max_tokens, int chunk_req) {
     return p;
 }
 
-int attn_max_chunks(int m, int KV, int max_tokens, int chunk_req) {
-    // the largest nchunks attn_plan returns for any token count <= max_tokens
-    if (chunk_req > 0) return attn_plan(m, KV, max_tokens, chunk_req).nchunks;
-    int target = 2 * cus_of_current_device() / (m * KV);
-    if (target < 1) target = 1;
-    int by_tile = (max_tokens + kTile - 1) / kTile;
-    return by_tile < target ? by_tile : target;
+int attn_max_chunks(int KV, int max_tokens, int chunk_req) {
+    // the largest nchunks attn_plan returns for any positions with at most
+    // max_tokens tokens per sequence: the chunk is at least
+    // max_tokens * KV / (2 CUs), so nchunks <= ceil(2 CUs / KV)
+    if (chunk_req > 0) return attn_plan(KV, max_tokens, max_tokens, chunk_req).nchunks;
+    const int target = 2 * cus_of_current_device();
+    const int by_items = (target + KV - 1) / KV;
+    const int by_tile = (max_tokens + kTile - 1) / kTile;
+    return by_tile < by_items ? by_tile : by_items;
 }
 
 // Workspace of the attention: unnormalized outputs, then (max, sum) per chunk
@@ -413,6 +471,11 @@ hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positio
     a.po = reinterpret_cast<float *>(base);
     a.pml = reinterpret_cast<float *>(base + up256(sizeof(float) * (size_t)m * H * plan.nchunks *
                                                    c.head_dim));
+    a.m = m;
+    a.first[0] = 0;
+    for (int s = 0; s < m; s++)
+        a.first[s + 1] = a.first[s] + (pos.p[s] + 1 + plan.chunk - 1) / plan.chunk;
+    for (int s = m + 1; s <= kMaxSeqs; s++) a.first[s] = a.first[m];
     const bool paged = c.page_size != 0;
     return c.head_dim == 64 ? launch_g<64>(a, G, m, paged, st) : launch_g<128>(a, G, m, paged, st);
 }

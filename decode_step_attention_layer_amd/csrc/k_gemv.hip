@@ -76,6 +76,17 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int wg_in_seg, XBlo
         }
     }
 
+    // bias and the first token's residual do not depend on anything either:
+    // their loads go out with the weights' (one round trip less at the end)
+    float bias_v[R], res0[R];
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        const int row = row0 + it * RPW + rsel;
+        const bool mine = sub == 0 && row < sg.rows;
+        bias_v[it] = (mine && sg.bias) ? sg.bias[row] : 0.0f;
+        res0[it] = (mine && sg.residual) ? sg.residual[row] : 0.0f;
+    }
+
     // 2. the activations into LDS while the weight loads are in flight
     stage_xq(xq, m * nb, xs);
 
@@ -102,8 +113,8 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int wg_in_seg, XBlo
             acc = row_reduce<LPR>(acc);
             const int row = row0 + it * RPW + rsel;
             if (sub == 0 && row < sg.rows) {
-                float o = acc + (sg.bias ? sg.bias[row] : 0.0f);
-                if (sg.residual) o = o + sg.residual[(size_t)s * sg.rows + row];
+                float o = acc + bias_v[it];
+                if (sg.residual) o = o + (s == 0 ? res0[it] : sg.residual[(size_t)s * sg.rows + row]);
                 sg.y[(size_t)s * sg.rows + row] = o;
             }
         }

@@ -46,11 +46,16 @@ __device__ __forceinline__ int rope_row(int r, int hd) {
 }
 
 // RMSNorm + Q8_0 of the m tokens into LDS (codes, fp16-rounded scale, code
-// sum); workgroup 0 also writes xn and the xq bytes to the workspace.
-__device__ void stage_normalized(const QkvArgs &a, XBlock *xs, float *red, bool write_trace) {
+// sum); workgroup 0 also writes xn and the xq bytes to the workspace. The
+// first token's x and gamma chunks arrive preloaded in `first`.
+__device__ void stage_normalized(const QkvArgs &a, const NormIn &first, XBlock *xs, float *red,
+                                 bool write_trace) {
     const int D = a.D, nb = D / kQK;
     for (int s = 0; s < a.m; s++) {
-        norm_quant_row(a.x + (size_t)s * D, a.gamma, D, a.eps, red,
+        NormIn in;
+        if (s == 0) in = first;
+        else norm_load(a.x + (size_t)s * D, a.gamma, D, in);
+        norm_quant_finish(in, a.x + (size_t)s * D, a.gamma, D, a.eps, red,
                        [&](int c, float4 v, uint32_t packed, uint16_t dbits, int csum) {
                            const int b = c >> 3, sub = c & 7;
                            XBlock &xb = xs[s * nb + b];
@@ -87,7 +92,10 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
     const bool rotate = seg < 2;
     const int row0 = (wg_in_seg * kGemvWaves + wave) * (RPW * R);
 
-    // 1. weights of all R rows in flight before anything else
+    // 1. the first token's x and gamma (the normalization needs them first),
+    // then the weights of all R rows: all in flight before any arithmetic
+    NormIn first;
+    norm_load(a.x, a.gamma, a.D, first);
     uint32_t wr[R][UPL][F::words];
 #pragma unroll
     for (int it = 0; it < R; it++) {
@@ -106,8 +114,21 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
         }
     }
 
+    // bias and the first token's RoPE factors go out with the weight loads
+    const int half = hd >> 1;
+    float bias_v[R], cs0[R], sn0[R];
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        const int lr = row0 + it * RPW + rsel;
+        const int pr = rotate ? rope_row(lr, hd) : lr;
+        bias_v[it] = (bias && lr < rows) ? bias[pr] : 0.0f;
+        const int i = (lr >> 1) % half;
+        cs0[it] = rotate ? a.cos_tab[(size_t)a.pos.p[0] * half + i] : 0.0f;
+        sn0[it] = rotate ? a.sin_tab[(size_t)a.pos.p[0] * half + i] : 0.0f;
+    }
+
     // 2. normalized, quantized activations into LDS (overlaps the loads)
-    stage_normalized(a, xs, red, blockIdx.x == 0);
+    stage_normalized(a, first, xs, red, blockIdx.x == 0);
 
     // 3. dots, bias, RoPE, stores
     for (int s = 0; s < a.m; s++) {
@@ -130,12 +151,9 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
 #pragma unroll
             for (int u = 0; u < UPL; u++) acc = unit_dot<Q5, PAIRED>(wr[it][u], xb[u], acc);
             acc = row_reduce<LPR>(acc);
-            const int lr = row0 + it * RPW + rsel;
-            const int pr = rotate ? rope_row(lr, hd) : lr;
-            val[it] = acc + ((bias && lr < rows) ? bias[pr] : 0.0f);
+            val[it] = acc + bias_v[it];
         }
         const int p = a.pos.p[s];
-        const int half = hd >> 1;
 #pragma unroll
         for (int it = 0; it < R; it++) {
             const int lr = row0 + it * RPW + rsel;
@@ -151,8 +169,8 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
                     other = __shfl_xor(val[it], LPR);
                 }
                 const int i = (lr >> 1) % half;
-                const float cs = a.cos_tab[(size_t)p * half + i];
-                const float sn = a.sin_tab[(size_t)p * half + i];
+                const float cs = s == 0 ? cs0[it] : a.cos_tab[(size_t)p * half + i];
+                const float sn = s == 0 ? sn0[it] : a.sin_tab[(size_t)p * half + i];
                 out = (lr & 1) ? other * sn + val[it] * cs : val[it] * cs - other * sn;
             }
             if (sub == 0 && lr < rows) {
@@ -214,10 +232,15 @@ hipError_t launch_lpr(const QkvArgs &a, int nunits, hipStream_t st) {
 
 }  // namespace
 
+// One token per call only: every workgroup recomputes the normalization of
+// the input, which is one row's latency for one token but serializes m rows
+// for a batch (measured on the 8-token paged workload: the separate
+// normalization kernel, parallel over tokens, then the projections saved
+// about 20 us per layer).
 bool qkv_shape_supported(int D, int m) {
     const int nb = D / kQK;
     const int nunits = (nb % 2 == 0) ? nb / 2 : nb;
-    return nunits <= 64 * 4 && sizeof(XBlock) * (size_t)m * nb <= 64 * 1024;
+    return m == 1 && nunits <= 64 * 4 && sizeof(XBlock) * (size_t)m * nb <= 64 * 1024;
 }
 
 hipError_t launch_qkv(const float *x, const float *gamma, float eps, int D, int H, int KV, int hd,

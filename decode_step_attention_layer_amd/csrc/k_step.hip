@@ -45,23 +45,6 @@ constexpr int kMaxChunksS = 1024;
 constexpr float kLog2eS = 1.4426950408889634f;
 constexpr unsigned kMaxSpins = 1u << 18;
 
-// ---------------------------------------------------------- coherent I/O --
-__device__ __forceinline__ float ld_c(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned ld_cu(const unsigned *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_c(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_cu(unsigned *p, unsigned v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float4 ld_c4(const float *p) {
-    return make_float4(ld_c(p), ld_c(p + 1), ld_c(p + 2), ld_c(p + 3));
-}
-
 // The thread index behind an empty volatile asm: values derived from it are
 // computed inside each item instead of being hoisted out of the persistent
 // loop, where they would stay live (and spill) across every item type.
