@@ -73,6 +73,12 @@ long long total_tokens(const Positions &p, int m) {
 
 namespace {
 
+// Batches of 4 or more tokens use the matrix-core GEMV where it applies; the
+// vector GEMV serves everything else.
+hipError_t gemv_any(const GemvArgs &g, hipStream_t st) {
+    return gemv_mfma_supported(g.K, g.m) ? launch_gemv_mfma(g, st) : launch_gemv(g, st);
+}
+
 struct WsLayout {
     size_t xn, xq, q, k, v, attn, aq, part, total;
 };
@@ -130,7 +136,7 @@ int gemv_common(const void *W, const void *xq, const float *bias, const float *r
     a.xq = static_cast<const uint8_t *>(xq);
     a.K = K;
     a.m = m;
-    return hip_rc(launch_gemv(a, (hipStream_t)stream));
+    return hip_rc(gemv_any(a, (hipStream_t)stream));
 }
 
 // Workspace of a whole step: the ping-pong layer outputs, then either the
@@ -523,7 +529,7 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
         g.xq = xq;
         g.K = d.D;
         g.m = d.m;
-        if ((e = launch_gemv(g, st)) != hipSuccess) return CK_EHIP;
+        if ((e = gemv_any(g, st)) != hipSuccess) return CK_EHIP;
 
         // steps 5-6: RoPE on q and k, then the append of (k, v) at pos
         if (fused) {
@@ -552,7 +558,7 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
     o.xq = aq;
     o.K = HD;
     o.m = d.m;
-    return hip_rc(launch_gemv(o, st));
+    return hip_rc(gemv_any(o, st));
 }
 
 }  // extern "C"

@@ -70,6 +70,10 @@ hipError_t launch_qkv(const float *x, const float *gamma, float eps, int D, int 
                       const float *sin_tab, const Positions &pos, const CacheView &c, float *q,
                       float *k, float *v, float *xn, uint8_t *xq, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
+// Small-M GEMV on the int8 matrix cores (k_gemv_mfma.hip): batches of 4..16
+// tokens; same arguments and results as launch_gemv.
+bool gemv_mfma_supported(int K, int m);
+hipError_t launch_gemv_mfma(GemvArgs a, hipStream_t st);
 hipError_t launch_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
                        const Positions &pos, int m, int H, int KV, int hd, hipStream_t st);
 hipError_t launch_kv_append(const CacheView &c, const float *k, const float *v,

@@ -1,0 +1,299 @@
+// k_gemv_mfma.hip — small-M block GEMV on the int8 matrix cores (gfx950).
+//
+// For a batch of m tokens sharing the weights (the batched decode layer, all
+// of its projections), y[s][r] = sum_b d_w(r,b) d_x(s,b) S(r,s,b) + bias[r]
+// (+ residual[s][r]) with S the exact integer dot of block b. The per-block
+// scales forbid accumulating across blocks in int32, so every
+// v_mfma_i32_16x16x32_i8 covers exactly one 32-element block: A = the
+// activation codes of 16 token slots (m used), B = the weight codes of 16
+// rows, D[token][row] = S. Lane l supplies token slot l%16 and row l%16 for
+// the k-slice 8*(l/16)..+7 and receives D[4*(l/16)+t][l%16], t < 4, so every
+// output a lane scales belongs to the weight row whose block scale it loaded.
+// Q5_0 codes enter unsigned (0..31) and the 16 * sum(x) offset is removed
+// after the integer dot, as in the vector path.
+//
+// Workgroup: 8 waves on one tile of 16 rows; wave w takes an eighth of the
+// rows' block pairs, loads them with coalesced dword loads (all before any
+// arithmetic) and redistributes them to the MFMA lane layout through its own
+// LDS region, in phases of 4 Q5_0 (2 Q8_0) block pairs; the activations are
+// staged in LDS once per workgroup (codes, scale, code sum), and the 8 partial
+// sums of each (token, row) are added through LDS in wave order
+// (deterministic).
+#include "ck_device.hpp"
+#include "ck_gemv_common.hpp"
+#include "ck_internal.hpp"
+
+namespace ck {
+
+namespace {
+
+constexpr int kMT = 512;             // threads
+constexpr int kMW = kMT / kWave;     // waves
+constexpr int kTileRows = 16;
+constexpr int kMaxUnitsPerWave = 8;  // block pairs per wave: K <= 8 * 8 * 64 = 4096
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// The dwords of one block pair a lane needs for its k-slice ks (Q5_0: 9,
+// Q8_0: 7), read from the wave's LDS copy of the pair.
+template <bool Q5>
+struct SliceWords {
+    static constexpr int n = Q5 ? 9 : 7;
+};
+
+template <bool Q5>
+__device__ __forceinline__ void load_slice(const uint32_t *u, int ks, uint32_t *w) {
+    if constexpr (Q5) {
+        const int k2 = 2 * (ks & 1);
+        w[0] = u[0];            // d0 | qh0 bytes 0-1
+        w[1] = u[1];            // qh0 bytes 2-3 | qs0 bytes 0-1
+        w[2] = u[1 + k2];       // qs0 slice, shifted by 2 bytes
+        w[3] = u[2 + k2];
+        w[4] = u[3 + k2];
+        w[5] = u[5];            // ... | d1
+        w[6] = u[6];            // qh1
+        w[7] = u[7 + k2];       // qs1 slice
+        w[8] = u[8 + k2];
+    } else {
+        const int k2 = 2 * ks;
+        w[0] = u[0];            // d0 | codes 0-1
+        w[1] = u[k2];           // block-0 codes of the slice, shifted by 2 bytes
+        w[2] = u[k2 + 1];
+        w[3] = u[k2 + 2];
+        w[4] = u[8];            // ... | d1
+        w[5] = u[9 + k2];       // block-1 codes of the slice
+        w[6] = u[10 + k2];
+    }
+}
+
+// The 8 codes of block bb (0, 1) in the lane's k-slice as a 64-bit operand,
+// and the block's weight scale.
+template <bool Q5>
+__device__ __forceinline__ long slice_codes(const uint32_t *w, int bb, int ks, float &dw) {
+    uint32_t c0, c1;
+    if constexpr (Q5) {
+        uint32_t qh, q0, q1;
+        if (bb == 0) {
+            dw = half_bits_to_float(w[0]);
+            qh = align2(w[1], w[0]);
+            q0 = align2(w[3], w[2]);
+            q1 = align2(w[4], w[3]);
+        } else {
+            dw = half_bits_to_float(w[5] >> 16);
+            qh = w[6];
+            q0 = w[7];
+            q1 = w[8];
+        }
+        const int sh = ks < 2 ? 0 : 4;
+        c0 = (q0 >> sh) & 0x0F0F0F0Fu;
+        c1 = (q1 >> sh) & 0x0F0F0F0Fu;
+        c0 |= spread4(__builtin_amdgcn_ubfe(qh, 8 * ks, 4)) << 4;
+        c1 |= spread4(__builtin_amdgcn_ubfe(qh, 8 * ks + 4, 4)) << 4;
+    } else {
+        if (bb == 0) {
+            dw = half_bits_to_float(w[0]);
+            c0 = align2(w[2], w[1]);
+            c1 = align2(w[3], w[2]);
+        } else {
+            dw = half_bits_to_float(w[4] >> 16);
+            c0 = w[5];
+            c1 = w[6];
+        }
+    }
+    return (long)((unsigned long)c0 | ((unsigned long)c1 << 32));
+}
+
+// Weight staging: a wave loads its 16 rows' block pairs with coalesced dword
+// loads (consecutive lanes, consecutive dwords of a row segment), all phases
+// before any arithmetic, then per phase writes them to its own LDS region
+// and every lane reads back the dwords of its (row, k-slice).
+template <bool Q5>
+struct Stage {
+    static constexpr int words = Q5 ? 11 : 17;        // dwords per block pair
+    static constexpr int pu = Q5 ? 4 : 2;             // block pairs per phase
+    static constexpr int nph = kMaxUnitsPerWave / pu; // phases (at most)
+    static constexpr int stride = pu * words + 1;     // LDS row stride (dwords)
+    static constexpr int per_lane = (kTileRows * pu * words + kWave - 1) / kWave;
+    static constexpr int region = kTileRows * stride; // dwords per wave
+};
+
+constexpr int kStageRegion = Stage<true>::region > Stage<false>::region ? Stage<true>::region
+                                                                        : Stage<false>::region;
+
+template <bool Q5>
+__device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb, int m,
+                          XBlock *xs, uint32_t *wst, float *red) {
+    using St = Stage<Q5>;
+    constexpr int NSW = SliceWords<Q5>::n;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, ks = lane >> 4;
+    const int nunits = nb / 2;
+    const int upw = (nunits + kMW - 1) / kMW;
+    const int u0 = wave * upw;
+    const int uend = min(u0 + upw, nunits);                // this wave's block pairs [u0, uend)
+    const size_t row_bytes = (size_t)nb * (Q5 ? kQ5Bytes : kQ8Bytes);
+    const int row0 = tile * kTileRows;
+
+    // 1. every phase's weight dwords, coalesced: flat index f over
+    // [16 rows][n_p block pairs][words] of the phase
+    uint32_t raw[St::nph][St::per_lane];
+#pragma unroll
+    for (int p = 0; p < St::nph; p++) {
+        const int pb = u0 + p * St::pu;
+        const int np = max(0, min(St::pu, uend - pb));
+        const int ndw = np * St::words;
+#pragma unroll
+        for (int i = 0; i < St::per_lane; i++) {
+            const int f = lane + kWave * i;
+            raw[p][i] = 0;
+            if (ndw > 0 && f < kTileRows * ndw) {
+                const int r = f / ndw, d = f - r * ndw;
+                if (row0 + r < sg.rows)
+                    raw[p][i] = *reinterpret_cast<const uint32_t *>(
+                        sg.W + (size_t)(row0 + r) * row_bytes + (size_t)pb * (2 * (Q5 ? kQ5Bytes : kQ8Bytes)) +
+                        4 * (size_t)d);
+            }
+        }
+    }
+    // the output thread's bias and residual go out with the weights
+    const int otok = tid / kTileRows, orow = row0 + tid % kTileRows;
+    const bool writer = tid < m * kTileRows && orow < sg.rows;
+    const float bias_o = (writer && sg.bias) ? sg.bias[orow] : 0.0f;
+    const float res_o = (writer && sg.residual) ? sg.residual[(size_t)otok * sg.rows + orow] : 0.0f;
+
+    // 2. the activations of all m tokens into LDS (codes, scale, code sum)
+    for (int b = tid; b < m * nb; b += kMT) {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)b * kQ8Bytes);
+        XBlock xb;
+        xb.d = half_bits_to_float(src[0]);
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t c = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+            xb.c[i] = (int)c;
+            sum = __builtin_amdgcn_sdot4((int)c, 0x01010101, sum, false);
+        }
+        xb.sum = sum;
+        xb.pad[0] = xb.pad[1] = 0;
+        xs[b] = xb;
+    }
+    __syncthreads();
+
+    // 3. per phase: weights into this wave's LDS region, then one MFMA per
+    // block: A = token slot j's codes, B = row j's codes
+    uint32_t *reg = wst + wave * kStageRegion;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bool a_valid = j < m;
+#pragma unroll
+    for (int p = 0; p < St::nph; p++) {
+        const int pb = u0 + p * St::pu;
+        const int np = max(0, min(St::pu, uend - pb));
+        if (np == 0) break;
+        const int ndw = np * St::words;
+#pragma unroll
+        for (int i = 0; i < St::per_lane; i++) {
+            const int f = lane + kWave * i;
+            if (f < kTileRows * ndw) {
+                const int r = f / ndw, d = f - r * ndw;
+                reg[r * St::stride + d] = raw[p][i];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int k = 0; k < St::pu; k++) {
+            if (k < np) {
+                uint32_t w[NSW];
+                load_slice<Q5>(reg + j * St::stride + k * St::words, ks, w);
+#pragma unroll
+                for (int bb = 0; bb < 2; bb++) {
+                    const int b = 2 * (pb + k) + bb;
+                    float dw;
+                    const long bop = slice_codes<Q5>(w, bb, ks, dw);
+                    long aop = 0;
+                    if (a_valid) {
+                        const int2 c = *reinterpret_cast<const int2 *>(&xs[j * nb + b].c[2 * ks]);
+                        aop = (long)((unsigned long)(uint32_t)c.x |
+                                     ((unsigned long)(uint32_t)c.y << 32));
+                    }
+                    v4i dd = {0, 0, 0, 0};
+                    dd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, dd, 0, 0, 0);
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        const int tok = 4 * ks + t;
+                        if (tok < m) {
+                            const XBlock &xb = xs[tok * nb + b];
+                            const int sdot = Q5 ? dd[t] - 16 * xb.sum : dd[t];
+                            acc[t] = fmaf((float)sdot, dw * xb.d, acc[t]);
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();   // the region is rewritten by the next phase
+    }
+
+    // 4. the waves' partial sums, added in wave order; thread (token, row)
+    // writes the output
+    __syncthreads();   // the staged activations are no longer read; red aliases them
+#pragma unroll
+    for (int t = 0; t < 4; t++) red[(wave * kWave + lane) * 4 + t] = acc[t];
+    __syncthreads();
+    if (writer) {
+        const int src_lane = tid % kTileRows + 16 * (otok / 4), t = otok % 4;
+        float v = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < kMW; wv++) v += red[(wv * kWave + src_lane) * 4 + t];
+        float o = v + bias_o;
+        if (sg.residual) o = o + res_o;
+        sg.y[(size_t)otok * sg.rows + orow] = o;
+    }
+}
+
+__global__ __launch_bounds__(kMT) void k_gemv_mfma(GemvArgs a) {
+    extern __shared__ __align__(16) uint32_t lds[];   // staged weights, then activations
+    const int wg = blockIdx.x;
+    const int si = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2
+                   : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
+    const GemvSeg sg = si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]);
+    const int nb = a.K / kQK;
+    // LDS: the staged weights of the 8 waves, then the activations (the final
+    // reduction reuses the activations' space)
+    uint32_t *wst = lds;
+    XBlock *xa = reinterpret_cast<XBlock *>(wst + kMW * kStageRegion);
+    float *red = reinterpret_cast<float *>(xa);
+    if (sg.is_q5)
+        mfma_body<true>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xa, wst, red);
+    else
+        mfma_body<false>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xa, wst, red);
+}
+
+size_t mfma_lds(int m, int nb) {
+    const size_t xs = sizeof(XBlock) * (size_t)m * nb;
+    const size_t red = sizeof(float) * kMT * 4;
+    return sizeof(uint32_t) * kMW * kStageRegion + (xs > red ? xs : red);
+}
+
+}  // namespace
+
+// Batches of 4..16 tokens, K a multiple of 64 up to 4096, the workgroup's LDS
+// (staged weights, activation bytes and scales) within 80 KB, two workgroups
+// per compute unit.
+bool gemv_mfma_supported(int K, int m) {
+    const int nb = K / kQK;
+    return m >= 4 && m <= 16 && K % 64 == 0 && nb / 2 <= kMW * kMaxUnitsPerWave &&
+           mfma_lds(m, nb) <= 80 * 1024;
+}
+
+hipError_t launch_gemv_mfma(GemvArgs a, hipStream_t st) {
+    int total = 0;
+    for (int i = 0; i < a.nseg; i++) {
+        a.seg[i].wg_begin = total;
+        total += (a.seg[i].rows + kTileRows - 1) / kTileRows;
+    }
+    for (int i = a.nseg; i < 3; i++) a.seg[i] = a.seg[0], a.seg[i].wg_begin = 1 << 30;
+    hipLaunchKernelGGL(k_gemv_mfma, dim3(total), dim3(kMT), mfma_lds(a.m, a.K / kQK), st, a);
+    return hipGetLastError();
+}
+
+}  // namespace ck

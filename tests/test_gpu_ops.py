@@ -132,6 +132,9 @@ GEMV_SHAPES = [
     # rows, K, m
     (1, 32, 1), (7, 96, 1), (129, 256, 1), (1152, 896, 1), (513, 3584, 1),
     (4096, 4096, 1), (200, 4096, 3), (300, 4096, 8), (64, 14336, 1), (33, 160, 2),
+    # batches of 4..16 tokens with K % 64 == 0 take the matrix-core kernel:
+    # ragged row tiles, block pairs spread unevenly over the 8 waves
+    (100, 3584, 4), (77, 896, 5), (16, 64, 16), (48, 256, 6), (1024, 4096, 8), (40, 640, 12),
 ]
 
 
