@@ -32,7 +32,7 @@ EXPORTS = (
     "ck_attn_decode_gqa", "ck_attn_partial", "ck_attn_merge", "ck_decode_layer_workspace_size",
     "ck_decode_layer",
     "ck_decode_layer_ws_offset", "ck_decode_step_workspace_size", "ck_decode_step",
-    "ck_decode_step_status_offset",
+    "ck_decode_step_status_offset", "ck_decode_layer_devpos", "ck_decode_step_devpos",
 )
 
 
@@ -105,6 +105,10 @@ def load():
         "ck_decode_step": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                             ctypes.POINTER(CkKVCache), I, P, IP, P, P, S, P], I),
         "ck_decode_step_status_offset": ([ctypes.POINTER(CkLayerDesc), I], ctypes.c_long),
+        "ck_decode_layer_devpos": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
+                                    ctypes.POINTER(CkKVCache), P, P, P, I, P, P, S, P], I),
+        "ck_decode_step_devpos": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
+                                   ctypes.POINTER(CkKVCache), I, P, P, I, P, P, S, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -253,3 +257,24 @@ def ck_decode_step(desc: CkLayerDesc, weights, caches, x, pos, out, ws, ws_bytes
     ca = caches if isinstance(caches, ctypes.Array) else (CkKVCache * n)(*caches)
     _check(load().ck_decode_step(ctypes.byref(desc), wa, ca, n, _ptr(x), _pos(pos), _ptr(out),
                                  _ptr(ws), ws_bytes, _stream(stream)), "ck_decode_step")
+
+
+def ck_decode_layer_devpos(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache, x,
+                           residual, pos_dev, max_ctx, out, ws, ws_bytes, stream=None):
+    """pos_dev: a device int32 tensor of m positions, read when the kernels run."""
+    _check(load().ck_decode_layer_devpos(ctypes.byref(desc), ctypes.byref(weights),
+                                         ctypes.byref(cache), _ptr(x), _ptr(residual),
+                                         _ptr(pos_dev), max_ctx, _ptr(out), _ptr(ws), ws_bytes,
+                                         _stream(stream)), "ck_decode_layer_devpos")
+
+
+def ck_decode_step_devpos(desc: CkLayerDesc, weights, caches, x, pos_dev, max_ctx, out, ws,
+                          ws_bytes, stream=None):
+    n = len(weights)
+    if len(caches) != n:
+        raise ValueError("one cache per layer")
+    wa = weights if isinstance(weights, ctypes.Array) else (CkLayerWeights * n)(*weights)
+    ca = caches if isinstance(caches, ctypes.Array) else (CkKVCache * n)(*caches)
+    _check(load().ck_decode_step_devpos(ctypes.byref(desc), wa, ca, n, _ptr(x), _ptr(pos_dev),
+                                        max_ctx, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
+           "ck_decode_step_devpos")

@@ -52,6 +52,8 @@ int read_positions(const int32_t *pos_host, int m, long long limit, Positions *p
     if (!pos_host || m < 1 || m > CK_MAX_SEQS) return CK_EINVAL;
     int mx = 0;
     memset(p, 0, sizeof(*p));
+    p->dev = nullptr;
+    p->limit = (int)(limit < (1LL << 30) ? limit : (1LL << 30));
     for (int s = 0; s < m; s++) {
         if (pos_host[s] < 0 || pos_host[s] >= limit) return CK_EINVAL;
         p->p[s] = pos_host[s];
@@ -72,6 +74,32 @@ long long total_tokens(const Positions &p, int m) {
 }  // namespace ck
 
 namespace {
+
+// Where a layer or step takes its positions from: a host array (validated
+// here) or a device array read by the kernels (bounded by max_ctx).
+struct PosIn {
+    const int32_t *host;
+    const int32_t *dev;
+    int max_ctx;
+};
+
+int resolve_positions(const PosIn &in, int m, long long limit, Positions *p, int *mx,
+                      long long *total) {
+    if (in.host) {
+        const int rc = read_positions(in.host, m, limit, p, mx);
+        if (rc) return rc;
+        *total = total_tokens(*p, m);
+        return CK_OK;
+    }
+    if (!in.dev || in.max_ctx < 1 || m < 1 || m > CK_MAX_SEQS || !al(in.dev, 4)) return CK_EINVAL;
+    memset(p, 0, sizeof(*p));
+    const long long lim = in.max_ctx < limit ? in.max_ctx : limit;
+    p->dev = in.dev;
+    p->limit = (int)lim;
+    *mx = (int)lim;
+    *total = (long long)m * lim;
+    return CK_OK;
+}
 
 // Batches of 4 or more tokens use the matrix-core GEMV where it applies; the
 // vector GEMV serves everything else.
@@ -313,9 +341,17 @@ long ck_decode_step_status_offset(const ck_layer_desc *desc, int layers) {
     return (long)(w.cnt + sizeof(unsigned) * (step_counter_words(layers, desc->m, desc->KV) - 1));
 }
 
-int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
-                   int layers, const float *x, const int32_t *pos_host, float *out, void *ws,
-                   size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                      const float *x, const float *residual, const PosIn &pin, float *out,
+                      void *ws, size_t ws_bytes, void *stream);
+
+int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                     int layers, const float *x, const PosIn &pin, float *out, void *ws,
+                     size_t ws_bytes, void *stream) {
     int rc = check_desc(desc);
     if (rc) return rc;
     const ck_layer_desc &d = *desc;
@@ -342,12 +378,13 @@ int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const c
     if (!w[0].rope_cos || !w[0].rope_sin) return CK_EINVAL;
     Positions p;
     int mx;
+    long long total;
     long long limit = cache_tokens(&kv[0]);
     if (w[0].rope_rows < limit) limit = w[0].rope_rows;
-    rc = read_positions(pos_host, d.m, limit, &p, &mx);
+    rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     StepWs L = step_layout(desc, layers, mx);
-    const AttnPlan plan = attn_plan(d.KV, mx, total_tokens(p, d.m), d.attn_chunk);
+    const AttnPlan plan = attn_plan(d.KV, mx, total, d.attn_chunk);
     if (ws_bytes < L.total) return CK_ENOSPC;
     hipStream_t st = (hipStream_t)stream;
     uint8_t *base = static_cast<uint8_t *>(ws);
@@ -362,8 +399,8 @@ int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const c
             wl.rope_cos = w[0].rope_cos;
             wl.rope_sin = w[0].rope_sin;
             wl.rope_rows = w[0].rope_rows;
-            rc = ck_decode_layer(desc, &wl, &kv[l], cur, cur, pos_host, dst, base + L.layer,
-                                 ws_bytes - L.layer, stream);
+            rc = decode_layer_impl(desc, &wl, &kv[l], cur, cur, pin, dst, base + L.layer,
+                                   ws_bytes - L.layer, stream);
             if (rc) return rc;
             cur = dst;
         }
@@ -422,6 +459,27 @@ int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const c
     return hip_rc(launch_step(sl, st));
 }
 
+}  // namespace
+
+extern "C" {
+
+int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                   int layers, const float *x, const int32_t *pos_host, float *out, void *ws,
+                   size_t ws_bytes, void *stream) {
+    if (!pos_host) return CK_EINVAL;
+    return decode_step_impl(desc, w, kv, layers, x, PosIn{pos_host, nullptr, 0}, out, ws,
+                            ws_bytes, stream);
+}
+
+int ck_decode_step_devpos(const ck_layer_desc *desc, const ck_layer_weights *w,
+                          const ck_kv_cache *kv, int layers, const float *x,
+                          const int32_t *pos_dev, int max_ctx, float *out, void *ws,
+                          size_t ws_bytes, void *stream) {
+    if (!pos_dev) return CK_EINVAL;
+    return decode_step_impl(desc, w, kv, layers, x, PosIn{nullptr, pos_dev, max_ctx}, out, ws,
+                            ws_bytes, stream);
+}
+
 size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx) {
     if (check_desc(desc) != CK_OK || max_ctx < 1) return 0;
     if (desc->variant == CK_VARIANT_PERSISTENT) return step_layout(desc, 1, max_ctx).total;
@@ -453,15 +511,19 @@ long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const cha
     return -1;
 }
 
-int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
-                    const float *x, const float *residual, const int32_t *pos_host, float *out,
-                    void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                      const float *x, const float *residual, const PosIn &pin, float *out,
+                      void *ws, size_t ws_bytes, void *stream) {
     int rc = check_desc(desc);
     if (rc) return rc;
     if (desc->variant == CK_VARIANT_PERSISTENT) {
         // a one-layer persistent step; its residual is its input
         if (residual != x) return CK_EINVAL;
-        return ck_decode_step(desc, w, kv, 1, x, pos_host, out, ws, ws_bytes, stream);
+        return decode_step_impl(desc, w, kv, 1, x, pin, out, ws, ws_bytes, stream);
     }
     const ck_layer_desc &d = *desc;
     if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->gamma || !w->rope_cos || !w->rope_sin)
@@ -476,12 +538,13 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
     if (c.kv_heads != d.KV || c.head_dim != d.head_dim) return CK_EINVAL;
     Positions p;
     int mx;
+    long long total;
     long long limit = cache_tokens(kv);
     if (w->rope_rows < limit) limit = w->rope_rows;
-    rc = read_positions(pos_host, d.m, limit, &p, &mx);
+    rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     WsLayout L = ws_layout(desc, mx);
-    const AttnPlan plan = attn_plan(d.KV, mx, total_tokens(p, d.m), d.attn_chunk);
+    const AttnPlan plan = attn_plan(d.KV, mx, total, d.attn_chunk);
     if (!attn_chunks_supported(plan.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, plan.nchunks))
         return CK_ENOSPC;
@@ -559,6 +622,27 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
     o.K = HD;
     o.m = d.m;
     return hip_rc(gemv_any(o, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
+                    const float *x, const float *residual, const int32_t *pos_host, float *out,
+                    void *ws, size_t ws_bytes, void *stream) {
+    if (!pos_host) return CK_EINVAL;
+    return decode_layer_impl(desc, w, kv, x, residual, PosIn{pos_host, nullptr, 0}, out, ws,
+                             ws_bytes, stream);
+}
+
+int ck_decode_layer_devpos(const ck_layer_desc *desc, const ck_layer_weights *w,
+                           const ck_kv_cache *kv, const float *x, const float *residual,
+                           const int32_t *pos_dev, int max_ctx, float *out, void *ws,
+                           size_t ws_bytes, void *stream) {
+    if (!pos_dev) return CK_EINVAL;
+    return decode_layer_impl(desc, w, kv, x, residual, PosIn{nullptr, pos_dev, max_ctx}, out,
+                             ws, ws_bytes, stream);
 }
 
 }  // extern "C"

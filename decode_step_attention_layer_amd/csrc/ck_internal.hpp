@@ -13,8 +13,20 @@ namespace ck {
 
 constexpr int kMaxSeqs = CK_MAX_SEQS;
 
+// Token positions: host values copied into the kernel arguments, or (dev not
+// null) a device array read by the kernels, so that a captured launch can be
+// replayed for the next token. A device position outside [0, limit) reads as
+// -1: that sequence then writes nothing to the cache and attends no token
+// (its outputs are undefined), and nothing is accessed out of bounds.
 struct Positions {
     int32_t p[kMaxSeqs];
+    const int32_t *dev;
+    int limit;
+    __device__ __forceinline__ int get(int s) const {
+        if (!dev) return p[s];
+        const int v = dev[s];
+        return (v >= 0 && v < limit) ? v : -1;
+    }
 };
 
 // Cache view passed by value to kernels (mirrors ck_kv_cache).

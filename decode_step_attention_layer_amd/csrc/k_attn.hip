@@ -79,7 +79,7 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
     int s = 0;
     while (s + 1 < a.m && item >= a.first[s + 1]) s++;
     const int cidx = item - a.first[s];
-    const int L = a.pos.p[s] + 1;
+    const int L = a.pos.get(s) + 1;
     const int t0 = cidx * a.chunk;
     if (t0 >= L) return;                             // (never: items cover [0, L) only)
     const int t1 = min(L, t0 + a.chunk);
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int G = a.H / a.KV, g = h / G, j = h % G;
-    const int L = a.pos.p[s] + 1;
+    const int L = a.pos.get(s) + 1;
     const int nc = (L + a.chunk - 1) / a.chunk;
     const size_t base = ((size_t)s * a.KV + g) * a.nchunks;
 
@@ -472,9 +472,13 @@ hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positio
     a.pml = reinterpret_cast<float *>(base + up256(sizeof(float) * (size_t)m * H * plan.nchunks *
                                                    c.head_dim));
     a.m = m;
+    // work items: host positions give each sequence exactly its chunks; with
+    // device positions every sequence gets plan.nchunks items and the ones
+    // past its length return at once
     a.first[0] = 0;
     for (int s = 0; s < m; s++)
-        a.first[s + 1] = a.first[s] + (pos.p[s] + 1 + plan.chunk - 1) / plan.chunk;
+        a.first[s + 1] = a.first[s] + (pos.dev ? plan.nchunks
+                                                : (pos.p[s] + 1 + plan.chunk - 1) / plan.chunk);
     for (int s = m + 1; s <= kMaxSeqs; s++) a.first[s] = a.first[m];
     const bool paged = c.page_size != 0;
     return c.head_dim == 64 ? launch_g<64>(a, G, m, paged, st) : launch_g<128>(a, G, m, paged, st);

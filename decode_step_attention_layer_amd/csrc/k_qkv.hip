@@ -115,7 +115,9 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
     }
 
     // bias and the first token's RoPE factors go out with the weight loads
+    // (an invalid position reads table row 0 and appends nothing)
     const int half = hd >> 1;
+    const int p0 = max(a.pos.get(0), 0);
     float bias_v[R], cs0[R], sn0[R];
 #pragma unroll
     for (int it = 0; it < R; it++) {
@@ -123,8 +125,8 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
         const int pr = rotate ? rope_row(lr, hd) : lr;
         bias_v[it] = (bias && lr < rows) ? bias[pr] : 0.0f;
         const int i = (lr >> 1) % half;
-        cs0[it] = rotate ? a.cos_tab[(size_t)a.pos.p[0] * half + i] : 0.0f;
-        sn0[it] = rotate ? a.sin_tab[(size_t)a.pos.p[0] * half + i] : 0.0f;
+        cs0[it] = rotate ? a.cos_tab[(size_t)p0 * half + i] : 0.0f;
+        sn0[it] = rotate ? a.sin_tab[(size_t)p0 * half + i] : 0.0f;
     }
 
     // 2. normalized, quantized activations into LDS (overlaps the loads)
@@ -153,7 +155,8 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
             acc = row_reduce<LPR>(acc);
             val[it] = acc + bias_v[it];
         }
-        const int p = a.pos.p[s];
+        const int pv = a.pos.get(s);
+        const int p = max(pv, 0);
 #pragma unroll
         for (int it = 0; it < R; it++) {
             const int lr = row0 + it * RPW + rsel;
@@ -179,7 +182,7 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
                     a.q[(size_t)s * rows + pr] = out;
                 } else {
                     (seg == 1 ? a.k : a.v)[(size_t)s * rows + pr] = out;
-                    const long long off = cache_row(a.c, s, g, p);
+                    const long long off = pv >= 0 ? cache_row(a.c, s, g, p) : -1;
                     if (off >= 0) (seg == 1 ? a.c.k : a.c.v)[off + d] = out;
                 }
             }

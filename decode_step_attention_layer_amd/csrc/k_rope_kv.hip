@@ -33,8 +33,10 @@ __global__ __launch_bounds__(256) void k_rope(float *__restrict__ q, float *__re
     }
     const int head = pair / half, d = pair % half;
     float *x = base + (size_t)head * hd;
-    const float c = cos_tab[(size_t)pos.p[s] * half + d];
-    const float sn = sin_tab[(size_t)pos.p[s] * half + d];
+    const int p = pos.get(s);
+    if (p < 0) return;
+    const float c = cos_tab[(size_t)p * half + d];
+    const float sn = sin_tab[(size_t)p * half + d];
     const float a = x[d], b = x[d + half];
     x[d] = a * c - b * sn;
     x[d + half] = a * sn + b * c;
@@ -47,7 +49,9 @@ __global__ __launch_bounds__(256) void k_kv_append(CacheView c, const float *__r
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int g = i / c.head_dim, d = i % c.head_dim;
-    long long off = cache_row(c, s, g, pos.p[s]);
+    const int p = pos.get(s);
+    if (p < 0) return;
+    long long off = cache_row(c, s, g, p);
     if (off < 0) return;  // unmapped page: nothing is written, attention reports NaN
     c.k[off + d] = k[(size_t)s * n + i];
     c.v[off + d] = v[(size_t)s * n + i];
@@ -66,7 +70,8 @@ __global__ __launch_bounds__(256) void k_rope_append(float *__restrict__ q, floa
     const int KV = c.kv_heads, hd = c.head_dim, half = hd >> 1;
     const int nq = H * half, nk = KV * half, nv = KV * hd;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    const int p = pos.p[s];
+    const int p = pos.get(s);
+    if (p < 0) return;
     if (i < nq + nk) {
         const bool isq = i < nq;
         const int pair = isq ? i : i - nq;

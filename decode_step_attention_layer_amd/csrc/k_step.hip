@@ -258,7 +258,8 @@ __device__ void qkv_item(const Ctx &cx, int item, XBlock *xs, float *red, int *f
             const int pr = rotate ? rope_row_s(lr, hd) : lr;
             val[it] = acc + ((bias && lr < rows) ? bias[pr] : 0.0f);
         }
-        const int p = a.pos.p[s];
+        const int pv = a.pos.get(s);
+        const int p = max(pv, 0);
 #pragma unroll
         for (int it = 0; it < R; it++) {
             const int lr = row0 + it * RPW + rsel;
@@ -278,7 +279,7 @@ __device__ void qkv_item(const Ctx &cx, int item, XBlock *xs, float *red, int *f
                     st_c(a.q + (size_t)s * rows + pr, o);
                 } else {
                     st_c((seg == 1 ? a.k : a.v) + (size_t)s * rows + pr, o);
-                    const long long off = cache_off(a, ly, s, pr / hd, p);
+                    const long long off = pv >= 0 ? cache_off(a, ly, s, pr / hd, p) : -1;
                     if (off >= 0) st_c((seg == 1 ? ly.kc : ly.vc) + off + pr % hd, o);
                 }
             }
@@ -313,7 +314,7 @@ __device__ void att_item(const Ctx &cx, int item, void *lds, int *flag) {
     const int cidx = item % a.nchunks;
     const int g = (item / a.nchunks) % KV;
     const int s = item / (a.nchunks * KV);
-    const int pos = a.pos.p[s];
+    const int pos = a.pos.get(s);
     const int L = pos + 1;
     const int t0 = cidx * a.chunk;
     if (t0 >= L) return;                              // no such chunk for this sequence
@@ -476,7 +477,7 @@ __device__ void mrg_item(const Ctx &cx, int item, float *lds, int *flag, bool la
     const int h = item % H, s = item / H;
     const int g = h / G, j = h % G;
     const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
-    const int L = a.pos.p[s] + 1;
+    const int L = a.pos.get(s) + 1;
     const int nc = (L + a.chunk - 1) / a.chunk;
     const size_t grp = (size_t)s * KV + g;
     if (!wait_ge(cx.c + 3 + grp, (unsigned)nc, cx.abort_word, flag)) return;

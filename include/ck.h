@@ -208,6 +208,27 @@ size_t ck_decode_step_workspace_size(const ck_layer_desc *desc, int layers, int 
 int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                    int layers, const float *x, const int32_t *pos_host, float *out,
                    void *ws, size_t ws_bytes, void *stream);
+/* Device-resident positions (the graph-capturable decode loop): as
+ * ck_decode_layer and ck_decode_step, but the m positions are read by the
+ * kernels from pos_dev (device memory, int32[m], 4-byte aligned) when they
+ * run, so that one captured launch sequence serves every later token: the
+ * caller advances pos_dev between replays (for example with a kernel in the
+ * same graph). The attention's chunk plan is sized for max_ctx attended
+ * tokens per sequence (the workspace: ck_decode_layer_workspace_size /
+ * ck_decode_step_workspace_size with the same max_ctx). Positions must lie in
+ * [0, min(max_ctx, cache capacity, rope_rows)); the host cannot check them:
+ * a sequence whose position is outside that range appends nothing, attends no
+ * token and gets undefined outputs, and nothing is accessed out of bounds.
+ * Host-side validation of everything else as in the host-position calls. */
+int ck_decode_layer_devpos(const ck_layer_desc *desc, const ck_layer_weights *w,
+                           const ck_kv_cache *kv, const float *x, const float *residual,
+                           const int32_t *pos_dev, int max_ctx, float *out, void *ws,
+                           size_t ws_bytes, void *stream);
+int ck_decode_step_devpos(const ck_layer_desc *desc, const ck_layer_weights *w,
+                          const ck_kv_cache *kv, int layers, const float *x,
+                          const int32_t *pos_dev, int max_ctx, float *out, void *ws,
+                          size_t ws_bytes, void *stream);
+
 /* Byte offset in the step workspace of the uint32 status word: zero after
  * a persistent step that completed, non-zero after one whose waits timed out
  * (read it after synchronizing). -1 for an invalid desc or a variant other

@@ -184,3 +184,28 @@ def test_step_validation_and_workspace(ck):
     cb = ck.CkKVCache(FAKE, FAKE, 8, 128, 64, 0, None, 0, 0)
     assert L.ck_decode_step(ctypes.byref(big), ws, (ck.CkKVCache * 1)(cb), 1, FAKE, pos,
                             FAKE + 4096, FAKE, nb, None) == ck.CK_EUNSUPPORTED
+
+
+def test_devpos_validation(ck):
+    L = ck.load()
+    d = ck.layer_desc(256, 4, 2, 64, 1, variant=ck.CK_VARIANT_FUSED)
+    n = ck.ck_decode_layer_workspace_size(d, 17)
+    w = ck.CkLayerWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, 64)
+    c = ck.CkKVCache(FAKE, FAKE, 2, 64, 64, 0, None, 0, 0)
+    ref = ctypes.byref
+    # no device positions, a non-positive bound, a misaligned position array
+    assert L.ck_decode_layer_devpos(ref(d), ref(w), ref(c), FAKE, FAKE, None, 17, FAKE + 4096,
+                                    FAKE, n, None) == ck.CK_EINVAL
+    assert L.ck_decode_layer_devpos(ref(d), ref(w), ref(c), FAKE, FAKE, FAKE, 0, FAKE + 4096,
+                                    FAKE, n, None) == ck.CK_EINVAL
+    assert L.ck_decode_layer_devpos(ref(d), ref(w), ref(c), FAKE, FAKE, FAKE + 2, 17,
+                                    FAKE + 4096, FAKE, n, None) == ck.CK_EINVAL
+    # the workspace is checked against max_ctx (clamped to the cache capacity)
+    assert L.ck_decode_layer_devpos(ref(d), ref(w), ref(c), FAKE, FAKE, FAKE, 17, FAKE + 4096,
+                                    FAKE, 256, None) == ck.CK_ENOSPC
+    ws = (ck.CkLayerWeights * 1)(w)
+    cs = (ck.CkKVCache * 1)(c)
+    assert L.ck_decode_step_devpos(ref(d), ws, cs, 1, FAKE, None, 17, FAKE + 4096, FAKE, n,
+                                   None) == ck.CK_EINVAL
+    assert L.ck_decode_step_devpos(ref(d), ws, cs, 1, FAKE, FAKE, 17, FAKE, FAKE, n,
+                                   None) == ck.CK_EINVAL      # out aliases x
