@@ -66,6 +66,14 @@ def lib():
         L.orc_gemv_q5_0.argtypes = [P, P, P, P, P, i, i]
         L.orc_gemv_q8_0.argtypes = [P, P, P, P, P, i, i]
         L.orc_rope.argtypes = [P, P, P, P, i, i, i, i]
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_f32.restype = f
+        L.orc_f32_to_bf16.argtypes = [f]
+        L.orc_f32_to_bf16.restype = ctypes.c_uint16
+        L.orc_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_to_f32.restype = f
+        L.orc_f32_to_e4m3.argtypes = [f]
+        L.orc_f32_to_e4m3.restype = ctypes.c_uint8
         L.orc_kv_append.argtypes = [ctypes.POINTER(OrcCache), i, i, P, P]
         L.orc_kv_append.restype = i
         L.orc_attention.argtypes = [P, ctypes.POINTER(OrcCache), i, i, i, P, P]
@@ -86,7 +94,12 @@ class OrcCache(ctypes.Structure):
         ("capacity", ctypes.c_int), ("page_size", ctypes.c_int),
         ("page_table", ctypes.c_void_p),
         ("max_pages_per_seq", ctypes.c_int), ("num_pages", ctypes.c_int),
+        ("dtype", ctypes.c_int), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
     ]
+
+
+KV_F32, KV_BF16, KV_FP8_E4M3 = 0, 1, 2
+_KV_NP = {KV_F32: np.float32, KV_BF16: np.uint16, KV_FP8_E4M3: np.uint8}
 
 
 class OrcDims(ctypes.Structure):
@@ -196,15 +209,20 @@ class Cache:
     page_table: np.ndarray | None = None
     max_pages_per_seq: int = 0
     num_pages: int = 0
+    dtype: int = KV_F32            # KV_F32 (float32 arrays), KV_BF16 (uint16), KV_FP8_E4M3 (uint8)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     def c(self) -> OrcCache:
-        assert self.k.dtype == np.float32 and self.v.dtype == np.float32
+        want = _KV_NP[self.dtype]
+        assert self.k.dtype == want and self.v.dtype == want
         assert self.k.flags["C_CONTIGUOUS"] and self.v.flags["C_CONTIGUOUS"]
         if self.page_table is not None:
             assert self.page_table.dtype == np.int32 and self.page_table.flags["C_CONTIGUOUS"]
         self._keep = OrcCache(
             _p(self.k), _p(self.v), self.kv_heads, self.head_dim, self.capacity,
             self.page_size, _p(self.page_table), self.max_pages_per_seq, self.num_pages,
+            self.dtype, self.k_scale, self.v_scale,
         )
         return self._keep
 
@@ -281,3 +299,47 @@ def decode_layer(dims: dict, weights: dict, cache: Cache, x, residual, pos, trac
     if rc:
         raise ValueError("oracle decode_layer: bad argument, position or page")
     return (out, bufs) if trace else out
+
+
+# ---- cache element codecs ---------------------------------------------------
+def bf16_to_f32(b: int) -> float:
+    return lib().orc_bf16_to_f32(int(b))
+
+
+def f32_to_bf16(x: float) -> int:
+    return int(lib().orc_f32_to_bf16(float(x)))
+
+
+def e4m3_to_f32(c: int) -> float:
+    return lib().orc_e4m3_to_f32(int(c))
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(lib().orc_f32_to_e4m3(float(x)))
+
+
+def encode_cache(values: np.ndarray, dtype: int, scale: float = 1.0) -> np.ndarray:
+    """Cache elements of `dtype` for fp32 values (the oracle's store rule,
+    element by element; fp8 stores fp32(x / scale))."""
+    x = np.ascontiguousarray(values, np.float32).reshape(-1)
+    if dtype == KV_F32:
+        return x.copy().reshape(values.shape)
+    if dtype == KV_BF16:
+        out = np.array([f32_to_bf16(v) for v in x], np.uint16)
+    else:
+        sc = np.float32(scale)
+        out = np.array([f32_to_e4m3(np.float32(v) / sc) for v in x], np.uint8)
+    return out.reshape(values.shape)
+
+
+def decode_cache(codes: np.ndarray, dtype: int, scale: float = 1.0) -> np.ndarray:
+    """fp32 values of cache elements (fp8: fp32(code value * scale))."""
+    c = np.ascontiguousarray(codes).reshape(-1)
+    if dtype == KV_F32:
+        return c.astype(np.float32).reshape(codes.shape)
+    if dtype == KV_BF16:
+        out = np.array([bf16_to_f32(v) for v in c], np.float32)
+    else:
+        sc = np.float32(scale)
+        out = np.array([np.float32(e4m3_to_f32(v)) * sc for v in c], np.float32)
+    return out.reshape(codes.shape)

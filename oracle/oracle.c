@@ -267,14 +267,108 @@ static long cache_row(const orc_cache *c, int seq, int g, int t)
     return (((long)page * c->kv_heads + g) * c->page_size + t % c->page_size) * hd;
 }
 
+/* ======================================================================== *
+ * Cache element codecs for the reduced-precision caches of the metrale
+ * paged decode launchers (paged_decode_attn_bf16 / _fp8, whose fp8 variant
+ * takes one k_scale and one v_scale). The pages name the types but not the
+ * FP8 flavour or the rounding of the store; readings: FP8 = OCP E4M3 (bias
+ * 7, no infinities, S.1111.111 the only NaN code, largest finite 448), value
+ * = code value x scale in fp32; storing rounds x / scale (fp32 division) to
+ * the nearest code, ties to even, saturating at +-448 (a cache stays
+ * finite), NaN -> 0x7F. bf16 = the top half of binary32, stored with
+ * round-to-nearest-even.
+ * ======================================================================== */
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+float orc_bf16_to_f32(uint16_t b) { return bits_f32((uint32_t)b << 16); }
+
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);            /* quiet NaN, sign kept */
+    /* add half an ulp of bf16 (minus one when the kept lsb is 0): ties to even */
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+float orc_e4m3_to_f32(uint8_t c)
+{
+    const int sgn = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+    double v;
+    if (e == 0xF && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);                 /* subnormal: m * 2^-6 / 8 */
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+    return (float)(sgn ? -v : v);
+}
+
+uint8_t orc_f32_to_e4m3(float f)
+{
+    if (isnan(f)) return 0x7F;
+    const uint8_t sgn = signbit(f) ? 0x80 : 0x00;
+    double a = fabs((double)f);
+    if (a >= 448.0) return sgn | 0x7E;                     /* saturate (inf included) */
+    /* the representable magnitudes are k * 2^(E-3) for the binade's exponent
+     * E (E >= -6; the subnormals share E = -6): scale, round half to even,
+     * and let a rounded-up mantissa of 16 carry into the next binade */
+    int E;
+    frexp(a, &E);                                          /* a = f * 2^E, f in [0.5, 1) */
+    E -= 1;                                                /* a in [2^E, 2^(E+1)) */
+    if (a == 0.0 || E < -6) E = -6;
+    double q = ldexp(a, 3 - E);                            /* exact: a power-of-two scaling */
+    double r = floor(q);
+    double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) == 1.0)) r += 1.0;
+    double v = ldexp(r, E - 3);
+    if (v >= 448.0) return sgn | 0x7E;
+    /* encode v exactly */
+    if (v < ldexp(1.0, -6)) return sgn | (uint8_t)(int)ldexp(v, 9);   /* subnormal code */
+    int e;
+    frexp(v, &e);
+    e -= 1;
+    int m = (int)(ldexp(v, 3 - e) - 8.0);
+    return sgn | (uint8_t)(((e + 7) << 3) | m);
+}
+
+/* element i of K (is_k) or V as the attention reads it */
+static double cache_value(const orc_cache *c, int is_k, long i)
+{
+    const void *p = is_k ? c->k : c->v;
+    switch (c->dtype) {
+    case ORC_KV_BF16: return (double)orc_bf16_to_f32(((const uint16_t *)p)[i]);
+    case ORC_KV_FP8_E4M3: {
+        const float sc = is_k ? c->k_scale : c->v_scale;
+        return (double)(orc_e4m3_to_f32(((const uint8_t *)p)[i]) * sc);   /* fp32 product */
+    }
+    default: return (double)((const float *)p)[i];
+    }
+}
+
+static void cache_store(const orc_cache *c, int is_k, long i, float x)
+{
+    void *p = is_k ? c->k : c->v;
+    switch (c->dtype) {
+    case ORC_KV_BF16: ((uint16_t *)p)[i] = orc_f32_to_bf16(x); break;
+    case ORC_KV_FP8_E4M3: {
+        const float sc = is_k ? c->k_scale : c->v_scale;
+        ((uint8_t *)p)[i] = orc_f32_to_e4m3(x / sc);                      /* fp32 division */
+        break;
+    }
+    default: ((float *)p)[i] = x; break;
+    }
+}
+
 /* STEP 6 — store the new token's k and v (after RoPE) at position pos. */
 int orc_kv_append(const orc_cache *c, int seq, int pos, const float *k, const float *v)
 {
     for (int g = 0; g < c->kv_heads; g++) {
         long off = cache_row(c, seq, g, pos);
         if (off < 0) return -1;
-        memcpy(c->k + off, k + (size_t)g * c->head_dim, sizeof(float) * c->head_dim);
-        memcpy(c->v + off, v + (size_t)g * c->head_dim, sizeof(float) * c->head_dim);
+        for (int d = 0; d < c->head_dim; d++) {
+            cache_store(c, 1, off + d, k[(size_t)g * c->head_dim + d]);
+            cache_store(c, 0, off + d, v[(size_t)g * c->head_dim + d]);
+        }
     }
     return 0;
 }
@@ -305,7 +399,7 @@ int orc_attention(const float *q, const orc_cache *c, int seq, int L, int H,
             if (off < 0) { rc = -1; break; }
             double s = 0.0;
             for (int d = 0; d < hd; d++)
-                s += (double)qh[d] * (double)c->k[off + d];
+                s += (double)qh[d] * cache_value(c, 1, off + d);
             score[t] = s * scale;
             if (score[t] > mx) mx = score[t];
         }
@@ -318,7 +412,7 @@ int orc_attention(const float *q, const orc_cache *c, int seq, int L, int H,
             score[t] = p;
             denom += p;
             for (int d = 0; d < hd; d++)
-                acc[d] += p * (double)c->v[off + d];
+                acc[d] += p * cache_value(c, 0, off + d);
         }
         for (int d = 0; d < hd; d++)
             out[(size_t)h * hd + d] = (float)(acc[d] / denom);

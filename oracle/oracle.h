@@ -58,13 +58,25 @@ void orc_gemv_q8_0(const uint8_t *W, const uint8_t *xq, const float *bias,
 void orc_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
               int pos, int H, int KV, int hd);
 
+/* ---- cache element codecs (the bf16 and fp8 KV caches) ----------------- */
+float    orc_bf16_to_f32(uint16_t b);   /* exact */
+uint16_t orc_f32_to_bf16(float f);      /* round to nearest, ties to even; NaN stays NaN */
+float    orc_e4m3_to_f32(uint8_t c);    /* OCP FP8 E4M3: bias 7, no infinities, S.1111.111 = NaN */
+uint8_t  orc_f32_to_e4m3(float f);      /* nearest, ties to even, saturating at +-448; NaN -> 0x7F */
+
 /* KV cache. page_size == 0: contiguous, [m][KV][capacity][hd] (sequence s at
  * s*KV*capacity*hd). page_size > 0: pools [num_pages][KV][page_size][hd],
  * token t of sequence s lives in page page_table[s*max_pages_per_seq + t/page_size]
- * at slot t % page_size. K and V use separate buffers of the same layout. */
+ * at slot t % page_size. K and V use separate buffers of the same layout.
+ * Element type (dtype): fp32; bf16; or FP8 E4M3 codes with one scale per
+ * tensor, value = fp32(e4m3(code) * k_scale) (k_scale for K, v_scale for V),
+ * stored code = e4m3(fp32(x / scale)). */
+#define ORC_KV_F32 0
+#define ORC_KV_BF16 1
+#define ORC_KV_FP8_E4M3 2
 typedef struct {
-    float *k;
-    float *v;
+    void *k;                 /* elements of type dtype */
+    void *v;
     int kv_heads;
     int head_dim;
     int capacity;            /* tokens per sequence (contiguous); unused if paged */
@@ -72,6 +84,8 @@ typedef struct {
     const int32_t *page_table;
     int max_pages_per_seq;
     int num_pages;
+    int dtype;               /* ORC_KV_* */
+    float k_scale, v_scale;  /* FP8 only */
 } orc_cache;
 
 /* Returns 0, or -1 if the token has no valid home (page id out of range). */
