@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=sorted(DESCRIBE))
     ap.add_argument("--variant", default="fused", choices=["fused", "chain", "persistent"])
+    ap.add_argument("--kv", default="f32", choices=["f32", "bf16", "fp8"],
+                    help="KV-cache element type (fp8: E4M3 with one scale per tensor)")
     ap.add_argument("--eager", action="store_true", help="launch from Python, no graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU-baseline sample")
@@ -97,9 +99,10 @@ def main():
                "persistent": ck.CK_VARIANT_PERSISTENT}[args.variant]
     persistent = variant == ck.CK_VARIANT_PERSISTENT
     t0 = time.time()
-    stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu)
+    kv_dtype = {"f32": synth.KV_F32, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}[args.kv]
+    stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu, kv_dtype=kv_dtype)
     log(f"[bench] {args.config}: {stack.nlayers} layers on device in {time.time() - t0:.1f}s")
-    nbytes = synth.algorithmic_bytes(cfg, stack.lens)
+    nbytes = synth.algorithmic_bytes(cfg, stack.lens, kv_dtype)
     step_bytes = nbytes["total"] * stack.nlayers
     replicas = 1
     if step_bytes < 3 * MALL_BYTES:
@@ -191,7 +194,9 @@ def main():
         "dtype": "int8-dot/f32",
         "data": "synthetic (seeded; quantized N(0,0.02) weights, N(0,1) activations and cache)",
         "config": {
-            "workload": f"{args.config}: {DESCRIBE[args.config]}",
+            "workload": f"{args.config}: {DESCRIBE[args.config]}" + (
+                "" if args.kv == "f32" else f", {args.kv} KV cache"),
+            "kv_cache": args.kv,
             "variant": args.variant,
             "launch": "eager" if args.eager else "hip-graph",
             "layers": stack.nlayers,
@@ -261,7 +266,9 @@ def roofline(args, stack, desc, ws, nbytes):
         name, gbs, us, b = "k_gemv", wo_gbs, wo_us, wo_bytes
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_GBS, 4),
-            "traffic": recorded_traffic(name, args.config), "traffic_unit": "bytes per launch",
+            "traffic": recorded_traffic(name, args.config if args.kv == "f32"
+                                        else f"{args.config}-{args.kv}"),
+            "traffic_unit": "bytes per launch",
             "kernel": name,
             "us_per_launch": round(us, 3), "bytes_per_launch": b,
             "other": {"k_attn_us": round(attn_us, 3), "k_attn_GBs": round(att_gbs, 1),
@@ -315,12 +322,13 @@ def cpu_baseline(args, stack, nbytes):
     while t_spent < args.cpu_seconds:
         L = stack.layers[li % stack.nlayers]
         h = L.host
+        kvd = dict(dtype=stack.kv_dtype, k_scale=stack.k_scale, v_scale=stack.v_scale)
         if cfg.page_size:
             c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, page_size=cfg.page_size,
                              page_table=h["table"], max_pages_per_seq=cfg.max_pages_per_seq,
-                             num_pages=h["k"].shape[0])
+                             num_pages=h["k"].shape[0], **kvd)
         else:
-            c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, capacity=cfg.capacity)
+            c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, capacity=cfg.capacity, **kvd)
         w = dict(h, rope_cos=cos, rope_sin=sin)
         t = time.perf_counter()
         oracle.decode_layer(dims, w, c, x, x, stack.pos)

@@ -25,6 +25,9 @@ CK_VARIANT_CHAIN = 0
 CK_VARIANT_FUSED = 1
 CK_VARIANT_PERSISTENT = 2
 CK_MAX_STEP_LAYERS = 32
+CK_KV_F32 = 0
+CK_KV_BF16 = 1
+CK_KV_FP8_E4M3 = 2
 
 EXPORTS = (
     "ck_strerror", "ck_version", "ck_rmsnorm", "ck_quantize_q8_0", "ck_gemv_q5_0_q8_0",
@@ -49,6 +52,7 @@ class CkKVCache(ctypes.Structure):
         ("capacity", ctypes.c_int32), ("page_size", ctypes.c_int32),
         ("page_table", ctypes.c_void_p),
         ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
     ]
 
 
@@ -183,9 +187,10 @@ def ck_rope(q, k, cos_tab, sin_tab, tab_rows, pos, m, H, KV, hd, stream=None):
 
 
 def kv_cache(k, v, kv_heads, head_dim, capacity=0, page_size=0, page_table=None,
-             max_pages_per_seq=0, num_pages=0) -> CkKVCache:
+             max_pages_per_seq=0, num_pages=0, dtype=CK_KV_F32, k_scale=1.0,
+             v_scale=1.0) -> CkKVCache:
     return CkKVCache(_ptr(k), _ptr(v), kv_heads, head_dim, capacity, page_size,
-                     _ptr(page_table), max_pages_per_seq, num_pages)
+                     _ptr(page_table), max_pages_per_seq, num_pages, dtype, k_scale, v_scale)
 
 
 def ck_kv_append(cache: CkKVCache, k, v, pos, m, stream=None):

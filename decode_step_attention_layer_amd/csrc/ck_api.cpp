@@ -22,6 +22,12 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Validates the cache descriptor and builds the kernel view.
 int cache_view(const ck_kv_cache *kv, CacheView *out) {
     if (!kv || !kv->k || !kv->v || kv->kv_heads <= 0 || kv->head_dim <= 0) return CK_EINVAL;
+    if (kv->dtype != CK_KV_F32 && kv->dtype != CK_KV_BF16 && kv->dtype != CK_KV_FP8_E4M3)
+        return CK_EINVAL;
+    if (kv->dtype == CK_KV_FP8_E4M3 &&
+        !(kv->k_scale > 0.0f && kv->k_scale < INFINITY && kv->v_scale > 0.0f &&
+          kv->v_scale < INFINITY))
+        return CK_EINVAL;
     if (!al(kv->k, 16) || !al(kv->v, 16) || kv->head_dim % 4) return CK_EINVAL;
     if (kv->page_size < 0) return CK_EINVAL;
     if (kv->page_size == 0) {
@@ -39,6 +45,9 @@ int cache_view(const ck_kv_cache *kv, CacheView *out) {
     out->page_size = kv->page_size;
     out->max_pages = kv->max_pages_per_seq;
     out->num_pages = kv->num_pages;
+    out->dtype = kv->dtype;
+    out->k_scale = kv->k_scale;
+    out->v_scale = kv->v_scale;
     return CK_OK;
 }
 
@@ -408,6 +417,8 @@ int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const
     }
 
     if (!step_supported(d.D, d.H, d.KV, d.head_dim, d.m, plan.nchunks)) return CK_EUNSUPPORTED;
+    for (int l = 0; l < layers; l++)
+        if (kv[l].dtype != CK_KV_F32) return CK_EUNSUPPORTED;   // fp32 caches only
     StepLaunch sl;
     memset(&sl, 0, sizeof(sl));
     sl.L = layers;
@@ -452,8 +463,8 @@ int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const
         s.bv = w[l].bv;
         s.bo = w[l].bo;
         s.gamma = w[l].gamma;
-        s.kc = kv[l].k;
-        s.vc = kv[l].v;
+        s.kc = static_cast<float *>(kv[l].k);
+        s.vc = static_cast<float *>(kv[l].v);
         s.table = kv[l].page_table;
     }
     return hip_rc(launch_step(sl, st));

@@ -177,6 +177,47 @@ __device__ __forceinline__ uint32_t align2(uint32_t hi, uint32_t lo) {
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x3a4 __attribute__((ext_vector_type(3), aligned(4)));
 
+// ----------------------------------------------- cache element codecs -----
+// bf16: the top half of binary32; stores round to nearest, ties to even.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; no
+// infinities; S.1111.111 is NaN; largest finite 448; subnormals m * 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t sgn = (c & 0x80u) << 24, e = (c >> 3) & 0xFu, m = c & 7u;
+    if (e == 0xFu && m == 7u) return __uint_as_float(sgn | 0x7FC00000u);
+    if (e == 0u) return __uint_as_float(sgn | __float_as_uint((float)m * 0x1p-9f));
+    return __uint_as_float(sgn | ((e + 120u) << 23) | (m << 20));
+}
+
+// Nearest code, ties to even, saturating at +-448; NaN -> 0x7F.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7F;
+    const uint32_t sgn = (u >> 24) & 0x80u;
+    const float a = __uint_as_float(u & 0x7FFFFFFFu);
+    if (a >= 448.0f) return (uint8_t)(sgn | 0x7Eu);
+    if (a < 0x1p-6f) {
+        // subnormal codes m * 2^-9 (m = 8 is the smallest normal, code 0x08)
+        return (uint8_t)(sgn | (uint32_t)rintf(a * 512.0f));
+    }
+    int E = (int)((u >> 23) & 0xFFu) - 127;                // a in [2^E, 2^(E+1)), E in [-6, 8]
+    uint32_t mant = u & 0x7FFFFFu;
+    mant += 0x7FFFFu + ((mant >> 20) & 1u);                // round the 23-bit mantissa to 3 bits
+    if (mant & 0x800000u) {                                // carried into the next binade
+        E += 1;
+        mant = 0;
+    }
+    return (uint8_t)(sgn | ((uint32_t)(E + 7) << 3) | ((mant >> 20) & 7u));
+}
+
 // Device-coherent accesses between workgroups of one launch: relaxed
 // agent-scope atomic loads and stores, which gfx950 issues as ordinary vector
 // loads/stores with device-scope coherence (no L2 write-back or invalidate).

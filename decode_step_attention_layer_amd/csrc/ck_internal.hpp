@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/ck.h"
+#include "ck_device.hpp"
 
 namespace ck {
 
@@ -31,11 +32,80 @@ struct Positions {
 
 // Cache view passed by value to kernels (mirrors ck_kv_cache).
 struct CacheView {
-    float *k;
-    float *v;
+    void *k;
+    void *v;
     const int32_t *table;
     int kv_heads, head_dim, capacity, page_size, max_pages, num_pages;
+    int dtype;                // CK_KV_*
+    float k_scale, v_scale;   // fp8
 };
+
+// Stores element idx of K (is_k) or V from an fp32 value, in the cache's type.
+__device__ __forceinline__ void cache_put(const CacheView &c, bool is_k, long long idx, float x) {
+    void *base = is_k ? c.k : c.v;
+    if (c.dtype == CK_KV_BF16) {
+        static_cast<uint16_t *>(base)[idx] = f32_to_bf16(x);
+    } else if (c.dtype == CK_KV_FP8_E4M3) {
+        static_cast<uint8_t *>(base)[idx] = f32_to_e4m3(x / (is_k ? c.k_scale : c.v_scale));
+    } else {
+        static_cast<float *>(base)[idx] = x;
+    }
+}
+
+// Four consecutive elements (idx a multiple of 4) of a cache whose element
+// type DT is known at compile time: the raw load, then the conversion to
+// fp32 (split, so that loads can be issued ahead of their use).
+template <int DT>
+struct CacheRaw4 {
+    typedef uint4 type;      // fp32: 16 bytes
+};
+template <>
+struct CacheRaw4<CK_KV_BF16> {
+    typedef uint2 type;      // 8 bytes
+};
+template <>
+struct CacheRaw4<CK_KV_FP8_E4M3> {
+    typedef uint32_t type;   // 4 bytes
+};
+
+template <int DT>
+__device__ __forceinline__ typename CacheRaw4<DT>::type cache_raw4(const CacheView &c, bool is_k,
+                                                                   long long idx) {
+    typedef typename CacheRaw4<DT>::type R;
+    const void *base = is_k ? c.k : c.v;
+    if constexpr (DT == CK_KV_BF16)
+        return *reinterpret_cast<const R *>(static_cast<const uint16_t *>(base) + idx);
+    else if constexpr (DT == CK_KV_FP8_E4M3)
+        return *reinterpret_cast<const R *>(static_cast<const uint8_t *>(base) + idx);
+    else
+        return *reinterpret_cast<const R *>(static_cast<const float *>(base) + idx);
+}
+
+template <int DT>
+__device__ __forceinline__ typename CacheRaw4<DT>::type cache_raw4_zero() {
+    if constexpr (DT == CK_KV_BF16) return make_uint2(0u, 0u);
+    else if constexpr (DT == CK_KV_FP8_E4M3) return 0u;
+    else return make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <int DT>
+__device__ __forceinline__ float4 cache_cvt4(const CacheView &c, bool is_k,
+                                             typename CacheRaw4<DT>::type r) {
+    if constexpr (DT == CK_KV_BF16) {
+        return make_float4(bf16_to_f32(r.x & 0xFFFFu), bf16_to_f32(r.x >> 16),
+                           bf16_to_f32(r.y & 0xFFFFu), bf16_to_f32(r.y >> 16));
+    } else if constexpr (DT == CK_KV_FP8_E4M3) {
+        // v_cvt_pk_f32_fp8 decodes OCP E4M3 on gfx950 (checked against the
+        // format's definition over all 256 codes, NaN included)
+        const float sc = is_k ? c.k_scale : c.v_scale;
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r, true);
+        return make_float4(lo[0] * sc, lo[1] * sc, hi[0] * sc, hi[1] * sc);
+    } else {
+        return make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                           __uint_as_float(r.w));
+    }
+}
 
 // Element offset of (seq, kv head, token) in the K (or V) buffer, or -1 if the
 // token's page is unmapped or out of range. Shared by the kernels.

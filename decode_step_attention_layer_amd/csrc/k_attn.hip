@@ -61,7 +61,7 @@ struct Smem {
     int bad;
 };
 
-template <int HD, int G, bool PAGED>
+template <int HD, int G, bool PAGED, int DT>
 __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
     static_assert(HD % 64 == 0 && G >= 1 && G <= kMaxG, "shape");
     constexpr int NT = G > 4 ? 512 : 256;            // threads
@@ -111,7 +111,8 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
     // loader geometry: this thread loads column ld_col of rows ld_row + i*ROWS_PER_LD
     const int ld_col = tid % C4, ld_row = tid / C4;
     const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
-    float4 kreg[NLD], vreg[NLD];
+    typedef typename CacheRaw4<DT>::type Raw;
+    Raw kreg[NLD], vreg[NLD];   // raw elements (fp32, bf16 or fp8), converted at the LDS store
     auto fetch = [&](int st) {
 #pragma unroll
         for (int i = 0; i < NLD; i++) {
@@ -133,11 +134,10 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
                 }
             }
             if (off >= 0) {
-                kreg[i] = *reinterpret_cast<const float4 *>(a.c.k + off + 4 * ld_col);
-                vreg[i] = *reinterpret_cast<const float4 *>(a.c.v + off + 4 * ld_col);
+                kreg[i] = cache_raw4<DT>(a.c, true, off + 4 * ld_col);
+                vreg[i] = cache_raw4<DT>(a.c, false, off + 4 * ld_col);
             } else {
-                kreg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-                vreg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                kreg[i] = vreg[i] = cache_raw4_zero<DT>();
             }
         }
     };
@@ -158,8 +158,8 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < NLD; i++) {
             const int r = ld_row + i * ROWS_PER_LD;
-            *reinterpret_cast<float4 *>(&sk[r * S + 4 * ld_col]) = kreg[i];
-            *reinterpret_cast<float4 *>(&sv[r * S + 4 * ld_col]) = vreg[i];
+            *reinterpret_cast<float4 *>(&sk[r * S + 4 * ld_col]) = cache_cvt4<DT>(a.c, true, kreg[i]);
+            *reinterpret_cast<float4 *>(&sv[r * S + 4 * ld_col]) = cache_cvt4<DT>(a.c, false, vreg[i]);
         }
         __syncthreads();
         if (st + kTile < t1) fetch(st + kTile);      // next tile's loads in flight
@@ -371,10 +371,18 @@ template <int HD, int G>
 hipError_t launch_t(const AttnArgs &a, int m, bool paged, hipStream_t st) {
     constexpr int NT = G > 4 ? 512 : 256;
     const dim3 grid(a.first[m], a.c.kv_heads);
-    if (paged)
-        hipLaunchKernelGGL((k_attn<HD, G, true>), grid, dim3(NT), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_attn<HD, G, false>), grid, dim3(NT), 0, st, a);
+    const int dt = a.c.dtype;
+#define CK_ATTN_LAUNCH(P, D) hipLaunchKernelGGL((k_attn<HD, G, P, D>), grid, dim3(NT), 0, st, a)
+    if (paged) {
+        if (dt == CK_KV_BF16) CK_ATTN_LAUNCH(true, CK_KV_BF16);
+        else if (dt == CK_KV_FP8_E4M3) CK_ATTN_LAUNCH(true, CK_KV_FP8_E4M3);
+        else CK_ATTN_LAUNCH(true, CK_KV_F32);
+    } else {
+        if (dt == CK_KV_BF16) CK_ATTN_LAUNCH(false, CK_KV_BF16);
+        else if (dt == CK_KV_FP8_E4M3) CK_ATTN_LAUNCH(false, CK_KV_FP8_E4M3);
+        else CK_ATTN_LAUNCH(false, CK_KV_F32);
+    }
+#undef CK_ATTN_LAUNCH
     return hipGetLastError();
 }
 

@@ -183,7 +183,7 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
                 } else {
                     (seg == 1 ? a.k : a.v)[(size_t)s * rows + pr] = out;
                     const long long off = pv >= 0 ? cache_row(a.c, s, g, p) : -1;
-                    if (off >= 0) (seg == 1 ? a.c.k : a.c.v)[off + d] = out;
+                    if (off >= 0) cache_put(a.c, seg == 1, off + d, out);
                 }
             }
         }

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void k_kv_append(CacheView c, const float *__r
     if (p < 0) return;
     long long off = cache_row(c, s, g, p);
     if (off < 0) return;  // unmapped page: nothing is written, attention reports NaN
-    c.k[off + d] = k[(size_t)s * n + i];
-    c.v[off + d] = v[(size_t)s * n + i];
+    cache_put(c, true, off + d, k[(size_t)s * n + i]);
+    cache_put(c, false, off + d, v[(size_t)s * n + i]);
 }
 
 // RoPE of q and k plus the append of (rotated k, v) at the token's position,
@@ -86,15 +86,15 @@ __global__ __launch_bounds__(256) void k_rope_append(float *__restrict__ q, floa
         if (!isq) {
             long long off = cache_row(c, s, head, p);
             if (off >= 0) {
-                c.k[off + d] = ra;
-                c.k[off + d + half] = rb;
+                cache_put(c, true, off + d, ra);
+                cache_put(c, true, off + d + half, rb);
             }
         }
     } else if (i < nq + nk + nv) {
         const int e = i - nq - nk;
         const int head = e / hd, d = e % hd;
         long long off = cache_row(c, s, head, p);
-        if (off >= 0) c.v[off + d] = v[(size_t)s * nv + e];
+        if (off >= 0) cache_put(c, false, off + d, v[(size_t)s * nv + e]);
     }
 }
 

@@ -35,6 +35,13 @@ Q5_0_BYTES = 22
 # tensor ids in the seed sequence
 T_X, T_GAMMA, T_BQ, T_BK, T_BV, T_BO, T_WQ, T_WK, T_WV, T_WO = range(10)
 T_KCACHE, T_VCACHE, T_LENS, T_PERM = 10, 11, 12, 13
+T_KCODES, T_VCODES = 14, 15
+
+# Reduced-precision caches: element types (the C ABI's CK_KV_*) and the fixed
+# per-tensor scales of the synthetic fp8 caches.
+KV_F32, KV_BF16, KV_FP8 = 0, 1, 2
+FP8_K_SCALE, FP8_V_SCALE = 0.25, 0.5
+KV_ELEM_BYTES = {KV_F32: 4, KV_BF16: 2, KV_FP8: 1}
 
 
 @dataclass(frozen=True)
@@ -234,20 +241,41 @@ def paged_cache(cfg: Config, layer: int, poison: float = float("nan"), spare_pag
     return k, v, table, lens
 
 
+def cache_codes(values: np.ndarray, kv_dtype: int, cfg_index: int, layer: int,
+                is_k: bool) -> np.ndarray:
+    """Synthetic cache contents of a reduced-precision cache, built from the
+    fp32 cache `values` (NaN marks poisoned slots). bf16: the upper half of
+    each fp32 value (truncation, a plain bit extraction; NaN stays NaN); fp8:
+    random E4M3 codes of magnitude 2^-3..7.5 with random signs, drawn from a
+    stream of their own, and the NaN code 0x7F where the fp32 cache is
+    poisoned. Test data only: the store rule under test is not involved."""
+    if kv_dtype == KV_F32:
+        return values
+    if kv_dtype == KV_BF16:
+        return (np.ascontiguousarray(values, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    g = rng(cfg_index, layer, T_KCODES if is_k else T_VCODES)
+    exp_field = g.integers(4, 10, size=values.shape, dtype=np.uint8)     # 2^-3 .. 2^2
+    mant = g.integers(0, 8, size=values.shape, dtype=np.uint8)
+    sign = (g.integers(0, 2, size=values.shape, dtype=np.uint8) << 7).astype(np.uint8)
+    codes = (sign | (exp_field << 3) | mant).astype(np.uint8)
+    codes[np.isnan(values)] = 0x7F
+    return codes
+
+
 def rope_for(cfg: Config):
     return rope_tables(cfg.rope_rows, cfg.hd, cfg.theta)
 
 
-def algorithmic_bytes(cfg: Config, lens=None) -> dict:
-    """Bytes one layer step must move: quantized weight blocks + fp32 K and V
-    of every attended token (L = pos + 1 per sequence)."""
+def algorithmic_bytes(cfg: Config, lens=None, kv_dtype: int = KV_F32) -> dict:
+    """Bytes one layer step must move: quantized weight blocks + K and V of
+    every attended token (L = pos + 1 per sequence) in the cache's type."""
     D, HD, KD = cfg.D, cfg.H * cfg.hd, cfg.KV * cfg.hd
     w = (HD * D // QK) * Q5_0_BYTES + (KD * D // QK) * Q5_0_BYTES \
         + (KD * D // QK) * Q8_0_BYTES + (D * HD // QK) * Q5_0_BYTES
     if lens is None:
         lens = context_lengths(cfg)
     tokens = int(np.sum(np.asarray(lens, np.int64) + 1))
-    kv = tokens * KD * 4 * 2
+    kv = tokens * KD * KV_ELEM_BYTES[kv_dtype] * 2
     return {"weights": w, "kv": kv, "total": w + kv}
 
 

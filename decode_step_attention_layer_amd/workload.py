@@ -33,8 +33,11 @@ class DeviceStack:
 
     def __init__(self, cfg: synth.Config, device="cuda", poison: float = float("nan"),
                  keep_host: bool = False, spare_pages: int = 0, layers: int | None = None,
-                 threads: int = 8):
+                 threads: int = 8, kv_dtype: int = synth.KV_F32):
         self.cfg = cfg
+        self.kv_dtype = kv_dtype
+        self.k_scale = synth.FP8_K_SCALE if kv_dtype == synth.KV_FP8 else 1.0
+        self.v_scale = synth.FP8_V_SCALE if kv_dtype == synth.KV_FP8 else 1.0
         self.device = torch.device(device)
         self.nlayers = cfg.layers if layers is None else layers
         cos, sin = synth.rope_for(cfg)
@@ -55,6 +58,9 @@ class DeviceStack:
             else:
                 k, v = synth.contiguous_cache(cfg, layer, poison)
                 c = dict(k=k, v=v)
+            if kv_dtype != synth.KV_F32:
+                c["k"] = synth.cache_codes(c["k"], kv_dtype, cfg.index, layer, True)
+                c["v"] = synth.cache_codes(c["v"], kv_dtype, cfg.index, layer, False)
             return layer, w, c
 
         self.layers: list[DeviceLayer] = []
@@ -78,9 +84,10 @@ class DeviceStack:
             t = {n: v.clone() for n, v in L.tensors.items()}
             if cfg.page_size:
                 cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, 0, cfg.page_size, t["table"],
-                                    cfg.max_pages_per_seq, L.cache.num_pages)
+                                    cfg.max_pages_per_seq, L.cache.num_pages, **self._kvargs())
             else:
-                cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity)
+                cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity,
+                                    **self._kvargs())
             weights = ck.layer_weights(t["wq"], t["wk"], t["wv"], t["wo"], t["bq"], t["bk"],
                                        t["bv"], t["bo"], t["gamma"], self.rope[0], self.rope[1],
                                        self.rope_rows)
@@ -100,14 +107,17 @@ class DeviceStack:
         if cfg.page_size:
             t["table"] = to_dev(c["table"], dev)
             cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, 0, cfg.page_size, t["table"],
-                                cfg.max_pages_per_seq, c["k"].shape[0])
+                                cfg.max_pages_per_seq, c["k"].shape[0], **self._kvargs())
         else:
-            cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity)
+            cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity, **self._kvargs())
         weights = ck.layer_weights(t["wq"], t["wk"], t["wv"], t["wo"], t["bq"], t["bk"], t["bv"],
                                    t["bo"], t["gamma"], self.rope[0], self.rope[1], self.rope_rows)
         host = dict(w, **{"k": c["k"], "v": c["v"]}, **({"table": c["table"]} if "table" in c else {})) \
             if keep_host else {}
         return DeviceLayer(t, weights, cache, host)
+
+    def _kvargs(self) -> dict:
+        return dict(dtype=self.kv_dtype, k_scale=self.k_scale, v_scale=self.v_scale)
 
     def desc(self, variant=ck.CK_VARIANT_FUSED, attn_chunk=0) -> ck.CkLayerDesc:
         c = self.cfg

@@ -60,16 +60,29 @@ extern "C" {
  *   [0, num_pages) is never dereferenced: the attention of that sequence
  *   returns NaN. */
 typedef struct ck_kv_cache {
-    float *k;
-    float *v;
+    void *k;                     /* elements of type dtype, 16-byte aligned */
+    void *v;
     int32_t kv_heads;
-    int32_t head_dim;
+    int32_t head_dim;            /* a multiple of 4 */
     int32_t capacity;            /* contiguous: tokens per sequence */
     int32_t page_size;           /* 0 = contiguous */
     const int32_t *page_table;   /* device, [m][max_pages_per_seq] */
     int32_t max_pages_per_seq;
     int32_t num_pages;
+    int32_t dtype;               /* CK_KV_F32 (0, the default), CK_KV_BF16, CK_KV_FP8_E4M3 */
+    float k_scale, v_scale;      /* CK_KV_FP8_E4M3: value = e4m3(code) * scale (fp32) */
 } ck_kv_cache;
+
+/* Element types of the cache (the bf16 and fp8 caches of the metrale page's
+ * paged_decode_attn_bf16 / paged_decode_attn_fp8, whose fp8 variant takes one
+ * k_scale and one v_scale). FP8 is OCP E4M3 (bias 7, largest finite 448,
+ * S.1111.111 the only NaN). A store rounds to nearest, ties to even; an fp8
+ * store encodes fp32(x / scale) and saturates at +-448 (NaN -> 0x7F). The
+ * attention reads every element back as fp32 (fp8: the product of the code
+ * value and the scale, in fp32). */
+#define CK_KV_F32 0
+#define CK_KV_BF16 1
+#define CK_KV_FP8_E4M3 2
 
 #define CK_VARIANT_CHAIN 0       /* one kernel per step (the unfused chain) */
 #define CK_VARIANT_FUSED 1       /* steps fused into four kernels per layer */
