@@ -221,8 +221,10 @@ size_t ck_decode_step_workspace_size(const ck_layer_desc *desc, int layers, int 
 int ck_decode_step(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                    int layers, const float *x, const int32_t *pos_host, float *out,
                    void *ws, size_t ws_bytes, void *stream);
-/* Device-resident positions (the graph-capturable decode loop): as
- * ck_decode_layer and ck_decode_step, but the m positions are read by the
+/* Device-resident positions (the graph-capturable decode loop of the
+ * spark_model page attn_v41/decode.rs: the per-token position lives in device
+ * memory and the launch arguments stay constant): as ck_decode_layer and
+ * ck_decode_step, but the m positions are read by the
  * kernels from pos_dev (device memory, int32[m], 4-byte aligned) when they
  * run, so that one captured launch sequence serves every later token: the
  * caller advances pos_dev between replays (for example with a kernel in the
