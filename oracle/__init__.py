@@ -95,6 +95,7 @@ class OrcCache(ctypes.Structure):
         ("page_table", ctypes.c_void_p),
         ("max_pages_per_seq", ctypes.c_int), ("num_pages", ctypes.c_int),
         ("dtype", ctypes.c_int), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("ring", ctypes.c_int), ("window", ctypes.c_int),
     ]
 
 
@@ -212,6 +213,8 @@ class Cache:
     dtype: int = KV_F32            # KV_F32 (float32 arrays), KV_BF16 (uint16), KV_FP8_E4M3 (uint8)
     k_scale: float = 1.0
     v_scale: float = 1.0
+    ring: bool = False             # contiguous only: token t lives in slot t % capacity
+    window: int = 0                # > 0: attention reads only the last `window` tokens
 
     def c(self) -> OrcCache:
         want = _KV_NP[self.dtype]
@@ -222,7 +225,7 @@ class Cache:
         self._keep = OrcCache(
             _p(self.k), _p(self.v), self.kv_heads, self.head_dim, self.capacity,
             self.page_size, _p(self.page_table), self.max_pages_per_seq, self.num_pages,
-            self.dtype, self.k_scale, self.v_scale,
+            self.dtype, self.k_scale, self.v_scale, int(self.ring), int(self.window),
         )
         return self._keep
 

@@ -251,15 +251,20 @@ void orc_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
  * table of the metrale paged decode launchers, one entry per page of
  * page_size tokens; the page pool is [pages][KV][page_size][hd] (reading: the
  * head-major order of the contiguous layout, kept inside each page).
+ * Ring (contiguous only): token t in slot t % capacity.
  * Returns the float offset of (seq, kv head, token), or -1 if unmapped.
  * ======================================================================== */
 static long cache_row(const orc_cache *c, int seq, int g, int t)
 {
     const long hd = c->head_dim;
     if (c->page_size == 0) {
-        if (t < 0 || t >= c->capacity) return -1;
-        return (((long)seq * c->kv_heads + g) * c->capacity + t) * hd;
+        if (t < 0 || (!c->ring && t >= c->capacity)) return -1;
+        /* ring (the window ring of the spark_model page's decode_body, written
+         * at pos % window): slot t % capacity */
+        const int slot = c->ring ? t % c->capacity : t;
+        return (((long)seq * c->kv_heads + g) * c->capacity + slot) * hd;
     }
+    if (c->ring) return -1;
     int lp = t / c->page_size;
     if (t < 0 || lp >= c->max_pages_per_seq) return -1;
     int page = c->page_table[(long)seq * c->max_pages_per_seq + lp];
@@ -385,6 +390,11 @@ int orc_attention(const float *q, const orc_cache *c, int seq, int L, int H,
                   float *out, double *probs)
 {
     const int KV = c->kv_heads, hd = c->head_dim;
+    /* sliding window (the metrale page's sliding_window: 0 = the whole
+     * sequence, else only the last `window` positions): tokens [t0, L) */
+    const int t0 = (c->window > 0 && L > c->window) ? L - c->window : 0;
+    /* a ring keeps only the last `capacity` tokens: older ones are gone */
+    if (c->ring && L - t0 > c->capacity) return -1;
     const double scale = 1.0 / sqrt((double)hd);
     double *score = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
     double *acc = (double *)malloc(sizeof(double) * (size_t)hd);
@@ -394,7 +404,7 @@ int orc_attention(const float *q, const orc_cache *c, int seq, int L, int H,
         const int g = h * KV / H;
         const float *qh = q + (size_t)h * hd;
         double mx = -INFINITY;
-        for (int t = 0; t < L; t++) {
+        for (int t = t0; t < L; t++) {
             long off = cache_row(c, seq, g, t);
             if (off < 0) { rc = -1; break; }
             double s = 0.0;
@@ -406,7 +416,7 @@ int orc_attention(const float *q, const orc_cache *c, int seq, int L, int H,
         if (rc) break;
         double denom = 0.0;
         for (int d = 0; d < hd; d++) acc[d] = 0.0;
-        for (int t = 0; t < L; t++) {
+        for (int t = t0; t < L; t++) {
             long off = cache_row(c, seq, g, t);
             double p = exp(score[t] - mx);
             score[t] = p;
@@ -418,7 +428,7 @@ int orc_attention(const float *q, const orc_cache *c, int seq, int L, int H,
             out[(size_t)h * hd + d] = (float)(acc[d] / denom);
         if (probs)
             for (int t = 0; t < L; t++)
-                probs[(size_t)h * L + t] = score[t] / denom;
+                probs[(size_t)h * L + t] = t < t0 ? 0.0 : score[t] / denom;
     }
     free(score);
     free(acc);

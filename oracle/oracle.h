@@ -68,6 +68,9 @@ uint8_t  orc_f32_to_e4m3(float f);      /* nearest, ties to even, saturating at 
  * s*KV*capacity*hd). page_size > 0: pools [num_pages][KV][page_size][hd],
  * token t of sequence s lives in page page_table[s*max_pages_per_seq + t/page_size]
  * at slot t % page_size. K and V use separate buffers of the same layout.
+ * Sliding window: window > 0 attends the tokens t >= L - window only; with
+ * ring = 1 a contiguous cache is a ring of `capacity` slots (token t in slot
+ * t % capacity), which then holds the last `capacity` tokens.
  * Element type (dtype): fp32; bf16; or FP8 E4M3 codes with one scale per
  * tensor, value = fp32(e4m3(code) * k_scale) (k_scale for K, v_scale for V),
  * stored code = e4m3(fp32(x / scale)). */
@@ -86,6 +89,8 @@ typedef struct {
     int num_pages;
     int dtype;               /* ORC_KV_* */
     float k_scale, v_scale;  /* FP8 only */
+    int ring;                /* contiguous only: token t lives in slot t % capacity */
+    int window;              /* > 0: attention reads only the last `window` tokens */
 } orc_cache;
 
 /* Returns 0, or -1 if the token has no valid home (page id out of range). */
