@@ -53,6 +53,7 @@ class CkKVCache(ctypes.Structure):
         ("page_table", ctypes.c_void_p),
         ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("window", ctypes.c_int32), ("ring", ctypes.c_int32),
     ]
 
 
@@ -99,7 +100,7 @@ def load():
         "ck_attn_workspace_size": ([I, I, I, I, I, I], S),
         "ck_attn_decode_gqa": ([P, ctypes.POINTER(CkKVCache), IP, P, I, I, F, I, P, S, P], I),
         "ck_attn_partial": ([P, ctypes.POINTER(CkKVCache), IP, I, I, F, I, P, S, P], I),
-        "ck_attn_merge": ([P, S, IP, I, I, I, I, I, P, P, P], I),
+        "ck_attn_merge": ([P, S, IP, I, I, I, I, I, I, P, P, P], I),
         "ck_decode_layer_workspace_size": ([ctypes.POINTER(CkLayerDesc), I], S),
         "ck_decode_layer": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                              ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, P], I),
@@ -188,9 +189,10 @@ def ck_rope(q, k, cos_tab, sin_tab, tab_rows, pos, m, H, KV, hd, stream=None):
 
 def kv_cache(k, v, kv_heads, head_dim, capacity=0, page_size=0, page_table=None,
              max_pages_per_seq=0, num_pages=0, dtype=CK_KV_F32, k_scale=1.0,
-             v_scale=1.0) -> CkKVCache:
+             v_scale=1.0, window=0, ring=False) -> CkKVCache:
     return CkKVCache(_ptr(k), _ptr(v), kv_heads, head_dim, capacity, page_size,
-                     _ptr(page_table), max_pages_per_seq, num_pages, dtype, k_scale, v_scale)
+                     _ptr(page_table), max_pages_per_seq, num_pages, dtype, k_scale, v_scale,
+                     window, int(ring))
 
 
 def ck_kv_append(cache: CkKVCache, k, v, pos, m, stream=None):
@@ -215,9 +217,10 @@ def ck_attn_partial(q, cache: CkKVCache, pos, m, H, scale, chunk, partials, nbyt
                                   _ptr(partials), nbytes, _stream(stream)), "ck_attn_partial")
 
 
-def ck_attn_merge(partials, nbytes, pos, m, H, KV, hd, chunk, out, out_q8=None, stream=None):
-    _check(load().ck_attn_merge(_ptr(partials), nbytes, _pos(pos), m, H, KV, hd, chunk, _ptr(out),
-                                _ptr(out_q8), _stream(stream)), "ck_attn_merge")
+def ck_attn_merge(partials, nbytes, pos, m, H, KV, hd, chunk, out, out_q8=None, stream=None,
+                  window=0):
+    _check(load().ck_attn_merge(_ptr(partials), nbytes, _pos(pos), m, H, KV, hd, chunk, window,
+                                _ptr(out), _ptr(out_q8), _stream(stream)), "ck_attn_merge")
 
 
 def layer_desc(D, H, KV, head_dim, m=1, eps=1e-6, variant=CK_VARIANT_FUSED, attn_chunk=0):

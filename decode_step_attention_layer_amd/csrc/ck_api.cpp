@@ -29,10 +29,13 @@ int cache_view(const ck_kv_cache *kv, CacheView *out) {
           kv->v_scale < INFINITY))
         return CK_EINVAL;
     if (!al(kv->k, 16) || !al(kv->v, 16) || kv->head_dim % 4) return CK_EINVAL;
-    if (kv->page_size < 0) return CK_EINVAL;
+    if (kv->page_size < 0 || kv->window < 0 || (kv->ring != 0 && kv->ring != 1)) return CK_EINVAL;
     if (kv->page_size == 0) {
         if (kv->capacity <= 0) return CK_EINVAL;
+        // a ring holds the last `capacity` tokens: the window may not reach further
+        if (kv->ring && (kv->window < 1 || kv->window > kv->capacity)) return CK_EINVAL;
     } else {
+        if (kv->ring) return CK_EINVAL;
         if (!kv->page_table || kv->max_pages_per_seq <= 0 || kv->num_pages <= 0) return CK_EINVAL;
         if (!al(kv->page_table, 4)) return CK_EINVAL;
     }
@@ -48,14 +51,21 @@ int cache_view(const ck_kv_cache *kv, CacheView *out) {
     out->dtype = kv->dtype;
     out->k_scale = kv->k_scale;
     out->v_scale = kv->v_scale;
+    out->window = kv->window;
+    out->ring = kv->ring;
     return CK_OK;
 }
 
-// Token capacity of one sequence of the cache (positions must stay below).
+// Token capacity of one sequence of the cache (positions must stay below); a
+// ring has no bound of its own.
 long long cache_tokens(const ck_kv_cache *kv) {
+    if (kv->page_size == 0 && kv->ring) return 1LL << 30;
     return kv->page_size == 0 ? (long long)kv->capacity
                               : (long long)kv->page_size * kv->max_pages_per_seq;
 }
+
+// Most tokens one sequence attends when the longest has max_len tokens.
+int attended(int max_len, int window) { return max_len - window_start(max_len, window); }
 
 int read_positions(const int32_t *pos_host, int m, long long limit, Positions *p, int *max_tokens) {
     if (!pos_host || m < 1 || m > CK_MAX_SEQS) return CK_EINVAL;
@@ -75,9 +85,9 @@ int read_positions(const int32_t *pos_host, int m, long long limit, Positions *p
 }  // namespace
 
 namespace ck {
-long long total_tokens(const Positions &p, int m) {
+long long total_tokens(const Positions &p, int m, int window) {
     long long t = 0;
-    for (int s = 0; s < m; s++) t += (long long)p.p[s] + 1;
+    for (int s = 0; s < m; s++) t += attended(p.p[s] + 1, window);
     return t;
 }
 }  // namespace ck
@@ -97,7 +107,7 @@ int resolve_positions(const PosIn &in, int m, long long limit, Positions *p, int
     if (in.host) {
         const int rc = read_positions(in.host, m, limit, p, mx);
         if (rc) return rc;
-        *total = total_tokens(*p, m);
+        *total = total_tokens(*p, m, 0);
         return CK_OK;
     }
     if (!in.dev || in.max_ctx < 1 || m < 1 || m > CK_MAX_SEQS || !al(in.dev, 4)) return CK_EINVAL;
@@ -296,7 +306,8 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(c.kv_heads, mx, total_tokens(p, m), chunk);
+    AttnPlan pl = attn_plan(c.kv_heads, attended(mx, c.window), total_tokens(p, m, c.window),
+                            chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream));
@@ -314,25 +325,28 @@ int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_ho
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(c.kv_heads, mx, total_tokens(p, m), chunk);
+    AttnPlan pl = attn_plan(c.kv_heads, attended(mx, c.window), total_tokens(p, m, c.window),
+                            chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attn_partial(q, c, p, m, H, scale, pl, partials, (hipStream_t)stream));
 }
 
 int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, int m, int H,
-                  int KV, int hd, int chunk, float *out, void *out_q8, void *stream) {
-    if (!partials || !out || H <= 0 || KV <= 0 || H % KV || chunk < 0) return CK_EINVAL;
+                  int KV, int hd, int chunk, int window, float *out, void *out_q8,
+                  void *stream) {
+    if (!partials || !out || H <= 0 || KV <= 0 || H % KV || chunk < 0 || window < 0)
+        return CK_EINVAL;
     if (!al(partials, 16) || !al(out, 16) || (out_q8 && !al(out_q8, 2))) return CK_EINVAL;
     if (!attn_shape_supported(H / KV, hd)) return CK_EUNSUPPORTED;
     Positions p;
     int mx;
     int rc = read_positions(pos_host, m, 1LL << 30, &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(KV, mx, total_tokens(p, m), chunk);
+    AttnPlan pl = attn_plan(KV, attended(mx, window), total_tokens(p, m, window), chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, hd, pl.nchunks)) return CK_ENOSPC;
-    return hip_rc(launch_attn_merge(partials, p, m, H, KV, hd, pl, out,
+    return hip_rc(launch_attn_merge(partials, p, window, m, H, KV, hd, pl, out,
                                     static_cast<uint8_t *>(out_q8), (hipStream_t)stream));
 }
 
@@ -388,8 +402,9 @@ int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const
     Positions p;
     int mx;
     long long total;
-    long long limit = cache_tokens(&kv[0]);
-    if (w[0].rope_rows < limit) limit = w[0].rope_rows;
+    long long limit = w[0].rope_rows;
+    for (int l = 0; l < layers; l++)
+        if (cache_tokens(&kv[l]) < limit) limit = cache_tokens(&kv[l]);
     rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     StepWs L = step_layout(desc, layers, mx);
@@ -417,8 +432,9 @@ int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const
     }
 
     if (!step_supported(d.D, d.H, d.KV, d.head_dim, d.m, plan.nchunks)) return CK_EUNSUPPORTED;
+    // fp32 caches without window or ring only
     for (int l = 0; l < layers; l++)
-        if (kv[l].dtype != CK_KV_F32) return CK_EUNSUPPORTED;   // fp32 caches only
+        if (kv[l].dtype != CK_KV_F32 || kv[l].window != 0 || kv[l].ring) return CK_EUNSUPPORTED;
     StepLaunch sl;
     memset(&sl, 0, sizeof(sl));
     sl.L = layers;
@@ -555,7 +571,10 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     WsLayout L = ws_layout(desc, mx);
-    const AttnPlan plan = attn_plan(d.KV, mx, total, d.attn_chunk);
+    // the attention covers each sequence's window only
+    const int amx = attended(mx, c.window);
+    const long long atot = p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window);
+    const AttnPlan plan = attn_plan(d.KV, amx, atot, d.attn_chunk);
     if (!attn_chunks_supported(plan.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, plan.nchunks))
         return CK_ENOSPC;

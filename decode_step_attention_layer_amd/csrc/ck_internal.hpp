@@ -38,7 +38,14 @@ struct CacheView {
     int kv_heads, head_dim, capacity, page_size, max_pages, num_pages;
     int dtype;                // CK_KV_*
     float k_scale, v_scale;   // fp8
+    int window;               // 0 = every token, else the last `window` positions
+    int ring;                 // contiguous ring: token t in slot t % capacity
 };
+
+// First token a sequence of L tokens attends under a window (0 = none).
+__host__ __device__ __forceinline__ int window_start(int L, int window) {
+    return (window > 0 && L > window) ? L - window : 0;
+}
 
 // Stores element idx of K (is_k) or V from an fp32 value, in the cache's type.
 __device__ __forceinline__ void cache_put(const CacheView &c, bool is_k, long long idx, float x) {
@@ -110,8 +117,10 @@ __device__ __forceinline__ float4 cache_cvt4(const CacheView &c, bool is_k,
 // Element offset of (seq, kv head, token) in the K (or V) buffer, or -1 if the
 // token's page is unmapped or out of range. Shared by the kernels.
 __device__ __forceinline__ long long cache_row(const CacheView &c, int s, int g, int t) {
-    if (c.page_size == 0)
-        return (((long long)s * c.kv_heads + g) * c.capacity + t) * (long long)c.head_dim;
+    if (c.page_size == 0) {
+        const int slot = c.ring ? t % c.capacity : t;
+        return (((long long)s * c.kv_heads + g) * c.capacity + slot) * (long long)c.head_dim;
+    }
     int page = c.table[(long long)s * c.max_pages + t / c.page_size];
     if (page < 0 || page >= c.num_pages) return -1;
     return (((long long)page * c.kv_heads + g) * c.page_size + t % c.page_size) *
@@ -171,16 +180,17 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int KV, int max_tokens, long long total_tokens, int chunk_req);
 int attn_max_chunks(int KV, int max_tokens, int chunk_req);
-long long total_tokens(const Positions &p, int m);
+// Tokens attended over all sequences (host positions), under a window.
+long long total_tokens(const Positions &p, int m, int window);
 bool attn_shape_supported(int G, int hd);
 bool attn_chunks_supported(int nchunks);
 size_t attn_partials_bytes(int m, int H, int hd, int nchunks);
 hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positions &pos, int m,
                                int H, float scale, const AttnPlan &plan, void *partials,
                                hipStream_t st);
-hipError_t launch_attn_merge(const void *partials, const Positions &pos, int m, int H, int KV,
-                             int hd, const AttnPlan &plan, float *out, uint8_t *out_q8,
-                             hipStream_t st);
+hipError_t launch_attn_merge(const void *partials, const Positions &pos, int window, int m,
+                             int H, int KV, int hd, const AttnPlan &plan, float *out,
+                             uint8_t *out_q8, hipStream_t st);
 hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
                             void *partials, hipStream_t st);

@@ -6,6 +6,10 @@
 // Paged caches are addressed through the block table of the metrale
 // "prefill_attn_a.rs" paged decode launchers; the GQA packing (one workgroup
 // serves all query heads of a KV head) follows its paged_decode_attn_*_gqa.
+// A sliding window (that page's sliding_window) restricts t to the last W
+// positions: chunks then count from the window's first token, so the grid
+// covers only attended tokens. A ring cache (the spark_model page's window
+// ring) keeps token t in slot t % capacity.
 //
 // One kernel, grid (chunk, KV head, sequence). A workgroup walks its chunk of
 // tokens in tiles of 64: the K and V tiles are staged through LDS with
@@ -80,8 +84,9 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
     while (s + 1 < a.m && item >= a.first[s + 1]) s++;
     const int cidx = item - a.first[s];
     const int L = a.pos.get(s) + 1;
-    const int t0 = cidx * a.chunk;
-    if (t0 >= L) return;                             // (never: items cover [0, L) only)
+    // chunks count from the window's first token (0 without a window)
+    const int t0 = window_start(L, a.c.window) + cidx * a.chunk;
+    if (t0 >= L) return;             // device positions: items past this sequence's chunks
     const int t1 = min(L, t0 + a.chunk);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -130,7 +135,9 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
                     }
                     if (off < 0) sm.bad = 1;
                 } else {
-                    off = (long long)(seq_base + (size_t)t * HD);
+                    // ring: slot t % capacity (t < L, so t is never negative)
+                    const int slot = a.c.ring ? t % a.c.capacity : t;
+                    off = (long long)(seq_base + (size_t)slot * HD);
                 }
             }
             if (off >= 0) {
@@ -254,6 +261,7 @@ struct MergeArgs {
     const float *pml;
     Positions pos;
     int chunk, nchunks, H, KV;
+    int window;          // 0 = none: the chunks cover the last `window` tokens
     float *out;          // [m][H][HD]
     uint8_t *out_q8;     // nullable: [m][H*HD/32] Q8_0 blocks
 };
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     const int lane = tid & 63, wave = tid >> 6;
     const int G = a.H / a.KV, g = h / G, j = h % G;
     const int L = a.pos.get(s) + 1;
-    const int nc = (L + a.chunk - 1) / a.chunk;
+    const int nc = (L - window_start(L, a.window) + a.chunk - 1) / a.chunk;
     const size_t base = ((size_t)s * a.KV + g) * a.nchunks;
 
     // Every load that does not depend on another goes out first: the (max,
@@ -484,17 +492,18 @@ hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positio
     // device positions every sequence gets plan.nchunks items and the ones
     // past its length return at once
     a.first[0] = 0;
-    for (int s = 0; s < m; s++)
-        a.first[s + 1] = a.first[s] + (pos.dev ? plan.nchunks
-                                                : (pos.p[s] + 1 + plan.chunk - 1) / plan.chunk);
+    for (int s = 0; s < m; s++) {
+        const int n = pos.p[s] + 1 - window_start(pos.p[s] + 1, c.window);
+        a.first[s + 1] = a.first[s] + (pos.dev ? plan.nchunks : (n + plan.chunk - 1) / plan.chunk);
+    }
     for (int s = m + 1; s <= kMaxSeqs; s++) a.first[s] = a.first[m];
     const bool paged = c.page_size != 0;
     return c.head_dim == 64 ? launch_g<64>(a, G, m, paged, st) : launch_g<128>(a, G, m, paged, st);
 }
 
-hipError_t launch_attn_merge(const void *partials, const Positions &pos, int m, int H, int KV,
-                             int hd, const AttnPlan &plan, float *out, uint8_t *out_q8,
-                             hipStream_t st) {
+hipError_t launch_attn_merge(const void *partials, const Positions &pos, int window, int m,
+                             int H, int KV, int hd, const AttnPlan &plan, float *out,
+                             uint8_t *out_q8, hipStream_t st) {
     const uint8_t *base = static_cast<const uint8_t *>(partials);
     MergeArgs b;
     b.po = reinterpret_cast<const float *>(base);
@@ -505,6 +514,7 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int m, 
     b.nchunks = plan.nchunks;
     b.H = H;
     b.KV = KV;
+    b.window = window;
     b.out = out;
     b.out_q8 = out_q8;
     if (hd == 64)
@@ -519,7 +529,8 @@ hipError_t launch_attention(const float *q, const CacheView &c, const Positions 
                             void *partials, hipStream_t st) {
     hipError_t e = launch_attn_partial(q, c, pos, m, H, scale, plan, partials, st);
     if (e != hipSuccess) return e;
-    return launch_attn_merge(partials, pos, m, H, c.kv_heads, c.head_dim, plan, out, out_q8, st);
+    return launch_attn_merge(partials, pos, c.window, m, H, c.kv_heads, c.head_dim, plan, out,
+                             out_q8, st);
 }
 
 }  // namespace ck

@@ -36,6 +36,7 @@ Q5_0_BYTES = 22
 T_X, T_GAMMA, T_BQ, T_BK, T_BV, T_BO, T_WQ, T_WK, T_WV, T_WO = range(10)
 T_KCACHE, T_VCACHE, T_LENS, T_PERM = 10, 11, 12, 13
 T_KCODES, T_VCODES = 14, 15
+T_KRING, T_VRING = 16, 17
 
 # Reduced-precision caches: element types (the C ABI's CK_KV_*) and the fixed
 # per-tensor scales of the synthetic fp8 caches.
@@ -210,6 +211,21 @@ def contiguous_cache(cfg: Config, layer: int, poison: float = float("nan")):
     return out[0], out[1]
 
 
+def ring_cache(cfg: Config, layer: int, slots: int, poison: float = float("nan")):
+    """K and V of a ring of `slots` tokens per (sequence, KV head):
+    [m][KV][slots][hd]. A ring past its first lap holds `slots` earlier tokens
+    in some order, so every slot is ~ N(0,1); before it (pos < slots) only
+    slots < pos were written and the rest hold `poison`."""
+    shape = (cfg.m, cfg.KV, slots, cfg.hd)
+    out = []
+    for tid in (T_KRING, T_VRING):
+        a = normal(rng(cfg.index, layer, tid), shape)
+        if cfg.pos < slots:
+            a[:, :, cfg.pos:, :] = poison
+        out.append(a)
+    return out[0], out[1]
+
+
 def paged_cache(cfg: Config, layer: int, poison: float = float("nan"), spare_pages: int = 0):
     """Paged K and V pools [P][KV][page][hd], the page table [m][max_pages]
     (int32, -1 = unmapped) and the context lengths. Sequence s owns
@@ -266,15 +282,19 @@ def rope_for(cfg: Config):
     return rope_tables(cfg.rope_rows, cfg.hd, cfg.theta)
 
 
-def algorithmic_bytes(cfg: Config, lens=None, kv_dtype: int = KV_F32) -> dict:
+def algorithmic_bytes(cfg: Config, lens=None, kv_dtype: int = KV_F32, window: int = 0) -> dict:
     """Bytes one layer step must move: quantized weight blocks + K and V of
-    every attended token (L = pos + 1 per sequence) in the cache's type."""
+    every attended token (L = pos + 1 per sequence, at most `window` of them
+    under a sliding window) in the cache's type."""
     D, HD, KD = cfg.D, cfg.H * cfg.hd, cfg.KV * cfg.hd
     w = (HD * D // QK) * Q5_0_BYTES + (KD * D // QK) * Q5_0_BYTES \
         + (KD * D // QK) * Q8_0_BYTES + (D * HD // QK) * Q5_0_BYTES
     if lens is None:
         lens = context_lengths(cfg)
-    tokens = int(np.sum(np.asarray(lens, np.int64) + 1))
+    att = np.asarray(lens, np.int64) + 1
+    if window > 0:
+        att = np.minimum(att, window)
+    tokens = int(np.sum(att))
     kv = tokens * KD * KV_ELEM_BYTES[kv_dtype] * 2
     return {"weights": w, "kv": kv, "total": w + kv}
 

@@ -33,9 +33,15 @@ class DeviceStack:
 
     def __init__(self, cfg: synth.Config, device="cuda", poison: float = float("nan"),
                  keep_host: bool = False, spare_pages: int = 0, layers: int | None = None,
-                 threads: int = 8, kv_dtype: int = synth.KV_F32):
+                 threads: int = 8, kv_dtype: int = synth.KV_F32, window: int = 0,
+                 ring: bool = False):
         self.cfg = cfg
         self.kv_dtype = kv_dtype
+        # sliding window; a ring (contiguous caches only) has `window` slots
+        assert not ring or (window > 0 and not cfg.page_size), "a ring is contiguous, window > 0"
+        self.window = window
+        self.ring = ring
+        self.capacity = window if ring else cfg.capacity
         self.k_scale = synth.FP8_K_SCALE if kv_dtype == synth.KV_FP8 else 1.0
         self.v_scale = synth.FP8_V_SCALE if kv_dtype == synth.KV_FP8 else 1.0
         self.device = torch.device(device)
@@ -55,6 +61,9 @@ class DeviceStack:
                 k, v, table, lens = synth.paged_cache(cfg, layer, poison, spare_pages)
                 assert np.array_equal(lens, self.lens)
                 c = dict(k=k, v=v, table=table)
+            elif ring:
+                k, v = synth.ring_cache(cfg, layer, window, poison)
+                c = dict(k=k, v=v)
             else:
                 k, v = synth.contiguous_cache(cfg, layer, poison)
                 c = dict(k=k, v=v)
@@ -86,7 +95,7 @@ class DeviceStack:
                 cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, 0, cfg.page_size, t["table"],
                                     cfg.max_pages_per_seq, L.cache.num_pages, **self._kvargs())
             else:
-                cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity,
+                cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, self.capacity,
                                     **self._kvargs())
             weights = ck.layer_weights(t["wq"], t["wk"], t["wv"], t["wo"], t["bq"], t["bk"],
                                        t["bv"], t["bo"], t["gamma"], self.rope[0], self.rope[1],
@@ -109,7 +118,7 @@ class DeviceStack:
             cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, 0, cfg.page_size, t["table"],
                                 cfg.max_pages_per_seq, c["k"].shape[0], **self._kvargs())
         else:
-            cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, cfg.capacity, **self._kvargs())
+            cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, self.capacity, **self._kvargs())
         weights = ck.layer_weights(t["wq"], t["wk"], t["wv"], t["wo"], t["bq"], t["bk"], t["bv"],
                                    t["bo"], t["gamma"], self.rope[0], self.rope[1], self.rope_rows)
         host = dict(w, **{"k": c["k"], "v": c["v"]}, **({"table": c["table"]} if "table" in c else {})) \
@@ -117,7 +126,8 @@ class DeviceStack:
         return DeviceLayer(t, weights, cache, host)
 
     def _kvargs(self) -> dict:
-        return dict(dtype=self.kv_dtype, k_scale=self.k_scale, v_scale=self.v_scale)
+        return dict(dtype=self.kv_dtype, k_scale=self.k_scale, v_scale=self.v_scale,
+                    window=self.window, ring=self.ring)
 
     def desc(self, variant=ck.CK_VARIANT_FUSED, attn_chunk=0) -> ck.CkLayerDesc:
         c = self.cfg

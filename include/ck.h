@@ -71,7 +71,23 @@ typedef struct ck_kv_cache {
     int32_t num_pages;
     int32_t dtype;               /* CK_KV_F32 (0, the default), CK_KV_BF16, CK_KV_FP8_E4M3 */
     float k_scale, v_scale;      /* CK_KV_FP8_E4M3: value = e4m3(code) * scale (fp32) */
+    int32_t window;              /* sliding window: 0 = attend every token; W > 0 = only
+                                    tokens t > pos - W (the last W positions) */
+    int32_t ring;                /* 1 = ring buffer (contiguous only; 1 <= window <=
+                                    capacity): token t lives in slot t % capacity */
 } ck_kv_cache;
+
+/* Sliding window and ring buffer. A window W attends, for a sequence at
+ * position pos, the tokens max(0, pos + 1 - W) .. pos (the sliding_window
+ * argument of the metrale page's paged decode attention, where 0 means the
+ * whole sequence). A ring cache is the window ring of the spark_model page's
+ * decode body: a contiguous cache of `capacity` slots per (sequence, KV head)
+ * in which the append writes token pos at slot pos % capacity, overwriting
+ * the token capacity positions back. Since the window never reaches further
+ * back than capacity tokens, a ring needs 1 <= window <= capacity (otherwise
+ * CK_EINVAL); positions are then bounded only by rope_rows. A ring or window
+ * applies to the chain and fused variants and to the attention calls; the
+ * persistent variant returns CK_EUNSUPPORTED for either. */
 
 /* Element types of the cache (the bf16 and fp8 caches of the metrale page's
  * paged_decode_attn_bf16 / paged_decode_attn_fp8, whose fp8 variant takes one
@@ -151,17 +167,19 @@ int ck_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
             void *stream);
 
 /* Step 6 — KV append: the new token's k and v ([m][KV][hd], k already
- * rotated) are written at position pos_host[s] of sequence s. */
+ * rotated) are written at position pos_host[s] of sequence s (a ring cache:
+ * slot pos_host[s] % capacity). */
 int ck_kv_append(const ck_kv_cache *kv, const float *k, const float *v,
                  const int32_t *pos_host, int m, void *stream);
 
 /* Workspace bytes ck_attn_decode_gqa needs for m sequences of at most
- * max_tokens attended tokens each, with the given split (0 = automatic). */
+ * max_tokens attended tokens each (under a window W: at most W), with the
+ * given split (0 = automatic). */
 size_t ck_attn_workspace_size(int m, int H, int KV, int hd, int max_tokens, int chunk);
 
 /* Step 7 — grouped-query decode attention: for each sequence s and query head
- * h, softmax(scale * q_h . K_g[t]) . V_g over tokens t <= pos_host[s], with
- * g = h*KV/H. q, out: [m][H][hd]. Tokens are split into chunks of `chunk`
+ * h, softmax(scale * q_h . K_g[t]) . V_g over tokens t <= pos_host[s] (under
+ * the cache's window W only t > pos_host[s] - W), with g = h*KV/H. q, out: [m][H][hd]. Tokens are split into chunks of `chunk`
  * tokens (0 = automatic); each chunk's online-softmax partial goes to the
  * workspace (at least ck_attn_workspace_size bytes, any contents) and a
  * second kernel merges them by log-sum-exp. Calls that share a workspace must
@@ -176,15 +194,19 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
  * `chunk` tokens and query head, the chunk's running max (log2 units), sum of
  * exponentials and unnormalized output into `partials` (layout: outputs
  * [m][KV][nchunks][H/KV][hd] fp32, then (max, sum) pairs, each region
- * 256-byte aligned; nchunks is fixed by (m, KV, max pos + 1, chunk)).
+ * 256-byte aligned; nchunks is fixed by (m, KV, the most tokens a sequence
+ * attends, chunk); chunk c of a sequence covers its attended tokens
+ * [c*chunk, (c+1)*chunk) counted from the window's first token).
  * ck_attn_merge combines them by log-sum-exp into out ([m][H][hd]) and, when
  * out_q8 is not NULL, also writes the Q8_0 blocks of out (the quantization
  * done before the O projection). Both validate like ck_attn_decode_gqa; the
- * merge must see the same pos_host, m, H, KV, hd and chunk as the partial. */
+ * merge must see the same pos_host, m, H, KV, hd and chunk as the partial,
+ * and as window the window of the partial's cache (0 = none). */
 int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, int m, int H,
                     float scale, int chunk, void *partials, size_t bytes, void *stream);
 int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, int m, int H,
-                  int KV, int hd, int chunk, float *out, void *out_q8, void *stream);
+                  int KV, int hd, int chunk, int window, float *out, void *out_q8,
+                  void *stream);
 
 /* Workspace bytes ck_decode_layer needs when every position is < max_ctx. */
 size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx);

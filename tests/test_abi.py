@@ -209,3 +209,85 @@ def test_devpos_validation(ck):
                                    None) == ck.CK_EINVAL
     assert L.ck_decode_step_devpos(ref(d), ws, cs, 1, FAKE, FAKE, 17, FAKE, FAKE, n,
                                    None) == ck.CK_EINVAL      # out aliases x
+
+
+def test_window_and_ring_validation(ck):
+    L = ck.load()
+    q, ws = FAKE, FAKE
+    far = (ctypes.c_int32 * 1)(1000)
+
+    def attn(c, pos=far, nws=16):
+        return L.ck_attn_decode_gqa(q, ctypes.byref(c), pos, FAKE, 1, 4, 0.1, 0, ws, nws, None)
+
+    def cache(window=0, ring=0, cap=64, page=0):
+        if page:
+            return ck.CkKVCache(FAKE, FAKE, 2, 64, 0, page, FAKE, 8, 10, 0, 1.0, 1.0, window, ring)
+        return ck.CkKVCache(FAKE, FAKE, 2, 64, cap, 0, None, 0, 0, 0, 1.0, 1.0, window, ring)
+
+    # a ring is contiguous, its window 1..capacity; windows are non-negative
+    assert attn(cache(window=8, ring=1, page=16)) == ck.CK_EINVAL
+    assert attn(cache(window=0, ring=1)) == ck.CK_EINVAL
+    assert attn(cache(window=65, ring=1)) == ck.CK_EINVAL
+    assert attn(cache(window=-1)) == ck.CK_EINVAL
+    assert attn(cache(window=8, ring=2)) == ck.CK_EINVAL
+    # a linear cache bounds positions by its capacity, a ring does not: the
+    # ring call gets past validation and stops at the workspace size
+    assert attn(cache(window=32)) == ck.CK_EINVAL
+    assert attn(cache(window=32, ring=1)) == ck.CK_ENOSPC
+    assert attn(cache(window=64, ring=1)) == ck.CK_ENOSPC
+    # the workspace for a windowed attention is sized by the window
+    need = ck.ck_attn_workspace_size(1, 4, 2, 64, 32, 0)
+    assert 0 < need <= ck.ck_attn_workspace_size(1, 4, 2, 64, 1001, 0)
+    c = cache(window=32, ring=1)
+    assert L.ck_attn_partial(q, ctypes.byref(c), far, 1, 4, 0.1, 0, ws, 16, None) == ck.CK_ENOSPC
+    assert L.ck_attn_merge(FAKE, 1 << 20, far, 1, 4, 2, 64, 0, -1, FAKE, None, None) == ck.CK_EINVAL
+    assert L.ck_attn_merge(FAKE, 16, far, 1, 4, 2, 64, 0, 32, FAKE, None, None) == ck.CK_ENOSPC
+    # the persistent step takes neither windows nor rings
+    d = ck.layer_desc(256, 4, 2, 64, 1, variant=ck.CK_VARIANT_PERSISTENT, attn_chunk=64)
+    n = ck.ck_decode_step_workspace_size(d, 1, 2000)
+    wts = (ck.CkLayerWeights * 1)(
+        ck.CkLayerWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, 4096))
+    for cc in (cache(window=32), cache(window=32, ring=1)):
+        caches = (ck.CkKVCache * 1)(cc)
+        pos = (ctypes.c_int32 * 1)(20)
+        assert L.ck_decode_step(ctypes.byref(d), wts, caches, 1, FAKE, pos, FAKE + 4096, FAKE,
+                                n, None) == ck.CK_EUNSUPPORTED
+
+
+_LAYOUT_C = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "ck.h"
+#define F(T, f) printf("%s.%s %zu\n", #T, #f, offsetof(T, f));
+int main(void) {
+    printf("ck_kv_cache %zu\nck_layer_desc %zu\nck_layer_weights %zu\n", sizeof(ck_kv_cache),
+           sizeof(ck_layer_desc), sizeof(ck_layer_weights));
+    %FIELDS%
+    return 0;
+}
+"""
+
+
+def test_struct_layout_matches_header(ck, tmp_path):
+    """The ctypes mirrors of the descriptor structs have the C header's size
+    and field offsets (compiled with the host C compiler)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc") or shutil.which("cc")
+    if gcc is None:
+        pytest.skip("no host C compiler")
+    structs = {"ck_kv_cache": ck.CkKVCache, "ck_layer_desc": ck.CkLayerDesc,
+               "ck_layer_weights": ck.CkLayerWeights}
+    lines = [f"F({n}, {f})" for n, T in structs.items() for f, _ in T._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(_LAYOUT_C.replace("%FIELDS%", "\n    ".join(lines)))
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-std=c11", "-I", os.path.dirname(HEADER), "-o", str(exe), str(src)],
+                   check=True)
+    out = dict(l.rsplit(" ", 1) for l in subprocess.run(
+        [str(exe)], check=True, capture_output=True, text=True).stdout.splitlines())
+    for n, T in structs.items():
+        assert int(out[n]) == ctypes.sizeof(T), n
+        for f, _ in T._fields_:
+            assert int(out[f"{n}.{f}"]) == getattr(T, f).offset, f"{n}.{f}"
