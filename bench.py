@@ -10,7 +10,8 @@ steps are timed with HIP events on that stream. Replicas of the whole stack
 are rotated when one step's bytes would fit the 256 MB last-level cache.
 
 Prints one JSON line: value = achieved GB/s over the algorithmic bytes
-(quantized weight blocks + fp32 K and V of every attended token) of the step.
+(quantized weight blocks + K and V of every attended token, in the cache's
+element type; under a sliding window only the last W tokens) of the step.
 """
 from __future__ import annotations
 
@@ -46,6 +47,12 @@ def parse():
     ap.add_argument("--variant", default="fused", choices=["fused", "chain", "persistent"])
     ap.add_argument("--kv", default="f32", choices=["f32", "bf16", "fp8"],
                     help="KV-cache element type (fp8: E4M3 with one scale per tensor)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: attend only the last W positions (0 = all)")
+    ap.add_argument("--ring", action="store_true",
+                    help="keep the cache as a ring of `window` slots (contiguous workloads)")
+    ap.add_argument("--attn-chunk", type=int, default=0,
+                    help="tokens per attention split (0 = sized to fill the GPU)")
     ap.add_argument("--eager", action="store_true", help="launch from Python, no graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU-baseline sample")
@@ -54,7 +61,34 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.window < 0 or (args.ring and args.window < 1):
+        ap.error("--ring needs --window W with W >= 1")
+    if args.ring and args.config == "c5":
+        ap.error("a ring cache is contiguous; c5 is paged")
+    if args.variant == "persistent" and args.window:
+        ap.error("the persistent variant takes no window or ring")
+    return args
+
+
+def workload_key(args) -> str:
+    """Short name of the timed workload: the configuration, plus the cache's
+    element type, window and ring when they differ from the defaults."""
+    key = args.config if args.kv == "f32" else f"{args.config}-{args.kv}"
+    if args.window:
+        key += f"-w{args.window}" + ("-ring" if args.ring else "")
+    return key
+
+
+def workload_text(args) -> str:
+    text = f"{args.config}: {DESCRIBE[args.config]}"
+    if args.kv != "f32":
+        text += f", {args.kv} KV cache"
+    if args.window:
+        text += f", sliding window of {args.window} tokens"
+        if args.ring:
+            text += f" in a ring of {args.window} slots"
+    return text
 
 
 def copy_calibration():
@@ -100,15 +134,16 @@ def main():
     persistent = variant == ck.CK_VARIANT_PERSISTENT
     t0 = time.time()
     kv_dtype = {"f32": synth.KV_F32, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}[args.kv]
-    stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu, kv_dtype=kv_dtype)
+    stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu, kv_dtype=kv_dtype,
+                        window=args.window, ring=args.ring)
     log(f"[bench] {args.config}: {stack.nlayers} layers on device in {time.time() - t0:.1f}s")
-    nbytes = synth.algorithmic_bytes(cfg, stack.lens, kv_dtype)
+    nbytes = synth.algorithmic_bytes(cfg, stack.lens, kv_dtype, args.window)
     step_bytes = nbytes["total"] * stack.nlayers
     replicas = 1
     if step_bytes < 3 * MALL_BYTES:
         replicas = min(8, math.ceil(3 * MALL_BYTES / step_bytes))
     stacks = [stack] + [stack.clone() for _ in range(replicas - 1)]
-    desc = stack.desc(variant)
+    desc = stack.desc(variant, args.attn_chunk)
     stream = torch.cuda.current_stream()
     if persistent:
         # every layer of the step in one persistent kernel (ck_decode_step)
@@ -177,7 +212,7 @@ def main():
                 "frac": round(value / PEAK_GBS, 4), "traffic": None, "kernel": "k_step",
                 "us_per_launch": round(ms_step * 1e3, 3), "bytes_per_launch": step_bytes}
     else:
-        roof = roofline(args, stack, desc, wss[0], nbytes)
+        roof = roofline(args, stacks, desc, wss[0], nbytes)
     cpu = None if args.no_cpu else cpu_baseline(args, stack, nbytes)
 
     line = {
@@ -194,10 +229,12 @@ def main():
         "dtype": "int8-dot/f32",
         "data": "synthetic (seeded; quantized N(0,0.02) weights, N(0,1) activations and cache)",
         "config": {
-            "workload": f"{args.config}: {DESCRIBE[args.config]}" + (
-                "" if args.kv == "f32" else f", {args.kv} KV cache"),
+            "workload": workload_text(args),
             "kv_cache": args.kv,
+            "window": args.window,
+            "ring": args.ring,
             "variant": args.variant,
+            "attn_chunk": args.attn_chunk,
             "launch": "eager" if args.eager else "hip-graph",
             "layers": stack.nlayers,
             "tokens_per_step": cfg.m,
@@ -228,19 +265,27 @@ def _time_launches(fn, reps):
     return a.elapsed_time(b) * 1e3 / reps     # us per launch
 
 
-def roofline(args, stack, desc, ws, nbytes):
+def roofline(args, stacks, desc, ws, nbytes):
     """Per-launch timing, with HIP events on the launch stream, of the layer's
-    large kernels through their C-ABI entry points on layer 0's data, in the
-    launch configuration the layer uses: the split-K attention pass
-    (ck_attn_partial, one kernel: k_attn) and the O-projection GEMV
-    (ck_gemv_q5_0_q8_0, one kernel: k_gemv). The one that takes longer is
-    reported, against the algorithmic bytes it must read."""
+    large kernels through their C-ABI entry points, in the launch
+    configuration the layer uses: the split-K attention pass (ck_attn_partial,
+    one kernel: k_attn) and the O-projection GEMV (ck_gemv_q5_0_q8_0, one
+    kernel: k_gemv). Successive launches cycle over every layer of every
+    replica, as the decode steps do, so that a launch does not find its cache
+    or weights left in the last-level cache by the one before. The kernel
+    that takes longer is reported, against the algorithmic bytes it reads."""
     import torch
 
     from decode_step_attention_layer_amd import ck, synth
 
+    stack = stacks[0]
     cfg = stack.cfg
-    L = stack.layers[0]
+    units = [L for s in stacks for L in s.layers]
+    turn = [0, 0]
+
+    def nxt(k):
+        turn[k] += 1
+        return units[turn[k] % len(units)]
     m, D, H, KV, hd = cfg.m, cfg.D, cfg.H, cfg.KV, cfg.hd
     off = lambda n: ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, n)
     base = ws.data_ptr()
@@ -251,9 +296,12 @@ def roofline(args, stack, desc, ws, nbytes):
     scale = 1.0 / math.sqrt(hd)
 
     attn_us = _time_launches(lambda: ck.ck_attn_partial(
-        q, L.cache, stack.pos, m, H, scale, desc.attn_chunk, part, nws), args.kernel_reps)
-    wo_us = _time_launches(lambda: ck.ck_gemv_q5_0_q8_0(
-        L.tensors["wo"], aq, L.tensors["bo"], stack.x0, out, D, H * hd, m), args.kernel_reps)
+        q, nxt(0).cache, stack.pos, m, H, scale, desc.attn_chunk, part, nws), args.kernel_reps)
+
+    def o_gemv():
+        L = nxt(1)
+        ck.ck_gemv_q5_0_q8_0(L.tensors["wo"], aq, L.tensors["bo"], stack.x0, out, D, H * hd, m)
+    wo_us = _time_launches(o_gemv, args.kernel_reps)
     kv_bytes = nbytes["kv"]
     wo_bytes = D * (H * hd // 32) * synth.Q5_0_BYTES
     att_gbs = kv_bytes / (attn_us * 1e-6) / 1e9
@@ -266,8 +314,7 @@ def roofline(args, stack, desc, ws, nbytes):
         name, gbs, us, b = "k_gemv", wo_gbs, wo_us, wo_bytes
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_GBS, 4),
-            "traffic": recorded_traffic(name, args.config if args.kv == "f32"
-                                        else f"{args.config}-{args.kv}"),
+            "traffic": recorded_traffic(name, workload_key(args)),
             "traffic_unit": "bytes per launch",
             "kernel": name,
             "us_per_launch": round(us, 3), "bytes_per_launch": b,
@@ -322,13 +369,14 @@ def cpu_baseline(args, stack, nbytes):
     while t_spent < args.cpu_seconds:
         L = stack.layers[li % stack.nlayers]
         h = L.host
-        kvd = dict(dtype=stack.kv_dtype, k_scale=stack.k_scale, v_scale=stack.v_scale)
+        kvd = dict(dtype=stack.kv_dtype, k_scale=stack.k_scale, v_scale=stack.v_scale,
+                   window=stack.window, ring=stack.ring)
         if cfg.page_size:
             c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, page_size=cfg.page_size,
                              page_table=h["table"], max_pages_per_seq=cfg.max_pages_per_seq,
                              num_pages=h["k"].shape[0], **kvd)
         else:
-            c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, capacity=cfg.capacity, **kvd)
+            c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, capacity=stack.capacity, **kvd)
         w = dict(h, rope_cos=cos, rope_sin=sin)
         t = time.perf_counter()
         oracle.decode_layer(dims, w, c, x, x, stack.pos)
@@ -338,7 +386,7 @@ def cpu_baseline(args, stack, nbytes):
     gbs = nbytes["total"] * done / t_spent / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "us_per_layer": round(t_spent * 1e6 / done, 1),
-            "sample": f"{done} whole-layer calls of the {args.config} workload "
+            "sample": f"{done} whole-layer calls of the {workload_key(args)} workload "
                       f"(layers cycled, first-layer input), {t_spent:.1f} s single-threaded"}
 
 

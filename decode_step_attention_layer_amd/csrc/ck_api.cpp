@@ -142,7 +142,7 @@ WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
     w.v = o; o = up256(o + sizeof(float) * m * KD);
     w.attn = o; o = up256(o + sizeof(float) * m * HD);
     w.aq = o; o = up256(o + m * (HD / CK_QK) * CK_Q8_0_BYTES);
-    const int maxc = attn_max_chunks(d->KV, max_ctx, d->attn_chunk);
+    const int maxc = attn_max_chunks(d->KV, d->H / d->KV, max_ctx, d->attn_chunk);
     w.part = o; o = up256(o + attn_partials_bytes(d->m, d->H, d->head_dim, maxc));
     w.total = o;
     return w;
@@ -200,7 +200,7 @@ StepWs step_layout(const ck_layer_desc *d, int layers, int max_ctx) {
     memset(&w, 0, sizeof(w));
     size_t o = 0;
     w.xbuf = o; o = up256(o + sizeof(float) * 2 * m * D);
-    w.maxc = attn_max_chunks(d->KV, max_ctx, d->attn_chunk);
+    w.maxc = attn_max_chunks(d->KV, d->H / d->KV, max_ctx, d->attn_chunk);
     if (d->variant == CK_VARIANT_PERSISTENT) {
         // intermediates (offsets independent of the layer count and the
         // context), then the counters (the status word's offset does not
@@ -289,8 +289,8 @@ int ck_kv_append(const ck_kv_cache *kv, const float *k, const float *v, const in
 }
 
 size_t ck_attn_workspace_size(int m, int H, int KV, int hd, int max_tokens, int chunk) {
-    if (m < 1 || H <= 0 || KV <= 0 || hd <= 0 || max_tokens < 1 || chunk < 0) return 0;
-    return attn_partials_bytes(m, H, hd, attn_max_chunks(KV, max_tokens, chunk));
+    if (m < 1 || H <= 0 || KV <= 0 || H % KV || hd <= 0 || max_tokens < 1 || chunk < 0) return 0;
+    return attn_partials_bytes(m, H, hd, attn_max_chunks(KV, H / KV, max_tokens, chunk));
 }
 
 int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, float *out,
@@ -306,8 +306,8 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(c.kv_heads, attended(mx, c.window), total_tokens(p, m, c.window),
-                            chunk);
+    AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, attended(mx, c.window),
+                            total_tokens(p, m, c.window), chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream));
@@ -325,8 +325,8 @@ int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_ho
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(c.kv_heads, attended(mx, c.window), total_tokens(p, m, c.window),
-                            chunk);
+    AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, attended(mx, c.window),
+                            total_tokens(p, m, c.window), chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attn_partial(q, c, p, m, H, scale, pl, partials, (hipStream_t)stream));
@@ -343,7 +343,7 @@ int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, i
     int mx;
     int rc = read_positions(pos_host, m, 1LL << 30, &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(KV, attended(mx, window), total_tokens(p, m, window), chunk);
+    AttnPlan pl = attn_plan(KV, H / KV, attended(mx, window), total_tokens(p, m, window), chunk);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, hd, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attn_merge(partials, p, window, m, H, KV, hd, pl, out,
@@ -408,7 +408,7 @@ int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const
     rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     StepWs L = step_layout(desc, layers, mx);
-    const AttnPlan plan = attn_plan(d.KV, mx, total, d.attn_chunk);
+    const AttnPlan plan = attn_plan(d.KV, d.H / d.KV, mx, total, d.attn_chunk);
     if (ws_bytes < L.total) return CK_ENOSPC;
     hipStream_t st = (hipStream_t)stream;
     uint8_t *base = static_cast<uint8_t *>(ws);
@@ -574,7 +574,7 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     // the attention covers each sequence's window only
     const int amx = attended(mx, c.window);
     const long long atot = p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window);
-    const AttnPlan plan = attn_plan(d.KV, amx, atot, d.attn_chunk);
+    const AttnPlan plan = attn_plan(d.KV, d.H / d.KV, amx, atot, d.attn_chunk);
     if (!attn_chunks_supported(plan.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, plan.nchunks))
         return CK_ENOSPC;

@@ -178,8 +178,11 @@ struct AttnPlan {
     int chunk;
     int nchunks;
 };
-AttnPlan attn_plan(int KV, int max_tokens, long long total_tokens, int chunk_req);
-int attn_max_chunks(int KV, int max_tokens, int chunk_req);
+// Chunks are whole steps of the attention kernel (attn_step tokens, which
+// depends on the query group size G).
+int attn_step(int G);
+AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req);
+int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req);
 // Tokens attended over all sequences (host positions), under a window.
 long long total_tokens(const Positions &p, int m, int window);
 bool attn_shape_supported(int G, int hd);

@@ -33,7 +33,6 @@ namespace ck {
 
 namespace {
 
-constexpr int kTile = 64;   // tokens per tile
 constexpr int kMaxG = 8;
 constexpr int kMaxChunks = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -43,7 +42,7 @@ struct AttnArgs {
     CacheView c;
     Positions pos;
     float scale;
-    int chunk;            // tokens per chunk, multiple of kTile
+    int chunk;            // tokens per chunk, a multiple of the kernel's step
     int nchunks;
     int H;
     float *po;            // [m][KV][nchunks][G][HD]  unnormalized outputs
@@ -53,32 +52,153 @@ struct AttnArgs {
 };
 
 constexpr int kPagesLds = 512;   // page ids of a chunk staged in LDS
+// Workgroup shape: 4 waves; per step a wave loads 4 rows per round, 4 rounds
+// (a 64-token step), or 3 rounds (48 tokens) for large query groups, whose
+// per-lane accumulators leave fewer registers for loads. Two workgroups fit
+// a compute unit either way. The attention plan sizes chunks in whole steps.
+template <int G>
+struct AttnShape {
+    static constexpr int waves = 4;
+    static constexpr int rounds = G > 4 ? 3 : 4;
+    static constexpr int sub = rounds;              // rows per online-softmax batch
+    static constexpr int threads = waves * 64;
+    static constexpr int step = waves * 4 * rounds;
+};
 
-template <int HD>
+// How one wave holds K/V rows: a row is read by 16 lanes, F = HD/16 elements
+// each, so one load round covers 4 rows. fp32 rows of 128 are read as two
+// 16-byte pieces per lane (columns 4i.. and 64+4i..), so that one load
+// instruction covers 256 contiguous bytes of each of its rows; otherwise a
+// lane's F elements are contiguous (columns F*i..). WORDS: raw words per lane
+// per row.
+template <int DT, int HD>
+struct RowGeo {
+    static constexpr int EB = DT == CK_KV_F32 ? 4 : (DT == CK_KV_BF16 ? 2 : 1);
+    static constexpr int LPR = 16;
+    static constexpr int F = HD / LPR;
+    static constexpr int RPR = kWave / LPR;            // rows per load round
+    static constexpr int WORDS = F * EB / 4;
+    static constexpr bool SPLIT = DT == CK_KV_F32 && F == 8;
+};
+
+
+// One lane's slice of a K or V row.
+template <int DT, int HD>
+struct Slice {
+    typedef RowGeo<DT, HD> Geo;
+    static constexpr int F = Geo::F;
+    static constexpr int EB = Geo::EB;
+    static constexpr int WORDS = Geo::WORDS;
+    uint32_t w[WORDS];
+
+    __device__ static __forceinline__ int col(int li, int e) {
+        if constexpr (Geo::SPLIT) return e < 4 ? 4 * li + e : 64 + 4 * li + (e - 4);
+        else return F * li + e;
+    }
+    __device__ __forceinline__ void load(const void *base, long long off, int li) {
+        if constexpr (Geo::SPLIT) {
+            const float *p = static_cast<const float *>(base) + off + 4 * li;
+            const uint4 a = *reinterpret_cast<const uint4 *>(p);
+            const uint4 b = *reinterpret_cast<const uint4 *>(p + 64);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else {
+            const uint8_t *p = static_cast<const uint8_t *>(base) + (off + (long long)F * li) * EB;
+            if constexpr (WORDS == 4) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(p);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            } else if constexpr (WORDS == 2) {
+                const uint2 a = *reinterpret_cast<const uint2 *>(p);
+                w[0] = a.x; w[1] = a.y;
+            } else {
+                static_assert(WORDS == 1, "slice size");
+                w[0] = *reinterpret_cast<const uint32_t *>(p);
+            }
+        }
+    }
+    // fp32 values (fp8: code value times the tensor's scale)
+    __device__ __forceinline__ void to_f32(float (&f)[F], float scale) const {
+        if constexpr (DT == CK_KV_F32) {
+#pragma unroll
+            for (int e = 0; e < F; e++) f[e] = __uint_as_float(w[e]);
+        } else if constexpr (DT == CK_KV_BF16) {
+#pragma unroll
+            for (int i = 0; i < WORDS; i++) {
+                f[2 * i] = __uint_as_float(w[i] << 16);
+                f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        } else {
+            // v_cvt_pk_f32_fp8 decodes OCP E4M3 on gfx950 (checked against the
+            // format's definition over all 256 codes, NaN included)
+#pragma unroll
+            for (int i = 0; i < WORDS; i++) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+                f[4 * i] = lo[0] * scale;
+                f[4 * i + 1] = lo[1] * scale;
+                f[4 * i + 2] = hi[0] * scale;
+                f[4 * i + 3] = hi[1] * scale;
+            }
+        }
+    }
+};
+
+template <int HD, int G>
 struct Smem {
-    static constexpr int stride = HD + 4;  // padded row: conflict-free b128 reads
-    float kv[2 * kTile * stride];           // K tile, then V tile; reused by reductions
-    float q[kMaxG * HD];
-    float p[kTile * kMaxG];
-    float alpha[kMaxG];
+    float ro[AttnShape<G>::waves][G][HD];   // per-wave partial outputs
+    float rm[AttnShape<G>::waves][G];       // per-wave running max (log2 units)
+    float rl[AttnShape<G>::waves][G];       // per-wave sum of exponentials
     int pages[kPagesLds];                   // paged caches: the chunk's page ids
     int bad;
 };
 
-template <int HD, int G, bool PAGED, int DT>
-__global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
-    static_assert(HD % 64 == 0 && G >= 1 && G <= kMaxG, "shape");
-    constexpr int NT = G > 4 ? 512 : 256;            // threads
-    constexpr int C4 = HD / 4;                       // float4 columns per row
-    constexpr int NLD = kTile * C4 / NT;             // float4 loads per thread per tile (K or V)
-    constexpr int ROWS_PER_LD = NT / C4;             // rows covered by one load round
-    constexpr int NTG = NT / C4;                     // token groups in the P.V phase
-    constexpr int TPG = kTile / NTG;                 // tokens per group per tile
-    constexpr int S = Smem<HD>::stride;
-    __shared__ Smem<HD> sm;
+// Combines the online-softmax state (m, l, o) of lane l with that of lane
+// l ^ SH (log-sum-exp rescaling); both lanes end with the same state.
+template <int G, int F, int SH>
+__device__ __forceinline__ void merge_lanes(float (&m)[G], float (&l)[G], float (&o)[G][F]) {
+#pragma unroll
+    for (int j = 0; j < G; j++) {
+        const float mo = SH == 16 ? swz_xor16_f(m[j]) : __shfl_xor(m[j], SH);
+        const float lo = SH == 16 ? swz_xor16_f(l[j]) : __shfl_xor(l[j], SH);
+        const float M = fmaxf(m[j], mo);
+        const float Mr = M == -INFINITY ? 0.0f : M;
+        const float wa = exp2f(m[j] - Mr), wb = exp2f(mo - Mr);
+        l[j] = l[j] * wa + lo * wb;
+#pragma unroll
+        for (int e = 0; e < F; e++) {
+            const float oo = SH == 16 ? swz_xor16_f(o[j][e]) : __shfl_xor(o[j][e], SH);
+            o[j][e] = o[j][e] * wa + oo * wb;
+        }
+        m[j] = M;
+    }
+}
 
-    // grid: (work item, KV head); the items are the chunks of every sequence
-    // back to back, so a batch of unequal lengths launches no idle workgroups
+// Grid: (work item, KV head); the items are the chunks of every sequence back
+// to back, so a batch of unequal lengths launches no idle workgroups.
+//
+// Each K/V row is held by a group of LPR lanes (RowGeo), so a wave covers
+// 64/LPR rows per load round and keeps its rows in registers: no LDS staging
+// and no barrier inside the token loop. Scores: per lane the partial dot
+// products of its slice with every query head of the group (q slice in
+// registers), summed over the row group with DPP. Every row group keeps its
+// own online softmax (running max, sum, unnormalized output of its slice) over
+// the rows it sees; at the end the row groups of a wave and then the waves
+// are combined by log-sum-exp.
+template <int HD, int G, bool PAGED, int DT>
+__global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
+    static_assert(HD % 64 == 0 && G >= 1 && G <= kMaxG, "shape");
+    typedef Slice<DT, HD> SL;
+    typedef RowGeo<DT, HD> GEO;
+    constexpr int F = SL::F;
+    constexpr int LPR = GEO::LPR;
+    constexpr int RPR = GEO::RPR;
+    constexpr int NW = AttnShape<G>::waves;
+    constexpr int NT = AttnShape<G>::threads;
+    constexpr int NR = AttnShape<G>::rounds;
+    constexpr int WROWS = NR * RPR;                  // rows per wave per step
+    constexpr int STEP = WROWS * NW;                 // tokens per workgroup step
+    __shared__ Smem<HD, G> sm;
+
     const int item = blockIdx.x, g = blockIdx.y;
     int s = 0;
     while (s + 1 < a.m && item >= a.first[s + 1]) s++;
@@ -91,13 +211,11 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = a.H, KV = a.c.kv_heads;
-    const float *qg = a.q + ((size_t)s * H + (size_t)g * G) * HD;
+    const int li = lane & (LPR - 1), rg = lane / LPR;
+    const int KV = a.c.kv_heads;
 
-    float *sk = sm.kv;
-    float *sv = sm.kv + kTile * S;
     if (tid == 0) sm.bad = 0;
-    // paged: the chunk's page ids in one batch of loads, so that a tile's K/V
+    // paged: the chunk's page ids in one batch of loads, so that row
     // addresses do not wait on table reads (chunks with more pages than the
     // LDS slots read the table per row)
     int pg0 = 0;
@@ -110,149 +228,187 @@ __global__ __launch_bounds__(G > 4 ? 512 : 256) void k_attn(AttnArgs a) {
         if (pages_in_lds)
             for (int i = tid; i < npg; i += NT)
                 sm.pages[i] = a.c.table[(long long)s * a.c.max_pages + pg0 + i];
-        __syncthreads();
+    }
+    __syncthreads();
+
+    const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
+    bool bad = false;
+    // element offset of token t's row (t < t1); an unmapped page reads page 0
+    // of the pool and marks the chunk bad
+    auto row_off = [&](int t) -> long long {
+        if constexpr (PAGED) {
+            long long off = -1;
+            if (pages_in_lds) {
+                const int ps = a.c.page_size;
+                const int page = sm.pages[t / ps - pg0];
+                if (page >= 0 && page < a.c.num_pages)
+                    off = (((long long)page * KV + g) * ps + t % ps) * (long long)HD;
+            } else {
+                off = cache_row(a.c, s, g, t);
+            }
+            if (off < 0) bad = true;      // unmapped page: the sum becomes NaN
+            return off < 0 ? 0 : off;
+        } else {
+            // ring: slot t % capacity (t < L, so t is never negative)
+            const int slot = a.c.ring ? t % a.c.capacity : t;
+            return (long long)(seq_base + (size_t)slot * HD);
+        }
+    };
+    // Rows past the chunk re-read its last row (their scores are masked), so
+    // that every load is issued unconditionally: no branch around the loads
+    // and no wait on the loads still in flight.
+    auto fetch = [&](SL (&k)[NR], SL (&v)[NR], int st) {
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            const long long off = row_off(min(st + wave * WROWS + r * RPR + rg, t1 - 1));
+            k[r].load(a.c.k, off, li);
+            v[r].load(a.c.v, off, li);
+        }
+    };
+
+    SL ka[NR], va[NR];
+    fetch(ka, va, t0);                               // first rows in flight before q
+
+    // the q slice of every head of the group, pre-scaled so that scores are
+    // in log2 units
+    float qr[G][F];
+    {
+        const float qs = a.scale * kLog2e;
+        const float *qg = a.q + ((size_t)s * a.H + (size_t)g * G) * HD;
+#pragma unroll
+        for (int j = 0; j < G; j++) {
+#pragma unroll
+            for (int e = 0; e < F; e += 4) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(qg + j * HD + SL::col(li, e));
+                qr[j][e] = v4.x * qs;
+                qr[j][e + 1] = v4.y * qs;
+                qr[j][e + 2] = v4.z * qs;
+                qr[j][e + 3] = v4.w * qs;
+            }
+        }
     }
 
-    // loader geometry: this thread loads column ld_col of rows ld_row + i*ROWS_PER_LD
-    const int ld_col = tid % C4, ld_row = tid / C4;
-    const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
-    typedef typename CacheRaw4<DT>::type Raw;
-    Raw kreg[NLD], vreg[NLD];   // raw elements (fp32, bf16 or fp8), converted at the LDS store
-    auto fetch = [&](int st) {
+    float m[G], l[G], o[G][F];
 #pragma unroll
-        for (int i = 0; i < NLD; i++) {
-            const int t = st + ld_row + i * ROWS_PER_LD;
-            long long off = -1;
-            if (t < t1) {
-                if constexpr (PAGED) {
-                    if (pages_in_lds) {
-                        const int ps = a.c.page_size;
-                        const int page = sm.pages[t / ps - pg0];
-                        if (page >= 0 && page < a.c.num_pages)
-                            off = (((long long)page * KV + g) * ps + t % ps) * (long long)HD;
-                    } else {
-                        off = cache_row(a.c, s, g, t);
-                    }
-                    if (off < 0) sm.bad = 1;
-                } else {
-                    // ring: slot t % capacity (t < L, so t is never negative)
-                    const int slot = a.c.ring ? t % a.c.capacity : t;
-                    off = (long long)(seq_base + (size_t)slot * HD);
+    for (int j = 0; j < G; j++) {
+        m[j] = -INFINITY;
+        l[j] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < F; e++) o[j][e] = 0.0f;
+    }
+    const float ksc = a.c.k_scale, vsc = a.c.v_scale;
+
+    // The online softmax advances over the step's rows in batches of SUB
+    // rows (scores, running max and sum, then P.V), which bounds the score
+    // registers whatever the rows per step.
+    constexpr int SUB = AttnShape<G>::sub;
+    auto compute = [&](const SL (&k)[NR], const SL (&v)[NR], int st) {
+#pragma unroll
+        for (int r0 = 0; r0 < NR; r0 += SUB) {
+            float sc[SUB][G];
+            bool ok[SUB];                            // row inside the chunk
+#pragma unroll
+            for (int r = 0; r < SUB; r++) {
+                ok[r] = st + wave * WROWS + (r0 + r) * RPR + rg < t1;
+                float kf[F];
+                k[r0 + r].to_f32(kf, ksc);
+#pragma unroll
+                for (int j = 0; j < G; j++) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < F; e++) acc = fmaf(qr[j][e], kf[e], acc);
+                    sc[r][j] = ok[r] ? group_sum<LPR>(acc) : -INFINITY;
                 }
             }
-            if (off >= 0) {
-                kreg[i] = cache_raw4<DT>(a.c, true, off + 4 * ld_col);
-                vreg[i] = cache_raw4<DT>(a.c, false, off + 4 * ld_col);
-            } else {
-                kreg[i] = vreg[i] = cache_raw4_zero<DT>();
+            float p[SUB][G];
+#pragma unroll
+            for (int j = 0; j < G; j++) {
+                float mx = sc[0][j];
+#pragma unroll
+                for (int r = 1; r < SUB; r++) mx = fmaxf(mx, sc[r][j]);
+                const float mn = fmaxf(m[j], mx);
+                const float mr = mn == -INFINITY ? 0.0f : mn;
+                const float alpha = exp2f(m[j] - mr);
+                float ps = 0.0f;
+#pragma unroll
+                for (int r = 0; r < SUB; r++) {
+                    p[r][j] = exp2f(sc[r][j] - mr);
+                    ps += p[r][j];
+                }
+                l[j] = l[j] * alpha + ps;
+                m[j] = mn;
+#pragma unroll
+                for (int e = 0; e < F; e++) o[j][e] *= alpha;
+            }
+#pragma unroll
+            for (int r = 0; r < SUB; r++) {
+                float vf[F];
+                v[r0 + r].to_f32(vf, vsc);
+                // a row past the chunk (a re-read of its last row) adds
+                // nothing, also where that row holds an infinity
+#pragma unroll
+                for (int e = 0; e < F; e++) vf[e] = ok[r] ? vf[e] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < G; j++) {
+#pragma unroll
+                    for (int e = 0; e < F; e++) o[j][e] = fmaf(p[r][j], vf[e], o[j][e]);
+                }
             }
         }
     };
 
-    float m_run = -INFINITY, l_lane = 0.0f;          // this wave's head (wave < G)
-    const int pv_col = tid % C4, pv_tg = tid / C4;
-    float4 o[G];
-#pragma unroll
-    for (int j = 0; j < G; j++) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // One register set per step: a step's loads are all issued, then waited
+    // for and computed on. (A second set for the next step's loads does not
+    // stay in flight across the loop: the compiler waits for every load at
+    // the loop head.)
+    for (int st = t0;;) {
+        compute(ka, va, st);
+        st += STEP;
+        if (st >= t1) break;
+        fetch(ka, va, st);
+    }
 
-    // the first tile's K/V loads, then q's, in flight together
-    fetch(t0);
-    // q of the group into LDS, pre-scaled so that scores are in log2 units
-    const float qs = a.scale * kLog2e;
-    for (int i = tid; i < G * HD; i += NT) sm.q[i] = qg[i] * qs;
-    for (int st = t0; st < t1; st += kTile) {
-        __syncthreads();                             // previous tile fully consumed
-#pragma unroll
-        for (int i = 0; i < NLD; i++) {
-            const int r = ld_row + i * ROWS_PER_LD;
-            *reinterpret_cast<float4 *>(&sk[r * S + 4 * ld_col]) = cache_cvt4<DT>(a.c, true, kreg[i]);
-            *reinterpret_cast<float4 *>(&sv[r * S + 4 * ld_col]) = cache_cvt4<DT>(a.c, false, vreg[i]);
-        }
-        __syncthreads();
-        if (st + kTile < t1) fetch(st + kTile);      // next tile's loads in flight
-
-        // ---- scores: wave j = head j, lane = token
-        if (wave < G) {
-            const float *krow = &sk[lane * S];
-            const float *qrow = &sm.q[wave * HD];
-            float sc0 = 0.0f, sc1 = 0.0f;
-#pragma unroll 8
-            for (int d = 0; d < HD; d += 8) {
-                const float4 k0 = *reinterpret_cast<const float4 *>(krow + d);
-                const float4 k1 = *reinterpret_cast<const float4 *>(krow + d + 4);
-                const float4 q0 = *reinterpret_cast<const float4 *>(qrow + d);
-                const float4 q1 = *reinterpret_cast<const float4 *>(qrow + d + 4);
-                sc0 = fmaf(k0.x, q0.x, sc0); sc0 = fmaf(k0.y, q0.y, sc0);
-                sc0 = fmaf(k0.z, q0.z, sc0); sc0 = fmaf(k0.w, q0.w, sc0);
-                sc1 = fmaf(k1.x, q1.x, sc1); sc1 = fmaf(k1.y, q1.y, sc1);
-                sc1 = fmaf(k1.z, q1.z, sc1); sc1 = fmaf(k1.w, q1.w, sc1);
-            }
-            const float sv2 = (st + lane < t1) ? sc0 + sc1 : -INFINITY;
-            const float m_new = fmaxf(m_run, wave_max(sv2));
-            const float alpha = exp2f(m_run - m_new);
-            const float p = exp2f(sv2 - m_new);
-            l_lane = l_lane * alpha + p;
-            m_run = m_new;
-            sm.p[lane * kMaxG + wave] = p;
-            if (lane == 0) sm.alpha[wave] = alpha;
-        }
-        __syncthreads();
-
-        // ---- P.V
+    // the row groups of the wave, then the waves through LDS
+    merge_lanes<G, F, 16>(m, l, o);
+    merge_lanes<G, F, 32>(m, l, o);
+    if (bad) sm.bad = 1;
+    if (rg == 0) {
 #pragma unroll
         for (int j = 0; j < G; j++) {
-            const float al = sm.alpha[j];
-            o[j].x *= al; o[j].y *= al; o[j].z *= al; o[j].w *= al;
-        }
 #pragma unroll
-        for (int i = 0; i < TPG; i++) {
-            const int r = pv_tg + i * NTG;
-            const float4 vv = *reinterpret_cast<const float4 *>(&sv[r * S + 4 * pv_col]);
-            const float4 p0 = *reinterpret_cast<const float4 *>(&sm.p[r * kMaxG]);
-            const float4 p1 = *reinterpret_cast<const float4 *>(&sm.p[r * kMaxG + 4]);
-            const float pj[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-            for (int j = 0; j < G; j++) {
-                o[j].x = fmaf(pj[j], vv.x, o[j].x);
-                o[j].y = fmaf(pj[j], vv.y, o[j].y);
-                o[j].z = fmaf(pj[j], vv.z, o[j].z);
-                o[j].w = fmaf(pj[j], vv.w, o[j].w);
+            for (int e = 0; e < F; e += 4)
+                *reinterpret_cast<float4 *>(&sm.ro[wave][j][SL::col(li, e)]) =
+                    make_float4(o[j][e], o[j][e + 1], o[j][e + 2], o[j][e + 3]);
+            if (li == 0) {
+                sm.rm[wave][j] = m[j];
+                sm.rl[wave][j] = l[j];
             }
         }
     }
     __syncthreads();
 
-    // ---- reduce the P.V token groups: first the groups inside a wave (xor
-    // shuffles over the C4-lane groups), then one group per wave through LDS
-    // (reusing the K/V tiles)
-    constexpr int NW = NT / kWave;
-    float *red = sm.kv;   // [NW][G][HD]
-    static_assert(NW * G * HD <= 2 * kTile * (HD + 4), "reduction buffer");
+    const size_t part = ((size_t)s * KV + g) * a.nchunks + cidx;
+    for (int idx = tid; idx < G * HD; idx += NT) {
+        const int j = idx / HD, c = idx % HD;
+        float M = sm.rm[0][j];
 #pragma unroll
-    for (int j = 0; j < G; j++) {
-#pragma unroll
-        for (int sh = C4; sh < kWave; sh <<= 1) {
-            o[j].x += __shfl_xor(o[j].x, sh);
-            o[j].y += __shfl_xor(o[j].y, sh);
-            o[j].z += __shfl_xor(o[j].z, sh);
-            o[j].w += __shfl_xor(o[j].w, sh);
-        }
-        if (lane < C4) *reinterpret_cast<float4 *>(&red[(wave * G + j) * HD + 4 * lane]) = o[j];
-    }
-    const float lsum = wave_sum(l_lane);
-    __syncthreads();
-
-    const size_t grp = (size_t)s * KV + g;
-    const size_t part = grp * a.nchunks + cidx;
-    for (int e = tid; e < G * HD; e += NT) {
+        for (int w = 1; w < NW; w++) M = fmaxf(M, sm.rm[w][j]);
+        const float Mr = M == -INFINITY ? 0.0f : M;
         float acc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; w++) acc += red[w * G * HD + e];
-        a.po[part * G * HD + e] = acc;
+        for (int w = 0; w < NW; w++) acc = fmaf(sm.ro[w][j][c], exp2f(sm.rm[w][j] - Mr), acc);
+        a.po[part * G * HD + idx] = acc;
     }
-    if (wave < G && lane == 0) {
-        a.pml[(part * G + wave) * 2 + 0] = m_run;
-        a.pml[(part * G + wave) * 2 + 1] = sm.bad ? NAN : lsum;
+    if (tid < G) {
+        float M = sm.rm[0][tid];
+#pragma unroll
+        for (int w = 1; w < NW; w++) M = fmaxf(M, sm.rm[w][tid]);
+        const float Mr = M == -INFINITY ? 0.0f : M;
+        float ls = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) ls = fmaf(sm.rl[w][tid], exp2f(sm.rm[w][tid] - Mr), ls);
+        a.pml[(part * G + tid) * 2 + 0] = M;
+        a.pml[(part * G + tid) * 2 + 1] = sm.bad ? NAN : ls;
     }
 }
 
@@ -377,7 +533,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
 
 template <int HD, int G>
 hipError_t launch_t(const AttnArgs &a, int m, bool paged, hipStream_t st) {
-    constexpr int NT = G > 4 ? 512 : 256;
+    constexpr int NT = AttnShape<G>::threads;
     const dim3 grid(a.first[m], a.c.kv_heads);
     const int dt = a.c.dtype;
 #define CK_ATTN_LAUNCH(P, D) hipLaunchKernelGGL((k_attn<HD, G, P, D>), grid, dim3(NT), 0, st, a)
@@ -434,10 +590,13 @@ bool attn_shape_supported(int G, int hd) {
 
 bool attn_chunks_supported(int nchunks) { return nchunks >= 1 && nchunks <= kMaxChunks; }
 
-AttnPlan attn_plan(int KV, int max_tokens, long long total_tokens, int chunk_req) {
+int attn_step(int G) { return G > 4 ? AttnShape<8>::step : AttnShape<1>::step; }
+
+AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req) {
     AttnPlan p;
+    const int step = attn_step(G);
     if (chunk_req > 0) {
-        p.chunk = (chunk_req + kTile - 1) / kTile * kTile;
+        p.chunk = (chunk_req + step - 1) / step * step;
     } else {
         // about two workgroups per compute unit over all (sequence, KV head,
         // chunk) items: chunks are sized from the tokens of every sequence,
@@ -445,22 +604,23 @@ AttnPlan attn_plan(int KV, int max_tokens, long long total_tokens, int chunk_req
         const long long target = 2LL * cus_of_current_device();
         if (total_tokens < max_tokens) total_tokens = max_tokens;
         const long long c = (total_tokens * KV + target - 1) / target;
-        p.chunk = (int)((c + kTile - 1) / kTile * kTile);
+        p.chunk = (int)((c + step - 1) / step * step);
     }
-    if (p.chunk < kTile) p.chunk = kTile;
+    if (p.chunk < step) p.chunk = step;
     p.nchunks = (max_tokens + p.chunk - 1) / p.chunk;
     if (p.nchunks < 1) p.nchunks = 1;
     return p;
 }
 
-int attn_max_chunks(int KV, int max_tokens, int chunk_req) {
+int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req) {
     // the largest nchunks attn_plan returns for any positions with at most
     // max_tokens tokens per sequence: the chunk is at least
     // max_tokens * KV / (2 CUs), so nchunks <= ceil(2 CUs / KV)
-    if (chunk_req > 0) return attn_plan(KV, max_tokens, max_tokens, chunk_req).nchunks;
+    if (chunk_req > 0) return attn_plan(KV, G, max_tokens, max_tokens, chunk_req).nchunks;
     const int target = 2 * cus_of_current_device();
     const int by_items = (target + KV - 1) / KV;
-    const int by_tile = (max_tokens + kTile - 1) / kTile;
+    const int step = attn_step(G);
+    const int by_tile = (max_tokens + step - 1) / step;
     return by_tile < by_items ? by_tile : by_items;
 }
 

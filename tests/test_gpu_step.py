@@ -13,7 +13,12 @@ workload in one call), in the three variants.
     GPU's own inputs (xq bytes exact, attention within 1e-4, its Q8_0 bytes
     exact); every cache slot other than the appended ones byte-identical, and
     the appended slots of every layer within max(2e-3, 3 x the same floor
-    taken for k and v over the layers up to that one) of the oracle chain's;
+    taken for k and v over the layers up to that one, 3 x one code flip) of
+    the oracle chain's. One code flip: a rounding difference anywhere upstream
+    can move one Q8_0 code of a layer's quantized input by one, which moves
+    every appended k (v) element by up to max|W_k| (max|W_v|) times that
+    block's scale; the floor estimates need not happen to contain a flip
+    where the persistent chain has one;
   * two persistent steps in a row at successive positions: the second attends
     over the row the first appended, checked against the oracle on the GPU's
     own caches and input.
@@ -45,23 +50,40 @@ def _dims(cfg):
 def _oracle_chain(stack, x0, nudge_seed=None):
     """The oracle through every layer from x0 on fresh copies of the original
     caches; with nudge_seed, every layer input is first moved by +-1 ulp.
-    Returns the output and, per layer, the appended (k, v) slots."""
+    Returns the output, per layer the appended (k, v) slots, and per layer
+    the largest Q8_0 block scale of the layer's quantized input."""
     cfg = stack.cfg
     cos, sin = synth.rope_for(cfg)
     g = np.random.default_rng(nudge_seed) if nudge_seed is not None else None
     x = x0.copy()
-    appended = []
+    appended, dmax = [], []
     for L in stack.layers:
         if g is not None:
             up = g.random(x.shape) < 0.5
             x = np.where(up, np.nextafter(x, np.float32(np.inf)),
                          np.nextafter(x, np.float32(-np.inf))).astype(np.float32)
+        xq = np.concatenate([oracle.quantize_q8_0(oracle.rmsnorm(r, L.host["gamma"], cfg.eps))
+                             for r in x])
+        dmax.append(float(np.max(np.abs(_block_scales(xq, 34)))))
         c = _ocache(cfg, L, L.host["k"].copy(), L.host["v"].copy())
         x = oracle.decode_layer(_dims(cfg), dict(L.host, rope_cos=cos, rope_sin=sin), c, x, x,
                                 stack.pos)
         mask = _appended_mask(cfg, L, stack.pos)
         appended.append((c.k.reshape(-1)[mask].copy(), c.v.reshape(-1)[mask].copy()))
-    return x, appended
+    return x, appended, dmax
+
+
+def _block_scales(blocks, nbytes):
+    """The binary16 scales (first two bytes) of Q8_0 (34-byte) or Q5_0
+    (22-byte) blocks."""
+    b = np.ascontiguousarray(blocks, np.uint8).reshape(-1, nbytes)
+    return b[:, :2].copy().view("<f2")[:, 0].astype(np.float64)
+
+
+def _max_weight(packed, q5):
+    """An upper bound of |w| over a Q5_0 (|code - 16| <= 16) or Q8_0
+    (|code| <= 128) weight matrix: the largest block scale times the code."""
+    return float(np.max(np.abs(_block_scales(packed, 22 if q5 else 34)))) * (16 if q5 else 128)
 
 
 def _rel_dev(a, b):
@@ -127,19 +149,23 @@ def _step_check(name, layers=None):
     # layer, stage by stage) against the oracle chain. For the appended k and
     # v of layer l, the larger deviation over layers 0..l (the noise only
     # accumulates down the chain).
-    x_orc, app_orc = _oracle_chain(stack, stack.x0_host)
+    x_orc, app_orc, dmax = _oracle_chain(stack, stack.x0_host)
     bound = TOL
     kv_bounds = [(TOL, TOL)] * stack.nlayers
     if stack.nlayers > 1:
-        x_nud, app_nud = _oracle_chain(stack, stack.x0_host, 1234)
+        x_nud, app_nud, _ = _oracle_chain(stack, stack.x0_host, 1234)
         floor = max(_rel_dev(x_nud, x_orc), _rel_dev(fused_out, x_orc))
         bound = max(TOL, 3.0 * floor)
         kv_bounds, fk, fv = [], 0.0, 0.0
-        for (kn, vn), (kf, vf), (ko, vo) in zip(app_nud, fused_app, app_orc):
+        for L, dq, (kn, vn), (kf, vf), (ko, vo) in zip(stack.layers, dmax, app_nud, fused_app,
+                                                       app_orc):
             fk = max(fk, _rel_dev(kn, ko), _rel_dev(kf, ko))
             fv = max(fv, _rel_dev(vn, vo), _rel_dev(vf, vo))
-            kv_bounds.append((max(TOL, 3.0 * fk), max(TOL, 3.0 * fv)))
-        print(f"{tag}: chain noise floor {floor:.2e}", flush=True)
+            flip_k = _max_weight(L.host["wk"], True) * dq / rms(ko)
+            flip_v = _max_weight(L.host["wv"], False) * dq / rms(vo)
+            kv_bounds.append((max(TOL, 3.0 * fk, 3.0 * flip_k), max(TOL, 3.0 * fv, 3.0 * flip_v)))
+        print(f"{tag}: chain noise floor {floor:.2e}; one-flip k/v bound of the last layer "
+              f"{kv_bounds[-1][0]:.2e} / {kv_bounds[-1][1]:.2e}", flush=True)
     e2e = assert_close_rms(out, x_orc, bound, f"{tag} persistent end to end")
     rel_fused = assert_close_rms(out, fused_out, bound, f"{tag} persistent vs fused")
     print(f"{tag} persistent: e2e rel err {e2e:.2e}, vs fused {rel_fused:.2e} (bound {bound:.2e})")
