@@ -83,6 +83,13 @@ def lib():
             P, P, P, P, ctypes.POINTER(OrcTrace),
         ]
         L.orc_decode_layer.restype = i
+        L.orc_attention_sparse.argtypes = [P, ctypes.POINTER(OrcCache), i, i, i, P, i, P, P]
+        L.orc_attention_sparse.restype = i
+        L.orc_decode_layer_sparse.argtypes = [
+            ctypes.POINTER(OrcDims), ctypes.POINTER(OrcWeights), ctypes.POINTER(OrcCache),
+            P, P, P, P, i, P, P, ctypes.POINTER(OrcTrace),
+        ]
+        L.orc_decode_layer_sparse.restype = i
         _lib = L
     return _lib
 
@@ -251,8 +258,26 @@ def attention(q, cache: Cache, seq: int, L: int, H: int, want_probs: bool = Fals
     return out
 
 
-def decode_layer(dims: dict, weights: dict, cache: Cache, x, residual, pos, trace: bool = False):
+def attention_sparse(q, cache: Cache, seq: int, L: int, H: int, sel, sink=None):
+    """Attention of one sequence over the selected token positions `sel`
+    (-1 = absent), with per-head sink logits joining the denominator."""
+    q = _f32(q)
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1)
+    sink = None if sink is None else _f32(sink)
+    out = np.empty(H * cache.head_dim, np.float32)
+    cc = cache.c()
+    rc = lib().orc_attention_sparse(_p(q), ctypes.byref(cc), seq, L, H, _p(sel), sel.size,
+                                    _p(sink), _p(out))
+    if rc:
+        raise ValueError("oracle sparse attention: entry past the sequence or not held")
+    return out
+
+
+def decode_layer(dims: dict, weights: dict, cache: Cache, x, residual, pos, trace: bool = False,
+                 sel=None, sink=None):
     """One decode step of the layer for m tokens. Mutates the cache (append).
+    With sel ([m][topk] token positions, -1 = absent) the attention is the
+    sparse one over that selection, with sink logits [H] (or none).
 
     dims: D, H, KV, hd, m, eps. weights: wq, wk, wv, wo (uint8 block bytes),
     bq, bk, bv, bo, gamma (fp32, biases may be None), rope_cos, rope_sin
@@ -296,9 +321,17 @@ def decode_layer(dims: dict, weights: dict, cache: Cache, x, residual, pos, trac
         tr = OrcTrace(*[_p(bufs[n]) for n in
                         ("xn", "xq", "q_pre", "k_pre", "q", "k", "v", "attn", "aq")])
     cc = cache.c()
-    rc = lib().orc_decode_layer(ctypes.byref(od), ctypes.byref(ow), ctypes.byref(cc),
-                                _p(x), _p(residual), _p(pos), _p(out),
-                                ctypes.byref(tr) if tr is not None else None)
+    if sel is None:
+        rc = lib().orc_decode_layer(ctypes.byref(od), ctypes.byref(ow), ctypes.byref(cc),
+                                    _p(x), _p(residual), _p(pos), _p(out),
+                                    ctypes.byref(tr) if tr is not None else None)
+    else:
+        sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(m, -1)
+        sink = None if sink is None else _f32(sink)
+        rc = lib().orc_decode_layer_sparse(ctypes.byref(od), ctypes.byref(ow), ctypes.byref(cc),
+                                           _p(x), _p(residual), _p(pos), _p(sel), sel.shape[1],
+                                           _p(sink), _p(out),
+                                           ctypes.byref(tr) if tr is not None else None)
     if rc:
         raise ValueError("oracle decode_layer: bad argument, position or page")
     return (out, bufs) if trace else out

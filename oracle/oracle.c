@@ -445,9 +445,70 @@ int orc_attention(const float *q, const orc_cache *c, int seq, int L, int H,
  * The page quantizes the same normalized input once per projection; the
  * three quantizations are identical, so one is kept.
  * ======================================================================== */
-int orc_decode_layer(const orc_dims *dm, const orc_weights *w, const orc_cache *c,
-                     const float *x, const float *residual, const int32_t *pos,
-                     float *out, orc_trace *tr)
+/* ======================================================================== *
+ * Sparse attention over a selection (the spark_model page's sparse_attn and
+ * decode_fixed_topk): for each sequence, `topk` token positions of its cache
+ * (-1 = absent: the entry is skipped, so padding changes nothing) and, per
+ * query head, a sink logit that joins the softmax denominator only (reading:
+ * the usual attention sink, a virtual token with a learned logit and a zero
+ * value). With s_e = scale * q_h . K_g[sel_e] over the present entries,
+ *   out_h = sum_e exp(s_e) V_g[sel_e] / (exp(sink_h) + sum_e exp(s_e)).
+ * An entry past the sequence (>= L), or whose row the cache does not hold,
+ * is an error; duplicates each count. The window setting is not applied:
+ * the selection is the attended set.
+ * ======================================================================== */
+int orc_attention_sparse(const float *q, const orc_cache *c, int seq, int L, int H,
+                         const int32_t *sel, int topk, const float *sink, float *out)
+{
+    const int KV = c->kv_heads, hd = c->head_dim;
+    const double scale = 1.0 / sqrt((double)hd);
+    double *score = (double *)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)hd);
+    if (!score || !acc) { free(score); free(acc); return -1; }
+    int rc = 0;
+    for (int e = 0; e < topk && rc == 0; e++) {
+        const int t = sel[e];
+        if (t < 0) continue;
+        if (t >= L || (c->ring && t < L - c->capacity)) rc = -1;
+    }
+    for (int h = 0; h < H && rc == 0; h++) {
+        const int g = h * KV / H;
+        const float *qh = q + (size_t)h * hd;
+        double mx = sink ? (double)sink[h] : -INFINITY;
+        for (int e = 0; e < topk; e++) {
+            if (sel[e] < 0) continue;
+            long off = cache_row(c, seq, g, sel[e]);
+            if (off < 0) { rc = -1; break; }
+            double sc = 0.0;
+            for (int d = 0; d < hd; d++)
+                sc += (double)qh[d] * cache_value(c, 1, off + d);
+            score[e] = sc * scale;
+            if (score[e] > mx) mx = score[e];
+        }
+        if (rc) break;
+        double denom = sink ? exp((double)sink[h] - mx) : 0.0;
+        for (int d = 0; d < hd; d++) acc[d] = 0.0;
+        for (int e = 0; e < topk; e++) {
+            if (sel[e] < 0) continue;
+            long off = cache_row(c, seq, g, sel[e]);
+            double p = exp(score[e] - mx);
+            denom += p;
+            for (int d = 0; d < hd; d++)
+                acc[d] += p * cache_value(c, 0, off + d);
+        }
+        /* nothing present and no sink: an empty softmax, output zero */
+        for (int d = 0; d < hd; d++)
+            out[(size_t)h * hd + d] = denom > 0.0 ? (float)(acc[d] / denom) : 0.0f;
+    }
+    free(score);
+    free(acc);
+    return rc;
+}
+
+static int decode_layer(const orc_dims *dm, const orc_weights *w, const orc_cache *c,
+                        const float *x, const float *residual, const int32_t *pos,
+                        const int32_t *sel, int topk, const float *sink,
+                        float *out, orc_trace *tr)
 {
     const int D = dm->D, H = dm->H, KV = dm->KV, hd = dm->hd;
     const int HD = H * hd, KD = KV * hd;
@@ -477,7 +538,15 @@ int orc_decode_layer(const orc_dims *dm, const orc_weights *w, const orc_cache *
         if (tr && tr->k_pre) memcpy(tr->k_pre + (size_t)s * KD, k, sizeof(float) * KD);
         orc_rope(q, k, w->rope_cos, w->rope_sin, p, H, KV, hd);
         if (orc_kv_append(c, s, p, k, v)) { rc = -1; break; }
-        if (orc_attention(q, c, s, p + 1, H, a, NULL)) { rc = -1; break; }
+        if (sel) {
+            if (orc_attention_sparse(q, c, s, p + 1, H, sel + (size_t)s * topk, topk, sink, a)) {
+                rc = -1;
+                break;
+            }
+        } else if (orc_attention(q, c, s, p + 1, H, a, NULL)) {
+            rc = -1;
+            break;
+        }
         orc_quantize_q8_0(a, aq, HD);
         orc_gemv_q5_0(w->wo, aq, w->bo, residual ? residual + (size_t)s * D : NULL,
                       out + (size_t)s * D, D, HD);
@@ -496,4 +565,20 @@ int orc_decode_layer(const orc_dims *dm, const orc_weights *w, const orc_cache *
     }
     free(xn); free(xq); free(q); free(k); free(v); free(a); free(aq);
     return rc;
+}
+
+int orc_decode_layer(const orc_dims *dm, const orc_weights *w, const orc_cache *c,
+                     const float *x, const float *residual, const int32_t *pos,
+                     float *out, orc_trace *tr)
+{
+    return decode_layer(dm, w, c, x, residual, pos, NULL, 0, NULL, out, tr);
+}
+
+int orc_decode_layer_sparse(const orc_dims *dm, const orc_weights *w, const orc_cache *c,
+                            const float *x, const float *residual, const int32_t *pos,
+                            const int32_t *sel, int topk, const float *sink,
+                            float *out, orc_trace *tr)
+{
+    if (!sel || topk < 0) return -1;
+    return decode_layer(dm, w, c, x, residual, pos, sel, topk, sink, out, tr);
 }

@@ -134,6 +134,20 @@ int orc_decode_layer(const orc_dims *dims, const orc_weights *w, const orc_cache
                      const float *x, const float *residual, const int32_t *pos,
                      float *out, orc_trace *trace);
 
+/* Sparse attention over a selection: sel[topk] token positions of sequence
+ * seq (-1 = absent), sink[H] logits joining the denominator only (NULL = no
+ * sink). out[h] = sum_e exp(s_e) V[sel_e] / (exp(sink_h) + sum_e exp(s_e)).
+ * Returns -1 for an entry >= L or a row the cache does not hold. */
+int orc_attention_sparse(const float *q, const orc_cache *c, int seq, int L, int H,
+                         const int32_t *sel, int topk, const float *sink, float *out);
+
+/* The decode layer with the sparse attention in place of step 7: sel is
+ * [m][topk] (per sequence), sink [H] or NULL. */
+int orc_decode_layer_sparse(const orc_dims *dims, const orc_weights *w, const orc_cache *c,
+                            const float *x, const float *residual, const int32_t *pos,
+                            const int32_t *sel, int topk, const float *sink,
+                            float *out, orc_trace *tr);
+
 #ifdef __cplusplus
 }
 #endif
