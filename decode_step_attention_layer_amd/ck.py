@@ -36,6 +36,7 @@ EXPORTS = (
     "ck_decode_layer",
     "ck_decode_layer_ws_offset", "ck_decode_step_workspace_size", "ck_decode_step",
     "ck_decode_step_status_offset", "ck_decode_layer_devpos", "ck_decode_step_devpos",
+    "ck_attn_sparse", "ck_decode_layer_sparse",
 )
 
 
@@ -114,6 +115,10 @@ def load():
                                     ctypes.POINTER(CkKVCache), P, P, P, I, P, P, S, P], I),
         "ck_decode_step_devpos": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                                    ctypes.POINTER(CkKVCache), I, P, P, I, P, P, S, P], I),
+        "ck_attn_sparse": ([P, ctypes.POINTER(CkKVCache), IP, P, I, P, P, I, I, F, I, P, S, P], I),
+        "ck_decode_layer_sparse": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
+                                    ctypes.POINTER(CkKVCache), P, P, IP, P, I, P, I, P, P, P, S,
+                                    P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -265,6 +270,26 @@ def ck_decode_step(desc: CkLayerDesc, weights, caches, x, pos, out, ws, ws_bytes
     ca = caches if isinstance(caches, ctypes.Array) else (CkKVCache * n)(*caches)
     _check(load().ck_decode_step(ctypes.byref(desc), wa, ca, n, _ptr(x), _pos(pos), _ptr(out),
                                  _ptr(ws), ws_bytes, _stream(stream)), "ck_decode_step")
+
+
+def ck_attn_sparse(q, cache: CkKVCache, pos, sel, topk, sink, out, m, H, scale, chunk, ws,
+                   ws_bytes, stream=None):
+    """sel: device int32 [m][topk] (-1 = absent); sink: device fp32 [H] or None."""
+    _check(load().ck_attn_sparse(_ptr(q), ctypes.byref(cache), _pos(pos), _ptr(sel), topk,
+                                 _ptr(sink), _ptr(out), m, H, scale, chunk, _ptr(ws), ws_bytes,
+                                 _stream(stream)), "ck_attn_sparse")
+
+
+def ck_decode_layer_sparse(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache, x,
+                           residual, sel, topk, sink, out, ws, ws_bytes, pos=None, pos_dev=None,
+                           max_ctx=0, stream=None):
+    """Exactly one of pos (host positions) and pos_dev (device int32 tensor)."""
+    _check(load().ck_decode_layer_sparse(ctypes.byref(desc), ctypes.byref(weights),
+                                         ctypes.byref(cache), _ptr(x), _ptr(residual),
+                                         _pos(pos) if pos is not None else None, _ptr(pos_dev),
+                                         max_ctx, _ptr(sel), topk, _ptr(sink), _ptr(out),
+                                         _ptr(ws), ws_bytes, _stream(stream)),
+           "ck_decode_layer_sparse")
 
 
 def ck_decode_layer_devpos(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache, x,

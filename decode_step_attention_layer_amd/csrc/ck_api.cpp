@@ -350,6 +350,29 @@ int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, i
                                     static_cast<uint8_t *>(out_q8), (hipStream_t)stream));
 }
 
+int ck_attn_sparse(const float *q, const ck_kv_cache *kv, const int32_t *pos_host,
+                   const int32_t *sel, int topk, const float *sink, float *out, int m, int H,
+                   float scale, int chunk, void *ws, size_t ws_bytes, void *stream) {
+    CacheView c;
+    int rc = cache_view(kv, &c);
+    if (rc) return rc;
+    if (!q || !out || !ws || !sel || topk < 1 || H <= 0 || chunk < 0 || H % c.kv_heads)
+        return CK_EINVAL;
+    if (!al(q, 16) || !al(out, 4) || !al(ws, 16) || !al(sel, 4) || (sink && !al(sink, 4)))
+        return CK_EINVAL;
+    if (!attn_shape_supported(H / c.kv_heads, c.head_dim)) return CK_EUNSUPPORTED;
+    Positions p;
+    int mx;
+    rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
+    if (rc) return rc;
+    const AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, topk, (long long)m * topk, chunk);
+    if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
+    if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
+    const SparseSel sp{sel, topk, sink};
+    return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream,
+                                   &sp));
+}
+
 size_t ck_decode_step_workspace_size(const ck_layer_desc *desc, int layers, int max_ctx) {
     if (check_desc(desc) != CK_OK || max_ctx < 1 || layers < 1 || layers > CK_MAX_STEP_LAYERS)
         return 0;
@@ -370,7 +393,7 @@ namespace {
 
 int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                       const float *x, const float *residual, const PosIn &pin, float *out,
-                      void *ws, size_t ws_bytes, void *stream);
+                      void *ws, size_t ws_bytes, void *stream, const SparseSel *sp = nullptr);
 
 int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                      int layers, const float *x, const PosIn &pin, float *out, void *ws,
@@ -544,9 +567,10 @@ namespace {
 
 int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                       const float *x, const float *residual, const PosIn &pin, float *out,
-                      void *ws, size_t ws_bytes, void *stream) {
+                      void *ws, size_t ws_bytes, void *stream, const SparseSel *sp) {
     int rc = check_desc(desc);
     if (rc) return rc;
+    if (sp && desc->variant == CK_VARIANT_PERSISTENT) return CK_EUNSUPPORTED;
     if (desc->variant == CK_VARIANT_PERSISTENT) {
         // a one-layer persistent step; its residual is its input
         if (residual != x) return CK_EINVAL;
@@ -571,9 +595,10 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     WsLayout L = ws_layout(desc, mx);
-    // the attention covers each sequence's window only
-    const int amx = attended(mx, c.window);
-    const long long atot = p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window);
+    // the attention covers each sequence's window only, or its selection
+    const int amx = sp ? sp->topk : attended(mx, c.window);
+    const long long atot = sp ? (long long)d.m * sp->topk
+                              : (p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window));
     const AttnPlan plan = attn_plan(d.KV, d.H / d.KV, amx, atot, d.attn_chunk);
     if (!attn_chunks_supported(plan.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, plan.nchunks))
@@ -634,9 +659,10 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
         if (e != hipSuccess) return CK_EHIP;
     }
 
-    // step 7: attention over pos + 1 tokens (fused: the merge also quantizes)
+    // step 7: attention over pos + 1 tokens, or the selection (fused: the
+    // merge also quantizes)
     const float scale = 1.0f / sqrtf((float)d.head_dim);
-    e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, plan, part, st);
+    e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, plan, part, st, sp);
     if (e != hipSuccess) return CK_EHIP;
     if (!fused) {
         e = launch_quantize_q8_0(attn, aq, (long long)d.m * (HD / CK_QK), st);
@@ -664,6 +690,18 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w, const 
     if (!pos_host) return CK_EINVAL;
     return decode_layer_impl(desc, w, kv, x, residual, PosIn{pos_host, nullptr, 0}, out, ws,
                              ws_bytes, stream);
+}
+
+int ck_decode_layer_sparse(const ck_layer_desc *desc, const ck_layer_weights *w,
+                           const ck_kv_cache *kv, const float *x, const float *residual,
+                           const int32_t *pos_host, const int32_t *pos_dev, int max_ctx,
+                           const int32_t *sel, int topk, const float *sink, float *out,
+                           void *ws, size_t ws_bytes, void *stream) {
+    if (!sel || topk < 1 || !al(sel, 4) || (sink && !al(sink, 4))) return CK_EINVAL;
+    if (!pos_host == !pos_dev) return CK_EINVAL;     // exactly one source of positions
+    const SparseSel sp{sel, topk, sink};
+    const PosIn pin = pos_host ? PosIn{pos_host, nullptr, 0} : PosIn{nullptr, pos_dev, max_ctx};
+    return decode_layer_impl(desc, w, kv, x, residual, pin, out, ws, ws_bytes, stream, &sp);
 }
 
 int ck_decode_layer_devpos(const ck_layer_desc *desc, const ck_layer_weights *w,

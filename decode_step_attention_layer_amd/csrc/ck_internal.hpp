@@ -188,15 +188,23 @@ long long total_tokens(const Positions &p, int m, int window);
 bool attn_shape_supported(int G, int hd);
 bool attn_chunks_supported(int nchunks);
 size_t attn_partials_bytes(int m, int H, int hd, int nchunks);
+// Sparse attention: per sequence, topk token positions (device, [m][topk],
+// -1 = absent) replace the sequence's tokens; sink (device, [H], nullable)
+// holds logits that join the softmax denominator only.
+struct SparseSel {
+    const int32_t *sel;
+    int topk;
+    const float *sink;
+};
 hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positions &pos, int m,
                                int H, float scale, const AttnPlan &plan, void *partials,
-                               hipStream_t st);
+                               hipStream_t st, const SparseSel *sp = nullptr);
 hipError_t launch_attn_merge(const void *partials, const Positions &pos, int window, int m,
                              int H, int KV, int hd, const AttnPlan &plan, float *out,
-                             uint8_t *out_q8, hipStream_t st);
+                             uint8_t *out_q8, hipStream_t st, const SparseSel *sp = nullptr);
 hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
-                            void *partials, hipStream_t st);
+                            void *partials, hipStream_t st, const SparseSel *sp = nullptr);
 
 // Persistent decode step (k_step.hip): every layer of a step in one launch.
 struct StepLayer {

@@ -49,9 +49,15 @@ struct AttnArgs {
     float *pml;           // [m][KV][nchunks][G][2]   (max in log2 units, sum)
     int m;
     int first[kMaxSeqs + 1];  // first work item of each sequence; first[m] = items
+    // sparse attention (sel not null): sequence s attends the token positions
+    // sel[s*topk .. s*topk + topk) (-1 = absent) instead of its tokens; chunks
+    // then split the selection entries
+    const int32_t *sel;
+    int topk;
 };
 
 constexpr int kPagesLds = 512;   // page ids of a chunk staged in LDS
+constexpr int kSelLds = 1024;    // selection entries of a chunk staged in LDS
 // Workgroup shape: 4 waves; per step a wave loads 4 rows per round, 4 rounds
 // (a 64-token step), or 3 rounds (48 tokens) for large query groups, whose
 // per-lane accumulators leave fewer registers for loads. Two workgroups fit
@@ -149,6 +155,7 @@ struct Smem {
     float rm[AttnShape<G>::waves][G];       // per-wave running max (log2 units)
     float rl[AttnShape<G>::waves][G];       // per-wave sum of exponentials
     int pages[kPagesLds];                   // paged caches: the chunk's page ids
+    int sel[kSelLds];                       // sparse: the chunk's selection entries
     int bad;
 };
 
@@ -204,10 +211,19 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     while (s + 1 < a.m && item >= a.first[s + 1]) s++;
     const int cidx = item - a.first[s];
     const int L = a.pos.get(s) + 1;
-    // chunks count from the window's first token (0 without a window)
-    const int t0 = window_start(L, a.c.window) + cidx * a.chunk;
-    if (t0 >= L) return;             // device positions: items past this sequence's chunks
-    const int t1 = min(L, t0 + a.chunk);
+    const bool sparse = a.sel != nullptr;
+    // The chunk's rows [t0, t1): tokens, counted from the window's first token
+    // (0 without a window); sparse, the selection entries.
+    int t0, t1;
+    if (sparse) {
+        t0 = cidx * a.chunk;
+        if (t0 >= a.topk || L <= 0) return;
+        t1 = min(a.topk, t0 + a.chunk);
+    } else {
+        t0 = window_start(L, a.c.window) + cidx * a.chunk;
+        if (t0 >= L) return;         // device positions: items past this sequence's chunks
+        t1 = min(L, t0 + a.chunk);
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,7 +236,7 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     // LDS slots read the table per row)
     int pg0 = 0;
     bool pages_in_lds = false;
-    if constexpr (PAGED) {
+    if (PAGED && !sparse) {
         const int ps = a.c.page_size;
         pg0 = t0 / ps;
         const int npg = (t1 - 1) / ps - pg0 + 1;
@@ -229,6 +245,11 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
             for (int i = tid; i < npg; i += NT)
                 sm.pages[i] = a.c.table[(long long)s * a.c.max_pages + pg0 + i];
     }
+    // sparse: the chunk's selection entries, read once
+    const int32_t *sel_s = sparse ? a.sel + (size_t)s * a.topk : nullptr;
+    const bool sel_in_lds = sparse && t1 - t0 <= kSelLds;
+    if (sel_in_lds)
+        for (int i = tid; i < t1 - t0; i += NT) sm.sel[i] = sel_s[t0 + i];
     __syncthreads();
 
     const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
@@ -256,11 +277,30 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     };
     // Rows past the chunk re-read its last row (their scores are masked), so
     // that every load is issued unconditionally: no branch around the loads
-    // and no wait on the loads still in flight.
+    // and no wait on the loads still in flight. okbits: bit r set where row r
+    // is attended. Sparse: an absent entry (-1) reads the first row of the
+    // buffer and is masked; an entry past the sequence or no longer held by
+    // a ring marks the chunk bad.
+    uint32_t okbits = 0;
     auto fetch = [&](SL (&k)[NR], SL (&v)[NR], int st) {
+        okbits = 0;
 #pragma unroll
         for (int r = 0; r < NR; r++) {
-            const long long off = row_off(min(st + wave * WROWS + r * RPR + rg, t1 - 1));
+            const int row = st + wave * WROWS + r * RPR + rg;
+            const int e = min(row, t1 - 1);
+            bool ok = row < t1;
+            long long off;
+            if (sparse) {
+                const int t = sel_in_lds ? sm.sel[e - t0] : sel_s[e];
+                bool held = t >= 0 && t < L;
+                if (!PAGED && a.c.ring) held = held && t >= L - a.c.capacity;
+                if (t >= 0 && !held) bad = true;
+                ok = ok && held;
+                off = held ? row_off(t) : (long long)seq_base;
+            } else {
+                off = row_off(e);
+            }
+            okbits |= (ok ? 1u : 0u) << r;
             k[r].load(a.c.k, off, li);
             v[r].load(a.c.v, off, li);
         }
@@ -302,14 +342,14 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     // rows (scores, running max and sum, then P.V), which bounds the score
     // registers whatever the rows per step.
     constexpr int SUB = AttnShape<G>::sub;
-    auto compute = [&](const SL (&k)[NR], const SL (&v)[NR], int st) {
+    auto compute = [&](const SL (&k)[NR], const SL (&v)[NR]) {
 #pragma unroll
         for (int r0 = 0; r0 < NR; r0 += SUB) {
             float sc[SUB][G];
             bool ok[SUB];                            // row inside the chunk
 #pragma unroll
             for (int r = 0; r < SUB; r++) {
-                ok[r] = st + wave * WROWS + (r0 + r) * RPR + rg < t1;
+                ok[r] = (okbits >> (r0 + r)) & 1u;
                 float kf[F];
                 k[r0 + r].to_f32(kf, ksc);
 #pragma unroll
@@ -362,7 +402,7 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     // stay in flight across the loop: the compiler waits for every load at
     // the loop head.)
     for (int st = t0;;) {
-        compute(ka, va, st);
+        compute(ka, va);
         st += STEP;
         if (st >= t1) break;
         fetch(ka, va, st);
@@ -418,6 +458,8 @@ struct MergeArgs {
     Positions pos;
     int chunk, nchunks, H, KV;
     int window;          // 0 = none: the chunks cover the last `window` tokens
+    int topk;            // > 0: sparse, the chunks split topk selection entries
+    const float *sink;   // nullable: [H] logits joining the denominator only
     float *out;          // [m][H][HD]
     uint8_t *out_q8;     // nullable: [m][H*HD/32] Q8_0 blocks
 };
@@ -442,8 +484,11 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     const int lane = tid & 63, wave = tid >> 6;
     const int G = a.H / a.KV, g = h / G, j = h % G;
     const int L = a.pos.get(s) + 1;
-    const int nc = (L - window_start(L, a.window) + a.chunk - 1) / a.chunk;
+    const int n = a.topk > 0 ? (L > 0 ? a.topk : 0) : L - window_start(L, a.window);
+    const int nc = (n + a.chunk - 1) / a.chunk;
     const size_t base = ((size_t)s * a.KV + g) * a.nchunks;
+    // the sink, in the partials' log2 units
+    const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
 
     // Every load that does not depend on another goes out first: the (max,
     // sum) pairs of this thread's chunks and the outputs of its first kPre
@@ -472,10 +517,14 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     float M = red[0];
 #pragma unroll
     for (int i = 1; i < NW; i++) M = fmaxf(M, red[i]);
+    M = fmaxf(M, sk);
+    // no attended row and no sink (a selection of absent entries): the
+    // weights are zero and so is the output
+    const float Mr = M == -INFINITY ? 0.0f : M;
     __syncthreads();
     float den = 0.0f;
     for (int c = tid; c < nc; c += kMergeThreads) {
-        const float w = exp2f(w_s[c] - M);
+        const float w = exp2f(w_s[c] - Mr);
         w_s[c] = w;
         den = fmaf(w, l_s[c], den);
     }
@@ -485,6 +534,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     float D = 0.0f;
 #pragma unroll
     for (int i = 0; i < NW; i++) D += red[i];
+    if (a.sink) D += exp2f(sk - Mr);
 
     float4 n0 = make_float4(0.f, 0.f, 0.f, 0.f), n1 = n0;
     auto fma4 = [](float w, float4 v, float4 acc) {
@@ -523,7 +573,9 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
             const float4 u = part[w][tid];
             t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
         }
-        const float inv = 1.0f / D;
+        // D == 0: nothing attended and no sink, the output is zero; a NaN D
+        // (a chunk that read an unmapped or unheld row) stays NaN
+        const float inv = D == 0.0f ? 0.0f : 1.0f / D;
         const float4 v = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
         const size_t oi = ((size_t)s * a.H + h) * HD + 4 * tid;
         *reinterpret_cast<float4 *>(&a.out[oi]) = v;
@@ -633,7 +685,7 @@ size_t attn_partials_bytes(int m, int H, int hd, int nchunks) {
 
 hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positions &pos, int m,
                                int H, float scale, const AttnPlan &plan, void *partials,
-                               hipStream_t st) {
+                               hipStream_t st, const SparseSel *sp) {
     const int G = H / c.kv_heads;
     AttnArgs a;
     a.q = q;
@@ -648,13 +700,17 @@ hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positio
     a.pml = reinterpret_cast<float *>(base + up256(sizeof(float) * (size_t)m * H * plan.nchunks *
                                                    c.head_dim));
     a.m = m;
+    a.sel = sp ? sp->sel : nullptr;
+    a.topk = sp ? sp->topk : 0;
     // work items: host positions give each sequence exactly its chunks; with
-    // device positions every sequence gets plan.nchunks items and the ones
-    // past its length return at once
+    // device positions (or a selection, the same topk entries for every
+    // sequence) every sequence gets plan.nchunks items, and the ones past a
+    // sequence's length return at once
     a.first[0] = 0;
     for (int s = 0; s < m; s++) {
         const int n = pos.p[s] + 1 - window_start(pos.p[s] + 1, c.window);
-        a.first[s + 1] = a.first[s] + (pos.dev ? plan.nchunks : (n + plan.chunk - 1) / plan.chunk);
+        a.first[s + 1] = a.first[s] + ((pos.dev || sp) ? plan.nchunks
+                                                        : (n + plan.chunk - 1) / plan.chunk);
     }
     for (int s = m + 1; s <= kMaxSeqs; s++) a.first[s] = a.first[m];
     const bool paged = c.page_size != 0;
@@ -663,7 +719,7 @@ hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positio
 
 hipError_t launch_attn_merge(const void *partials, const Positions &pos, int window, int m,
                              int H, int KV, int hd, const AttnPlan &plan, float *out,
-                             uint8_t *out_q8, hipStream_t st) {
+                             uint8_t *out_q8, hipStream_t st, const SparseSel *sp) {
     const uint8_t *base = static_cast<const uint8_t *>(partials);
     MergeArgs b;
     b.po = reinterpret_cast<const float *>(base);
@@ -675,6 +731,8 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
     b.H = H;
     b.KV = KV;
     b.window = window;
+    b.topk = sp ? sp->topk : 0;
+    b.sink = sp ? sp->sink : nullptr;
     b.out = out;
     b.out_q8 = out_q8;
     if (hd == 64)
@@ -686,11 +744,11 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
 
 hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
-                            void *partials, hipStream_t st) {
-    hipError_t e = launch_attn_partial(q, c, pos, m, H, scale, plan, partials, st);
+                            void *partials, hipStream_t st, const SparseSel *sp) {
+    hipError_t e = launch_attn_partial(q, c, pos, m, H, scale, plan, partials, st, sp);
     if (e != hipSuccess) return e;
     return launch_attn_merge(partials, pos, c.window, m, H, c.kv_heads, c.head_dim, plan, out,
-                             out_q8, st);
+                             out_q8, st, sp);
 }
 
 }  // namespace ck

@@ -208,6 +208,41 @@ int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, i
                   int KV, int hd, int chunk, int window, float *out, void *out_q8,
                   void *stream);
 
+/* Sparse attention over a selection (the spark_model page's sparse_attn,
+ * with selections padded by -1 as in its decode_fixed_topk): for each
+ * sequence s and query head h (KV head g = h*KV/H),
+ *   out_h = sum_e exp(s_e) V_g[t_e] / (exp(sink_h) + sum_e exp(s_e)),
+ *   s_e = scale * q_h . K_g[t_e],
+ * over the entries t_e = sel[s*topk + e], e < topk, that are not -1. A -1
+ * entry adds nothing, so padding a selection with -1 changes no result;
+ * duplicates each count. sel: device int32 [m][topk]; sink: device fp32 [H]
+ * logits that join the denominator only (the usual attention sink), or NULL
+ * for none. Every entry other than -1 must be a token of its sequence
+ * (0 <= t <= pos_host[s]) that the cache holds: an entry past the sequence,
+ * on an unmapped page or already overwritten in a ring makes that sequence's
+ * outputs NaN (nothing is read out of bounds). With no entry and no sink the
+ * output is zero. The cache's window is not applied: the selection is the
+ * attended set. q, out: [m][H][hd]. Workspace: at least
+ * ck_attn_workspace_size(m, H, KV, hd, topk, chunk) bytes. */
+int ck_attn_sparse(const float *q, const ck_kv_cache *kv, const int32_t *pos_host,
+                   const int32_t *sel, int topk, const float *sink, float *out, int m, int H,
+                   float scale, int chunk, void *ws, size_t ws_bytes, void *stream);
+
+/* The decode layer (as ck_decode_layer) with ck_attn_sparse's attention in
+ * place of step 7, over sel [m][topk] and sink [H] (nullable), both device
+ * arrays; a selection may include the position being appended. Positions:
+ * exactly one of pos_host (host array) and pos_dev (device array, bounded by
+ * max_ctx as in ck_decode_layer_devpos). With sel, sink and pos_dev on the
+ * device and topk fixed (-1-padded selections), one captured call serves
+ * every token. Workspace: ck_decode_layer_workspace_size(desc, n) bytes with
+ * n at least the larger of topk and the largest position + 1. Chain and
+ * fused variants; the persistent variant returns CK_EUNSUPPORTED. */
+int ck_decode_layer_sparse(const ck_layer_desc *desc, const ck_layer_weights *w,
+                           const ck_kv_cache *kv, const float *x, const float *residual,
+                           const int32_t *pos_host, const int32_t *pos_dev, int max_ctx,
+                           const int32_t *sel, int topk, const float *sink, float *out,
+                           void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes ck_decode_layer needs when every position is < max_ctx. */
 size_t ck_decode_layer_workspace_size(const ck_layer_desc *desc, int max_ctx);
 

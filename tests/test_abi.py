@@ -291,3 +291,35 @@ def test_struct_layout_matches_header(ck, tmp_path):
         assert int(out[n]) == ctypes.sizeof(T), n
         for f, _ in T._fields_:
             assert int(out[f"{n}.{f}"]) == getattr(T, f).offset, f"{n}.{f}"
+
+
+def test_sparse_validation(ck):
+    L = ck.load()
+    c = ck.CkKVCache(FAKE, FAKE, 2, 64, 64, 0, None, 0, 0)
+    pos = (ctypes.c_int32 * 1)(10)
+
+    def sp(sel=FAKE, topk=8, sink=None, nws=16):
+        return L.ck_attn_sparse(FAKE, ctypes.byref(c), pos, sel, topk, sink, FAKE, 1, 4, 0.1, 0,
+                                FAKE, nws, None)
+
+    assert sp(sel=None) == ck.CK_EINVAL
+    assert sp(topk=0) == ck.CK_EINVAL
+    assert sp(sink=FAKE + 2) == ck.CK_EINVAL
+    assert sp(sel=FAKE + 1) == ck.CK_EINVAL
+    assert sp() == ck.CK_ENOSPC                       # valid arguments, workspace too small
+    assert sp(sink=FAKE) == ck.CK_ENOSPC
+    d = ck.layer_desc(256, 4, 2, 64, 1)
+    n = ck.ck_decode_layer_workspace_size(d, 64)
+    w = ck.CkLayerWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, 64)
+
+    def layer(desc=d, ph=pos, pd=None, sel=FAKE, topk=8, nws=n):
+        return L.ck_decode_layer_sparse(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(c),
+                                        FAKE, FAKE, ph, pd, 64, sel, topk, None, FAKE + 4096,
+                                        FAKE, nws, None)
+
+    assert layer(ph=None, pd=None) == ck.CK_EINVAL    # no positions
+    assert layer(pd=FAKE) == ck.CK_EINVAL             # both sources
+    assert layer(sel=None) == ck.CK_EINVAL
+    assert layer(nws=256) == ck.CK_ENOSPC
+    pers = ck.layer_desc(256, 4, 2, 64, 1, variant=ck.CK_VARIANT_PERSISTENT)
+    assert layer(desc=pers, nws=1 << 30) == ck.CK_EUNSUPPORTED
