@@ -51,6 +51,10 @@ def parse():
                     help="sliding window: attend only the last W positions (0 = all)")
     ap.add_argument("--ring", action="store_true",
                     help="keep the cache as a ring of `window` slots (contiguous workloads)")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="sparse attention: each sequence attends a selection of this many "
+                         "entries (its last 128 tokens, then uniform picks, then -1), with "
+                         "per-head sinks")
     ap.add_argument("--attn-chunk", type=int, default=0,
                     help="tokens per attention split (0 = sized to fill the GPU)")
     ap.add_argument("--eager", action="store_true", help="launch from Python, no graph replay")
@@ -66,8 +70,10 @@ def parse():
         ap.error("--ring needs --window W with W >= 1")
     if args.ring and args.config == "c5":
         ap.error("a ring cache is contiguous; c5 is paged")
-    if args.variant == "persistent" and args.window:
-        ap.error("the persistent variant takes no window or ring")
+    if args.variant == "persistent" and (args.window or args.topk):
+        ap.error("the persistent variant takes no window, ring or selection")
+    if args.topk < 0 or (args.topk and args.window):
+        ap.error("--topk takes a positive count and no window")
     return args
 
 
@@ -77,6 +83,8 @@ def workload_key(args) -> str:
     key = args.config if args.kv == "f32" else f"{args.config}-{args.kv}"
     if args.window:
         key += f"-w{args.window}" + ("-ring" if args.ring else "")
+    if args.topk:
+        key += f"-top{args.topk}"
     return key
 
 
@@ -88,6 +96,9 @@ def workload_text(args) -> str:
         text += f", sliding window of {args.window} tokens"
         if args.ring:
             text += f" in a ring of {args.window} slots"
+    if args.topk:
+        text += (f", sparse attention over selections of {args.topk} entries (the last 128 "
+                 f"tokens, then uniform picks) with per-head sinks")
     return text
 
 
@@ -135,9 +146,9 @@ def main():
     t0 = time.time()
     kv_dtype = {"f32": synth.KV_F32, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}[args.kv]
     stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu, kv_dtype=kv_dtype,
-                        window=args.window, ring=args.ring)
+                        window=args.window, ring=args.ring, topk=args.topk)
     log(f"[bench] {args.config}: {stack.nlayers} layers on device in {time.time() - t0:.1f}s")
-    nbytes = synth.algorithmic_bytes(cfg, stack.lens, kv_dtype, args.window)
+    nbytes = synth.algorithmic_bytes(cfg, stack.lens, kv_dtype, args.window, args.topk)
     step_bytes = nbytes["total"] * stack.nlayers
     replicas = 1
     if step_bytes < 3 * MALL_BYTES:
@@ -233,6 +244,7 @@ def main():
             "kv_cache": args.kv,
             "window": args.window,
             "ring": args.ring,
+            "topk": args.topk,
             "variant": args.variant,
             "attn_chunk": args.attn_chunk,
             "launch": "eager" if args.eager else "hip-graph",
@@ -295,8 +307,24 @@ def roofline(args, stacks, desc, ws, nbytes):
     out = torch.empty((m, D), dtype=torch.float32, device=ws.device)
     scale = 1.0 / math.sqrt(hd)
 
-    attn_us = _time_launches(lambda: ck.ck_attn_partial(
-        q, nxt(0).cache, stack.pos, m, H, scale, desc.attn_chunk, part, nws), args.kernel_reps)
+    if stack.topk:
+        # the sparse attention has no separate partial entry point: the pair
+        # of kernels (partial and merge) is timed
+        nws = ck.ck_attn_workspace_size(m, H, KV, hd, stack.topk, desc.attn_chunk)
+        part = torch.empty(nws, dtype=torch.uint8, device=ws.device)
+        att_out = torch.empty((m, H * hd), dtype=torch.float32, device=ws.device)
+
+        def sparse_attn():
+            L = nxt(0)
+            ck.ck_attn_sparse(q, L.cache, stack.pos, L.tensors["sel"], stack.topk,
+                              L.tensors["sink"], att_out, m, H, scale, desc.attn_chunk, part, nws)
+        attn_us = _time_launches(sparse_attn, args.kernel_reps)
+        attn_name = "k_attn+k_attn_merge"
+    else:
+        attn_us = _time_launches(lambda: ck.ck_attn_partial(
+            q, nxt(0).cache, stack.pos, m, H, scale, desc.attn_chunk, part, nws),
+            args.kernel_reps)
+        attn_name = "k_attn"
 
     def o_gemv():
         L = nxt(1)
@@ -309,7 +337,7 @@ def roofline(args, stacks, desc, ws, nbytes):
     log(f"[bench] k_attn {attn_us:.2f} us ({att_gbs:.0f} GB/s), O GEMV {wo_us:.2f} us "
         f"({wo_gbs:.0f} GB/s)")
     if attn_us >= wo_us:
-        name, gbs, us, b = "k_attn", att_gbs, attn_us, kv_bytes
+        name, gbs, us, b = attn_name, att_gbs, attn_us, kv_bytes
     else:
         name, gbs, us, b = "k_gemv", wo_gbs, wo_us, wo_bytes
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
@@ -326,7 +354,11 @@ def recorded_traffic(kernel: str, workload: str, launches_bytes=None):
     """HBM bytes per dispatch of `kernel` on `workload` from the FETCH_SIZE /
     WRITE_SIZE counter runs recorded in profiles/hbm_traffic_counters.md
     (each counter scaled by its reading for a copy of known size), or None if
-    there is no record or the kernel's source changed since it was taken."""
+    there is no record or the kernel's source changed since it was taken.
+    A name joined by '+' sums the records of its kernels."""
+    if "+" in kernel:
+        parts = [recorded_traffic(k, workload) for k in kernel.split("+")]
+        return None if any(p is None for p in parts) else sum(parts)
     import hashlib
     import re
 
@@ -341,7 +373,8 @@ def recorded_traffic(kernel: str, workload: str, launches_bytes=None):
     rec = json.loads(mt.group(1))
     csrc = os.path.join(ROOT, "decode_step_attention_layer_amd", "csrc")
     h = hashlib.sha256()
-    for f in (kernel + ".hip", "ck_device.hpp", "ck_internal.hpp", "ck_gemv_common.hpp"):
+    src_file = {"k_attn_merge": "k_attn"}.get(kernel, kernel) + ".hip"
+    for f in (src_file, "ck_device.hpp", "ck_internal.hpp", "ck_gemv_common.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     src = h.hexdigest()[:16]
@@ -379,7 +412,10 @@ def cpu_baseline(args, stack, nbytes):
             c = oracle.Cache(h["k"], h["v"], cfg.KV, cfg.hd, capacity=stack.capacity, **kvd)
         w = dict(h, rope_cos=cos, rope_sin=sin)
         t = time.perf_counter()
-        oracle.decode_layer(dims, w, c, x, x, stack.pos)
+        if stack.topk:
+            oracle.decode_layer(dims, w, c, x, x, stack.pos, sel=h["sel"], sink=h["sink"])
+        else:
+            oracle.decode_layer(dims, w, c, x, x, stack.pos)
         t_spent += time.perf_counter() - t
         done += 1
         li += 1

@@ -37,6 +37,8 @@ T_X, T_GAMMA, T_BQ, T_BK, T_BV, T_BO, T_WQ, T_WK, T_WV, T_WO = range(10)
 T_KCACHE, T_VCACHE, T_LENS, T_PERM = 10, 11, 12, 13
 T_KCODES, T_VCODES = 14, 15
 T_KRING, T_VRING = 16, 17
+T_SEL, T_SINK = 18, 19
+SEL_WINDOW = 128               # selections: the last tokens, then index picks
 
 # Reduced-precision caches: element types (the C ABI's CK_KV_*) and the fixed
 # per-tensor scales of the synthetic fp8 caches.
@@ -226,6 +228,32 @@ def ring_cache(cfg: Config, layer: int, slots: int, poison: float = float("nan")
     return out[0], out[1]
 
 
+def selection(cfg: Config, layer: int, topk: int, lens=None) -> np.ndarray:
+    """Sparse-attention selections [m][topk] int32, shaped like a sliding
+    window plus an index's picks: per sequence of L prior tokens (attending
+    L + 1 with the appended one) the last min(SEL_WINDOW, L + 1) positions,
+    then distinct earlier positions drawn uniformly, up to topk entries in
+    all, then -1."""
+    if lens is None:
+        lens = context_lengths(cfg)
+    g = rng(cfg.index, layer, T_SEL)
+    out = np.full((len(lens), topk), -1, np.int32)
+    for s, L in enumerate(lens):
+        n = int(L) + 1
+        w = min(SEL_WINDOW, n, topk)
+        win = np.arange(n - w, n, dtype=np.int32)
+        k = min(topk - w, n - w)
+        picks = g.choice(n - w, size=k, replace=False).astype(np.int32) if k > 0 else []
+        row = np.concatenate([win, picks]).astype(np.int32)
+        out[s, :row.size] = row
+    return out
+
+
+def sink_logits(cfg: Config, layer: int) -> np.ndarray:
+    """Per-head attention-sink logits [H] ~ N(0, 1)."""
+    return normal(rng(cfg.index, layer, T_SINK), (cfg.H,))
+
+
 def paged_cache(cfg: Config, layer: int, poison: float = float("nan"), spare_pages: int = 0):
     """Paged K and V pools [P][KV][page][hd], the page table [m][max_pages]
     (int32, -1 = unmapped) and the context lengths. Sequence s owns
@@ -282,10 +310,12 @@ def rope_for(cfg: Config):
     return rope_tables(cfg.rope_rows, cfg.hd, cfg.theta)
 
 
-def algorithmic_bytes(cfg: Config, lens=None, kv_dtype: int = KV_F32, window: int = 0) -> dict:
+def algorithmic_bytes(cfg: Config, lens=None, kv_dtype: int = KV_F32, window: int = 0,
+                      topk: int = 0) -> dict:
     """Bytes one layer step must move: quantized weight blocks + K and V of
     every attended token (L = pos + 1 per sequence, at most `window` of them
-    under a sliding window) in the cache's type."""
+    under a sliding window, min(L, topk) under a selection of topk entries)
+    in the cache's type."""
     D, HD, KD = cfg.D, cfg.H * cfg.hd, cfg.KV * cfg.hd
     w = (HD * D // QK) * Q5_0_BYTES + (KD * D // QK) * Q5_0_BYTES \
         + (KD * D // QK) * Q8_0_BYTES + (D * HD // QK) * Q5_0_BYTES
@@ -294,6 +324,8 @@ def algorithmic_bytes(cfg: Config, lens=None, kv_dtype: int = KV_F32, window: in
     att = np.asarray(lens, np.int64) + 1
     if window > 0:
         att = np.minimum(att, window)
+    if topk > 0:
+        att = np.minimum(att, topk)
     tokens = int(np.sum(att))
     kv = tokens * KD * KV_ELEM_BYTES[kv_dtype] * 2
     return {"weights": w, "kv": kv, "total": w + kv}

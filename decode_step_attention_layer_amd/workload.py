@@ -34,7 +34,7 @@ class DeviceStack:
     def __init__(self, cfg: synth.Config, device="cuda", poison: float = float("nan"),
                  keep_host: bool = False, spare_pages: int = 0, layers: int | None = None,
                  threads: int = 8, kv_dtype: int = synth.KV_F32, window: int = 0,
-                 ring: bool = False):
+                 ring: bool = False, topk: int = 0):
         self.cfg = cfg
         self.kv_dtype = kv_dtype
         # sliding window; a ring (contiguous caches only) has `window` slots
@@ -42,6 +42,8 @@ class DeviceStack:
         self.window = window
         self.ring = ring
         self.capacity = window if ring else cfg.capacity
+        # sparse attention: per layer a selection [m][topk] and sink logits [H]
+        self.topk = topk
         self.k_scale = synth.FP8_K_SCALE if kv_dtype == synth.KV_FP8 else 1.0
         self.v_scale = synth.FP8_V_SCALE if kv_dtype == synth.KV_FP8 else 1.0
         self.device = torch.device(device)
@@ -70,6 +72,9 @@ class DeviceStack:
             if kv_dtype != synth.KV_F32:
                 c["k"] = synth.cache_codes(c["k"], kv_dtype, cfg.index, layer, True)
                 c["v"] = synth.cache_codes(c["v"], kv_dtype, cfg.index, layer, False)
+            if topk:
+                c["sel"] = synth.selection(cfg, layer, topk, self.lens)
+                c["sink"] = synth.sink_logits(cfg, layer)
             return layer, w, c
 
         self.layers: list[DeviceLayer] = []
@@ -112,6 +117,9 @@ class DeviceStack:
         t = {n: to_dev(w[n], dev) for n in ("wq", "wk", "wv", "wo", "bq", "bk", "bv", "bo", "gamma")}
         t["k"] = to_dev(c["k"], dev)
         t["v"] = to_dev(c["v"], dev)
+        for n in ("sel", "sink"):
+            if n in c:
+                t[n] = to_dev(c[n], dev)
         cfg = self.cfg
         if cfg.page_size:
             t["table"] = to_dev(c["table"], dev)
@@ -121,7 +129,7 @@ class DeviceStack:
             cache = ck.kv_cache(t["k"], t["v"], cfg.KV, cfg.hd, self.capacity, **self._kvargs())
         weights = ck.layer_weights(t["wq"], t["wk"], t["wv"], t["wo"], t["bq"], t["bk"], t["bv"],
                                    t["bo"], t["gamma"], self.rope[0], self.rope[1], self.rope_rows)
-        host = dict(w, **{"k": c["k"], "v": c["v"]}, **({"table": c["table"]} if "table" in c else {})) \
+        host = dict(w, **{n: c[n] for n in ("k", "v", "table", "sel", "sink") if n in c}) \
             if keep_host else {}
         return DeviceLayer(t, weights, cache, host)
 
@@ -134,7 +142,7 @@ class DeviceStack:
         return ck.layer_desc(c.D, c.H, c.KV, c.hd, c.m, c.eps, variant, attn_chunk)
 
     def workspace(self, desc: ck.CkLayerDesc) -> torch.Tensor:
-        n = ck.ck_decode_layer_workspace_size(desc, self.max_ctx)
+        n = ck.ck_decode_layer_workspace_size(desc, max(self.max_ctx, self.topk))
         assert n > 0, "layer shape rejected by libck"
         return torch.empty(n, dtype=torch.uint8, device=self.device)
 
@@ -143,8 +151,13 @@ class DeviceStack:
         cur = self.x0 if x is None else x
         for i, L in enumerate(self.layers):
             out = self.bufs[i % 2]
-            ck.ck_decode_layer(desc, L.weights, L.cache, cur, cur, self.pos, out, ws,
-                               ws.numel(), stream)
+            if self.topk:
+                ck.ck_decode_layer_sparse(desc, L.weights, L.cache, cur, cur, L.tensors["sel"],
+                                          self.topk, L.tensors["sink"], out, ws, ws.numel(),
+                                          pos=self.pos, stream=stream)
+            else:
+                ck.ck_decode_layer(desc, L.weights, L.cache, cur, cur, self.pos, out, ws,
+                                   ws.numel(), stream)
             cur = out
         return cur
 
