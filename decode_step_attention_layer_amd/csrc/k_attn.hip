@@ -151,34 +151,18 @@ struct Slice {
 
 template <int HD, int G>
 struct Smem {
-    float ro[AttnShape<G>::waves][G][HD];   // per-wave partial outputs
-    float rm[AttnShape<G>::waves][G];       // per-wave running max (log2 units)
-    float rl[AttnShape<G>::waves][G];       // per-wave sum of exponentials
+    // the online-softmax state of every row group (waves x 4): unnormalized
+    // outputs, running max (log2 units), sum of exponentials; then the
+    // weight of each state in the combination
+    static constexpr int NS = AttnShape<G>::waves * 4;
+    float ro[NS][G][HD];
+    float rm[NS][G];
+    float rl[NS][G];
+    float rw[NS][G];
     int pages[kPagesLds];                   // paged caches: the chunk's page ids
     int sel[kSelLds];                       // sparse: the chunk's selection entries
     int bad;
 };
-
-// Combines the online-softmax state (m, l, o) of lane l with that of lane
-// l ^ SH (log-sum-exp rescaling); both lanes end with the same state.
-template <int G, int F, int SH>
-__device__ __forceinline__ void merge_lanes(float (&m)[G], float (&l)[G], float (&o)[G][F]) {
-#pragma unroll
-    for (int j = 0; j < G; j++) {
-        const float mo = SH == 16 ? swz_xor16_f(m[j]) : __shfl_xor(m[j], SH);
-        const float lo = SH == 16 ? swz_xor16_f(l[j]) : __shfl_xor(l[j], SH);
-        const float M = fmaxf(m[j], mo);
-        const float Mr = M == -INFINITY ? 0.0f : M;
-        const float wa = exp2f(m[j] - Mr), wb = exp2f(mo - Mr);
-        l[j] = l[j] * wa + lo * wb;
-#pragma unroll
-        for (int e = 0; e < F; e++) {
-            const float oo = SH == 16 ? swz_xor16_f(o[j][e]) : __shfl_xor(o[j][e], SH);
-            o[j][e] = o[j][e] * wa + oo * wb;
-        }
-        m[j] = M;
-    }
-}
 
 // Grid: (work item, KV head); the items are the chunks of every sequence back
 // to back, so a batch of unequal lengths launches no idle workgroups.
@@ -189,8 +173,8 @@ __device__ __forceinline__ void merge_lanes(float (&m)[G], float (&l)[G], float 
 // products of its slice with every query head of the group (q slice in
 // registers), summed over the row group with DPP. Every row group keeps its
 // own online softmax (running max, sum, unnormalized output of its slice) over
-// the rows it sees; at the end the row groups of a wave and then the waves
-// are combined by log-sum-exp.
+// the rows it sees; at the end the row groups' states are combined by
+// log-sum-exp through LDS.
 template <int HD, int G, bool PAGED, int DT>
 __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     static_assert(HD % 64 == 0 && G >= 1 && G <= kMaxG, "shape");
@@ -408,47 +392,47 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
         fetch(ka, va, st);
     }
 
-    // the row groups of the wave, then the waves through LDS
-    merge_lanes<G, F, 16>(m, l, o);
-    merge_lanes<G, F, 32>(m, l, o);
+    // Every row group's state goes to LDS as it is (no cross-lane exchange),
+    // then the chunk's state is their log-sum-exp combination: per head the
+    // largest max M, each state's weight 2^(m - M), the weighted sums.
+    constexpr int NS = Smem<HD, G>::NS;
+    const int sid = wave * 4 + rg;
     if (bad) sm.bad = 1;
-    if (rg == 0) {
 #pragma unroll
-        for (int j = 0; j < G; j++) {
+    for (int j = 0; j < G; j++) {
 #pragma unroll
-            for (int e = 0; e < F; e += 4)
-                *reinterpret_cast<float4 *>(&sm.ro[wave][j][SL::col(li, e)]) =
-                    make_float4(o[j][e], o[j][e + 1], o[j][e + 2], o[j][e + 3]);
-            if (li == 0) {
-                sm.rm[wave][j] = m[j];
-                sm.rl[wave][j] = l[j];
-            }
+        for (int e = 0; e < F; e += 4)
+            *reinterpret_cast<float4 *>(&sm.ro[sid][j][SL::col(li, e)]) =
+                make_float4(o[j][e], o[j][e + 1], o[j][e + 2], o[j][e + 3]);
+        if (li == 0) {
+            sm.rm[sid][j] = m[j];
+            sm.rl[sid][j] = l[j];
         }
     }
     __syncthreads();
-
     const size_t part = ((size_t)s * KV + g) * a.nchunks + cidx;
-    for (int idx = tid; idx < G * HD; idx += NT) {
-        const int j = idx / HD, c = idx % HD;
-        float M = sm.rm[0][j];
-#pragma unroll
-        for (int w = 1; w < NW; w++) M = fmaxf(M, sm.rm[w][j]);
-        const float Mr = M == -INFINITY ? 0.0f : M;
-        float acc = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; w++) acc = fmaf(sm.ro[w][j][c], exp2f(sm.rm[w][j] - Mr), acc);
-        a.po[part * G * HD + idx] = acc;
-    }
     if (tid < G) {
         float M = sm.rm[0][tid];
 #pragma unroll
-        for (int w = 1; w < NW; w++) M = fmaxf(M, sm.rm[w][tid]);
+        for (int i = 1; i < NS; i++) M = fmaxf(M, sm.rm[i][tid]);
         const float Mr = M == -INFINITY ? 0.0f : M;
         float ls = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; w++) ls = fmaf(sm.rl[w][tid], exp2f(sm.rm[w][tid] - Mr), ls);
+        for (int i = 0; i < NS; i++) {
+            const float w = exp2f(sm.rm[i][tid] - Mr);
+            sm.rw[i][tid] = w;
+            ls = fmaf(sm.rl[i][tid], w, ls);
+        }
         a.pml[(part * G + tid) * 2 + 0] = M;
         a.pml[(part * G + tid) * 2 + 1] = sm.bad ? NAN : ls;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * HD; idx += NT) {
+        const int j = idx / HD, c = idx % HD;
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NS; i++) acc = fmaf(sm.ro[i][j][c], sm.rw[i][j], acc);
+        a.po[part * G * HD + idx] = acc;
     }
 }
 
