@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     // Every load that does not depend on another goes out first: the (max,
     // sum) pairs of this thread's chunks and the outputs of its first kPre
     // chunk slots, so that the merge costs one memory round trip.
-    constexpr int kPre = 8;
+    constexpr int kPre = 16;
     const int d4 = tid % C4, cg = tid / C4;
     auto ld = [&](int c) {
         return *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
