@@ -71,16 +71,20 @@ struct AttnShape {
     static constexpr int step = waves * 4 * rounds;
 };
 
-// How one wave holds K/V rows: a row is read by 16 lanes, F = HD/16 elements
-// each, so one load round covers 4 rows. fp32 rows of 128 are read as two
-// 16-byte pieces per lane (columns 4i.. and 64+4i..), so that one load
-// instruction covers 256 contiguous bytes of each of its rows; otherwise a
-// lane's F elements are contiguous (columns F*i..). WORDS: raw words per lane
-// per row.
-template <int DT, int HD>
+// How one wave holds K/V rows: a row is read by LPR lanes, F = HD/LPR
+// elements each, so one load round covers 64/LPR rows. fp32 rows of 128 are
+// read as two 16-byte pieces per lane (columns 4i.. and 64+4i..), so that one
+// load instruction covers 256 contiguous bytes of each of its rows; otherwise
+// a lane's F elements are contiguous (columns F*i..). fp8 rows use 8 lanes
+// where the query group is small (16 codes, one 16-byte load a lane), so that
+// a step holds twice the rows for the same load instructions: with a quarter
+// of fp32's bytes per row, the rows per step set the bytes in flight (bf16
+// would need 32 bytes a lane, more registers than two workgroups per CU
+// leave). WORDS: raw words per lane per row.
+template <int DT, int HD, int G>
 struct RowGeo {
     static constexpr int EB = DT == CK_KV_F32 ? 4 : (DT == CK_KV_BF16 ? 2 : 1);
-    static constexpr int LPR = 16;
+    static constexpr int LPR = (DT == CK_KV_FP8_E4M3 && G <= 4) ? 8 : 16;
     static constexpr int F = HD / LPR;
     static constexpr int RPR = kWave / LPR;            // rows per load round
     static constexpr int WORDS = F * EB / 4;
@@ -89,9 +93,9 @@ struct RowGeo {
 
 
 // One lane's slice of a K or V row.
-template <int DT, int HD>
+template <int DT, int HD, int G>
 struct Slice {
-    typedef RowGeo<DT, HD> Geo;
+    typedef RowGeo<DT, HD, G> Geo;
     static constexpr int F = Geo::F;
     static constexpr int EB = Geo::EB;
     static constexpr int WORDS = Geo::WORDS;
@@ -110,7 +114,12 @@ struct Slice {
             w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
         } else {
             const uint8_t *p = static_cast<const uint8_t *>(base) + (off + (long long)F * li) * EB;
-            if constexpr (WORDS == 4) {
+            if constexpr (WORDS == 8) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(p);
+                const uint4 b = *reinterpret_cast<const uint4 *>(p + 16);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+            } else if constexpr (WORDS == 4) {
                 const uint4 a = *reinterpret_cast<const uint4 *>(p);
                 w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
             } else if constexpr (WORDS == 2) {
@@ -149,12 +158,11 @@ struct Slice {
     }
 };
 
-template <int HD, int G>
+template <int HD, int G, int NS>
 struct Smem {
-    // the online-softmax state of every row group (waves x 4): unnormalized
+    // the online-softmax state of every row group (NS of them): unnormalized
     // outputs, running max (log2 units), sum of exponentials; then the
     // weight of each state in the combination
-    static constexpr int NS = AttnShape<G>::waves * 4;
     float ro[NS][G][HD];
     float rm[NS][G];
     float rl[NS][G];
@@ -178,8 +186,8 @@ struct Smem {
 template <int HD, int G, bool PAGED, int DT>
 __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     static_assert(HD % 64 == 0 && G >= 1 && G <= kMaxG, "shape");
-    typedef Slice<DT, HD> SL;
-    typedef RowGeo<DT, HD> GEO;
+    typedef Slice<DT, HD, G> SL;
+    typedef RowGeo<DT, HD, G> GEO;
     constexpr int F = SL::F;
     constexpr int LPR = GEO::LPR;
     constexpr int RPR = GEO::RPR;
@@ -188,7 +196,8 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     constexpr int NR = AttnShape<G>::rounds;
     constexpr int WROWS = NR * RPR;                  // rows per wave per step
     constexpr int STEP = WROWS * NW;                 // tokens per workgroup step
-    __shared__ Smem<HD, G> sm;
+    constexpr int NS = NW * RPR;                     // row groups of the workgroup
+    __shared__ Smem<HD, G, NS> sm;
 
     const int item = blockIdx.x, g = blockIdx.y;
     int s = 0;
@@ -395,8 +404,7 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     // Every row group's state goes to LDS as it is (no cross-lane exchange),
     // then the chunk's state is their log-sum-exp combination: per head the
     // largest max M, each state's weight 2^(m - M), the weighted sums.
-    constexpr int NS = Smem<HD, G>::NS;
-    const int sid = wave * 4 + rg;
+    const int sid = wave * RPR + rg;
     if (bad) sm.bad = 1;
 #pragma unroll
     for (int j = 0; j < G; j++) {
@@ -411,20 +419,21 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     }
     __syncthreads();
     const size_t part = ((size_t)s * KV + g) * a.nchunks + cidx;
-    if (tid < G) {
-        float M = sm.rm[0][tid];
-#pragma unroll
-        for (int i = 1; i < NS; i++) M = fmaxf(M, sm.rm[i][tid]);
+    // one lane per (head, state), the NS states of a head in one aligned lane
+    // group: the max and the weighted sum are group reductions
+    static_assert(NS <= kWave && (NS & (NS - 1)) == 0 && G * NS <= NT, "state groups");
+    if (tid < G * NS) {
+        const int j = tid / NS, i = tid % NS;
+        const float mi = sm.rm[i][j];
+        const float M = group_max<NS>(mi);
         const float Mr = M == -INFINITY ? 0.0f : M;
-        float ls = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NS; i++) {
-            const float w = exp2f(sm.rm[i][tid] - Mr);
-            sm.rw[i][tid] = w;
-            ls = fmaf(sm.rl[i][tid], w, ls);
+        const float w = exp2f(mi - Mr);
+        sm.rw[i][j] = w;
+        const float ls = group_sum<NS>(sm.rl[i][j] * w);
+        if (i == 0) {
+            a.pml[(part * G + j) * 2 + 0] = M;
+            a.pml[(part * G + j) * 2 + 1] = sm.bad ? NAN : ls;
         }
-        a.pml[(part * G + tid) * 2 + 0] = M;
-        a.pml[(part * G + tid) * 2 + 1] = sm.bad ? NAN : ls;
     }
     __syncthreads();
     for (int idx = tid; idx < G * HD; idx += NT) {
