@@ -26,6 +26,8 @@
 // by the last workgroup to finish needs an agent-scope release per
 // workgroup, an L2 write-back on this GPU; measured, it cost more than the
 // kernel boundary.)
+#include <type_traits>
+
 #include "ck_device.hpp"
 #include "ck_internal.hpp"
 
@@ -131,8 +133,9 @@ struct Slice {
             }
         }
     }
-    // fp32 values (fp8: code value times the tensor's scale)
-    __device__ __forceinline__ void to_f32(float (&f)[F], float scale) const {
+    // fp32 values (fp8: the code values; the tensor's scale is applied by
+    // the caller, to q for K and to the output for V)
+    __device__ __forceinline__ void to_f32(float (&f)[F]) const {
         if constexpr (DT == CK_KV_F32) {
 #pragma unroll
             for (int e = 0; e < F; e++) f[e] = __uint_as_float(w[e]);
@@ -149,10 +152,10 @@ struct Slice {
             for (int i = 0; i < WORDS; i++) {
                 const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
                 const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-                f[4 * i] = lo[0] * scale;
-                f[4 * i + 1] = lo[1] * scale;
-                f[4 * i + 2] = hi[0] * scale;
-                f[4 * i + 3] = hi[1] * scale;
+                f[4 * i] = lo[0];
+                f[4 * i + 1] = lo[1];
+                f[4 * i + 2] = hi[0];
+                f[4 * i + 3] = hi[1];
             }
         }
     }
@@ -306,7 +309,8 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     // in log2 units
     float qr[G][F];
     {
-        const float qs = a.scale * kLog2e;
+        // fp8: the K scale folded in here (scores = q . (code * k_scale))
+        const float qs = a.scale * kLog2e * (DT == CK_KV_FP8_E4M3 ? a.c.k_scale : 1.0f);
         const float *qg = a.q + ((size_t)s * a.H + (size_t)g * G) * HD;
 #pragma unroll
         for (int j = 0; j < G; j++) {
@@ -329,13 +333,16 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < F; e++) o[j][e] = 0.0f;
     }
-    const float ksc = a.c.k_scale, vsc = a.c.v_scale;
 
     // The online softmax advances over the step's rows in batches of SUB
     // rows (scores, running max and sum, then P.V), which bounds the score
     // registers whatever the rows per step.
     constexpr int SUB = AttnShape<G>::sub;
-    auto compute = [&](const SL (&k)[NR], const SL (&v)[NR]) {
+    // MASKED: some row of the step lies outside the chunk (or is an absent
+    // selection entry) somewhere in the wave; steps where every row is
+    // attended skip the masking selects.
+    auto compute = [&](const SL (&k)[NR], const SL (&v)[NR], auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
         for (int r0 = 0; r0 < NR; r0 += SUB) {
             float sc[SUB][G];
@@ -344,13 +351,14 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
             for (int r = 0; r < SUB; r++) {
                 ok[r] = (okbits >> (r0 + r)) & 1u;
                 float kf[F];
-                k[r0 + r].to_f32(kf, ksc);
+                k[r0 + r].to_f32(kf);
 #pragma unroll
                 for (int j = 0; j < G; j++) {
                     float acc = 0.0f;
 #pragma unroll
                     for (int e = 0; e < F; e++) acc = fmaf(qr[j][e], kf[e], acc);
-                    sc[r][j] = ok[r] ? group_sum<LPR>(acc) : -INFINITY;
+                    sc[r][j] = group_sum<LPR>(acc);
+                    if constexpr (MASKED) sc[r][j] = ok[r] ? sc[r][j] : -INFINITY;
                 }
             }
             float p[SUB][G];
@@ -376,11 +384,13 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < SUB; r++) {
                 float vf[F];
-                v[r0 + r].to_f32(vf, vsc);
+                v[r0 + r].to_f32(vf);
                 // a row past the chunk (a re-read of its last row) adds
                 // nothing, also where that row holds an infinity
+                if constexpr (MASKED) {
 #pragma unroll
-                for (int e = 0; e < F; e++) vf[e] = ok[r] ? vf[e] : 0.0f;
+                    for (int e = 0; e < F; e++) vf[e] = ok[r] ? vf[e] : 0.0f;
+                }
 #pragma unroll
                 for (int j = 0; j < G; j++) {
 #pragma unroll
@@ -394,8 +404,15 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     // for and computed on. (A second set for the next step's loads does not
     // stay in flight across the loop: the compiler waits for every load at
     // the loop head.)
+    // The unmasked copy of the step costs registers; it is kept where two
+    // workgroups per CU still fit (small query groups, fp32 and bf16 rows).
+    constexpr bool kTwoBodies = G <= 4 && DT != CK_KV_FP8_E4M3;
+    constexpr uint32_t kAllRows = (1u << NR) - 1u;
     for (int st = t0;;) {
-        compute(ka, va);
+        if (kTwoBodies && __builtin_amdgcn_ballot_w64(okbits != kAllRows) == 0)
+            compute(ka, va, std::integral_constant<bool, !kTwoBodies>{});
+        else
+            compute(ka, va, std::true_type{});
         st += STEP;
         if (st >= t1) break;
         fetch(ka, va, st);
@@ -436,12 +453,14 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
         }
     }
     __syncthreads();
+    // fp8: the V scale applied once to the weighted sum of code values
+    const float vsc = DT == CK_KV_FP8_E4M3 ? a.c.v_scale : 1.0f;
     for (int idx = tid; idx < G * HD; idx += NT) {
         const int j = idx / HD, c = idx % HD;
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < NS; i++) acc = fmaf(sm.ro[i][j][c], sm.rw[i][j], acc);
-        a.po[part * G * HD + idx] = acc;
+        a.po[part * G * HD + idx] = acc * vsc;
     }
 }
 
