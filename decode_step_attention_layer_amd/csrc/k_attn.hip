@@ -11,17 +11,24 @@
 // covers only attended tokens. A ring cache (the spark_model page's window
 // ring) keeps token t in slot t % capacity.
 //
-// One kernel, grid (chunk, KV head, sequence). A workgroup walks its chunk of
-// tokens in tiles of 64: the K and V tiles are staged through LDS with
-// coalesced 16-byte loads (the next tile's loads are in flight while the
-// current one is computed), so each K/V byte is read from HBM once for the
-// whole query group. Scores: wave j owns query head j of the group, lane =
-// token, q (pre-scaled by scale * log2 e) broadcast from LDS; the online
-// softmax keeps a running max per head (wave-uniform) and per-lane sums.
-// P.V: thread = (4 output dims, token subset), p broadcast from LDS. The
-// chunk's (max, sum, unnormalized output) per head goes to the partials.
-// A second kernel, one workgroup per (head, sequence), merges the chunks by
-// log-sum-exp with all chunks' loads in flight at once, writes the attention
+// A sparse mode (the spark_model page's sparse_attn) attends, per sequence,
+// the token positions of a selection (-1 = absent) with per-head sink
+// logits that join the denominator: the chunks then split the selection.
+//
+// One kernel, grid (chunk, KV head): the chunks of every sequence back to
+// back. A workgroup serves all query heads of its KV head over its chunk, so
+// each K/V byte is read from HBM once for the whole query group. Its waves
+// hold K/V rows in registers, a row spread over a group of 16 lanes (8 for
+// fp8), and walk the chunk in steps of 16 (fp8: 32) rows per wave: every
+// load of a step is issued, then the rows are scored against the q slices
+// the lanes hold (pre-scaled by scale * log2 e), the partial dots summed over
+// the row group with DPP, and each row group keeps its own online softmax
+// (running max, sum, unnormalized output slice). No LDS staging and no
+// barrier inside the token loop. At the end the row groups' states are
+// combined by log-sum-exp through LDS into the chunk's (max, sum,
+// unnormalized output) per head, the partials. A second kernel, one
+// workgroup per (head, sequence), merges the chunks by log-sum-exp with all
+// chunks' loads in flight at once (the sink joins here), writes the attention
 // output and, optionally, its Q8_0 blocks. (Merging inside the first kernel
 // by the last workgroup to finish needs an agent-scope release per
 // workgroup, an L2 write-back on this GPU; measured, it cost more than the
