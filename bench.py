@@ -263,15 +263,24 @@ def main():
 
 
 def _time_launches(fn, reps):
+    """Average time of one fn() launch: `reps` launches captured in one HIP
+    graph (torch's graph API on the current stream) and replayed, timed with
+    events on that stream, so that the host's launch rate does not pace short
+    kernels."""
     import torch
 
     stream = torch.cuda.current_stream()
     fn()
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
-    for _ in range(reps):
-        fn()
+    g.replay()
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / reps     # us per launch
@@ -284,8 +293,9 @@ def roofline(args, stacks, desc, ws, nbytes):
     one kernel: k_attn) and the O-projection GEMV (ck_gemv_q5_0_q8_0, one
     kernel: k_gemv). Successive launches cycle over every layer of every
     replica, as the decode steps do, so that a launch does not find its cache
-    or weights left in the last-level cache by the one before. The kernel
-    that takes longer is reported, against the algorithmic bytes it reads."""
+    or weights left in the last-level cache by the one before; they are
+    replayed from one HIP graph. The kernel that takes longer is reported,
+    against the algorithmic bytes it reads."""
     import torch
 
     from decode_step_attention_layer_amd import ck, synth
