@@ -118,15 +118,20 @@ __device__ __forceinline__ void norm_load(const float *x, const float *gamma, in
     const int tid = threadIdx.x, n4 = D / 4;
     const float4 *x4 = reinterpret_cast<const float4 *>(x);
     const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
+    // unconditional loads (chunks past the row re-read its last chunk, and
+    // norm_quant_finish ignores them): a conditional load would make the
+    // compiler wait for it, and for every load issued before it, early
 #pragma unroll
     for (int i = 0; i < NormIn::KEEP; i++) {
-        const int c = tid + i * NT;
-        in.xv[i] = c < n4 ? x4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        in.gv[i] = c < n4 ? g4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int c = min(tid + i * NT, n4 - 1);
+        in.xv[i] = x4[c];
+        in.gv[i] = g4[c];
     }
 }
 
-template <class Sink>
+// TAIL = false: the row has at most KEEP * 256 float4 chunks (D <= 4096),
+// so the second-pass loops over wider rows are compiled out.
+template <bool TAIL = true, class Sink>
 __device__ __forceinline__ void norm_quant_finish(const NormIn &in, const float *x,
                                                   const float *gamma, int D, float eps, float *red,
                                                   Sink sink) {
@@ -137,12 +142,16 @@ __device__ __forceinline__ void norm_quant_finish(const NormIn &in, const float 
     const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
     float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < KEEP; i++)
-        ss += (in.xv[i].x * in.xv[i].x + in.xv[i].y * in.xv[i].y) +
-              (in.xv[i].z * in.xv[i].z + in.xv[i].w * in.xv[i].w);
-    for (int c = tid + KEEP * NT; c < n4; c += NT) {
-        const float4 t = x4[c];
-        ss += (t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w);
+    for (int i = 0; i < KEEP; i++) {
+        const float t = (in.xv[i].x * in.xv[i].x + in.xv[i].y * in.xv[i].y) +
+                        (in.xv[i].z * in.xv[i].z + in.xv[i].w * in.xv[i].w);
+        ss += tid + i * NT < n4 ? t : 0.0f;
+    }
+    if constexpr (TAIL) {
+        for (int c = tid + KEEP * NT; c < n4; c += NT) {
+            const float4 t = x4[c];
+            ss += (t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w);
+        }
     }
     ss = group_sum<32>(ss);
     if (lane == 0) red[2 * wave] = ss;
@@ -168,7 +177,8 @@ __device__ __forceinline__ void norm_quant_finish(const NormIn &in, const float 
         const int c = tid + i * NT;
         if (c < n4) emit(c, in.xv[i], in.gv[i]);
     }
-    for (int c = tid + KEEP * NT; c < n4; c += NT) emit(c, x4[c], g4[c]);
+    if constexpr (TAIL)
+        for (int c = tid + KEEP * NT; c < n4; c += NT) emit(c, x4[c], g4[c]);
     __syncthreads();   // red is free again
 }
 

@@ -509,22 +509,31 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     // the sink, in the partials' log2 units
     const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
 
-    // Every load that does not depend on another goes out first: the (max,
-    // sum) pairs of this thread's chunks and the outputs of its first kPre
-    // chunk slots, so that the merge costs one memory round trip.
+    // Every load that does not depend on another goes out first, none of
+    // them conditional (a slot past the last chunk re-reads the last one and
+    // is not used; a load under a branch makes the compiler wait early for
+    // it and for everything issued before it): this thread's first (max,
+    // sum) pair, then the outputs of its first kPre chunk slots, so that the
+    // merge costs one memory round trip.
     constexpr int kPre = 16;
     const int d4 = tid % C4, cg = tid / C4;
+    const int ncl = nc > 0 ? nc - 1 : 0;
     auto ld = [&](int c) {
         return *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
     };
+    const float2 ml0 =
+        *reinterpret_cast<const float2 *>(&a.pml[((base + min(tid, ncl)) * G + j) * 2]);
     float4 pre[kPre];
 #pragma unroll
-    for (int i = 0; i < kPre; i++) {
-        const int c = cg + i * CG;
-        pre[i] = c < nc ? ld(c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int i = 0; i < kPre; i++) pre[i] = ld(min(cg + i * CG, ncl));
+    __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
-    for (int c = tid; c < nc; c += kMergeThreads) {
+    if (tid < nc) {
+        w_s[tid] = ml0.x;
+        l_s[tid] = ml0.y;
+        mx = ml0.x;
+    }
+    for (int c = tid + kMergeThreads; c < nc; c += kMergeThreads) {
         const float2 ml = *reinterpret_cast<const float2 *>(&a.pml[((base + c) * G + j) * 2]);
         w_s[c] = ml.x;
         l_s[c] = ml.y;

@@ -121,7 +121,97 @@ __device__ __forceinline__ void gemv_body(const GemvSeg &sg, int wg_in_seg, XBlo
     }
 }
 
-template <int LPR, int UPL, int R, bool PAIRED>
+// One token with at most 256 activation blocks (m = 1, K <= 8192). The
+// loads go out in the order their values are needed and none is
+// conditional (rows and units past the end re-read the last one; what they
+// contribute is discarded), because the memory counter retires loads in
+// issue order and a load under a branch makes the compiler wait early for
+// it and for everything before it: this thread's activation block, bias and
+// residual, then the weights. The activation block is staged into LDS while
+// the weights are in flight.
+template <bool Q5, int LPR, int UPL, int R, bool PAIRED>
+__device__ __forceinline__ void gemv_body1(const GemvSeg &sg, int wg_in_seg, XBlock *xs,
+                                           const uint8_t *xq, int nb) {
+    using F = Fmt<Q5, PAIRED>;
+    constexpr int RPW = kWave / LPR;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = lane % LPR, rsel = lane / LPR;
+    const int nunits = nb / F::blocks;
+    const size_t row_bytes = (size_t)nb * (Q5 ? kQ5Bytes : kQ8Bytes);
+    const int row0 = (wg_in_seg * kGemvWaves + wave) * (RPW * R);
+
+    const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)min(tid, nb - 1) * kQ8Bytes);
+    uint32_t xr[9];
+    xr[0] = src[0];
+#pragma unroll
+    for (int i = 0; i < 8; i++) xr[1 + i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+
+    int row[R];
+    float bias_v[R], res_v[R];
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        row[it] = min(row0 + it * RPW + rsel, sg.rows - 1);
+        bias_v[it] = sg.bias ? sg.bias[row[it]] : 0.0f;
+        res_v[it] = sg.residual ? sg.residual[row[it]] : 0.0f;
+    }
+    uint32_t wr[R][UPL][F::words];
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        const uint8_t *rp = sg.W + (size_t)row[it] * row_bytes;
+#pragma unroll
+        for (int u = 0; u < UPL; u++) {
+            const int unit = min(sub + u * LPR, nunits - 1);
+            load_unit<Q5, PAIRED>(rp + (size_t)unit * F::bytes, wr[it][u]);
+        }
+    }
+    // keep the scheduler from moving the staging above the weight loads
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (tid < nb) {
+        XBlock xb;
+        xb.d = half_bits_to_float(xr[0]);
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            xb.c[i] = (int)xr[1 + i];
+            sum = __builtin_amdgcn_sdot4((int)xr[1 + i], 0x01010101, sum, false);
+        }
+        xb.sum = sum;
+        xb.pad[0] = xb.pad[1] = 0;
+        xs[tid] = xb;
+    }
+    __syncthreads();
+
+    // units past the row take a zero activation block: the re-read unit adds
+    // exactly zero
+    XBlock xb[UPL][F::blocks];
+#pragma unroll
+    for (int u = 0; u < UPL; u++) {
+        const int unit = sub + u * LPR;
+#pragma unroll
+        for (int b = 0; b < F::blocks; b++) {
+            if (unit < nunits)
+                xb[u][b] = xs[unit * F::blocks + b];
+            else
+                xb[u][b] = XBlock{{0, 0, 0, 0, 0, 0, 0, 0}, 0.0f, 0, {0, 0}};
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < UPL; u++) acc = unit_dot<Q5, PAIRED>(wr[it][u], xb[u], acc);
+        acc = row_reduce<LPR>(acc);
+        const int r = row0 + it * RPW + rsel;
+        if (sub == 0 && r < sg.rows) {
+            float o = acc + bias_v[it];
+            if (sg.residual) o = o + res_v[it];
+            sg.y[r] = o;
+        }
+    }
+}
+
+template <int LPR, int UPL, int R, bool PAIRED, bool ONE>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
     extern __shared__ XBlock xs[];
     const int wg = blockIdx.x;
@@ -131,10 +221,17 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
     const int nb = a.K / kQK;
 
     const int wg_in_seg = wg - sg.wg_begin;
-    if (sg.is_q5)
-        gemv_body<true, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb, a.m);
-    else
-        gemv_body<false, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb, a.m);
+    if constexpr (ONE) {
+        if (sg.is_q5)
+            gemv_body1<true, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb);
+        else
+            gemv_body1<false, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb);
+    } else {
+        if (sg.is_q5)
+            gemv_body<true, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb, a.m);
+        else
+            gemv_body<false, LPR, UPL, R, PAIRED>(sg, wg_in_seg, xs, a.xq, nb, a.m);
+    }
 }
 
 constexpr int kRowsIter = 2;
@@ -149,8 +246,12 @@ hipError_t launch_t(GemvArgs a, hipStream_t st) {
     }
     for (int i = a.nseg; i < 3; i++) a.seg[i] = a.seg[0], a.seg[i].wg_begin = 1 << 30;
     const size_t lds = sizeof(XBlock) * (size_t)a.m * (a.K / kQK);
-    hipLaunchKernelGGL((k_gemv<LPR, UPL, kRowsIter, PAIRED>), dim3(total), dim3(kGemvThreads), lds,
-                       st, a);
+    if (a.m == 1 && a.K / kQK <= kGemvThreads)
+        hipLaunchKernelGGL((k_gemv<LPR, UPL, kRowsIter, PAIRED, true>), dim3(total),
+                           dim3(kGemvThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((k_gemv<LPR, UPL, kRowsIter, PAIRED, false>), dim3(total),
+                           dim3(kGemvThreads), lds, st, a);
     return hipGetLastError();
 }
 

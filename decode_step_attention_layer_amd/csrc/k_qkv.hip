@@ -4,10 +4,11 @@
 // "mega_fused_attention_decode_q5_0.c" (MAIN KERNEL steps 1-6) in one launch:
 //   xn = RMSNorm(x); xq = Q8_0(xn); q = Wq xq + bq; k = Wk xq + bk; v = Wv xq + bv
 //   RoPE(q, k, pos); cache[pos] = (k, v)
-// Every workgroup first issues the loads of its weight rows (they do not
-// depend on x), then recomputes the normalization and quantization of x for
-// all tokens into LDS while those loads are in flight (x and gamma come from
-// L2; every workgroup computes bit-identical values), then the block dots.
+// One token per launch. Every workgroup issues the loads of x and gamma and
+// then those of its weight rows (they do not depend on x), recomputes the
+// normalization and quantization of x into LDS while the weight loads are in
+// flight (x and gamma come from L2; every workgroup computes bit-identical
+// values), then the block dots.
 // Logical rows are ordered so that the two rows a RoPE rotation pairs (head
 // element i and i + hd/2) sit in the same wavefront: consecutive iterations
 // of a wave when a row spans the wave, neighbouring lane groups otherwise.
@@ -45,45 +46,49 @@ __device__ __forceinline__ int rope_row(int r, int hd) {
     return (p / half) * hd + (p % half) + (r & 1) * half;
 }
 
-// RMSNorm + Q8_0 of the m tokens into LDS (codes, fp16-rounded scale, code
-// sum); workgroup 0 also writes xn and the xq bytes to the workspace. The
-// first token's x and gamma chunks arrive preloaded in `first`.
-__device__ void stage_normalized(const QkvArgs &a, const NormIn &first, XBlock *xs, float *red,
-                                 bool write_trace) {
-    const int D = a.D, nb = D / kQK;
-    for (int s = 0; s < a.m; s++) {
-        NormIn in;
-        if (s == 0) in = first;
-        else norm_load(a.x + (size_t)s * D, a.gamma, D, in);
-        norm_quant_finish(in, a.x + (size_t)s * D, a.gamma, D, a.eps, red,
-                       [&](int c, float4 v, uint32_t packed, uint16_t dbits, int csum) {
-                           const int b = c >> 3, sub = c & 7;
-                           XBlock &xb = xs[s * nb + b];
-                           xb.c[sub] = (int)packed;
-                           if (sub == 0) {
-                               xb.d = half_bits_to_float(dbits);
-                               xb.sum = csum;
-                           }
-                           if (write_trace) {
-                               reinterpret_cast<float4 *>(a.xn + (size_t)s * D)[c] = v;
-                               uint8_t *blk = a.xq + ((size_t)s * nb + b) * kQ8Bytes;
-                               uint16_t *dst = reinterpret_cast<uint16_t *>(blk + 2 + 4 * sub);
-                               dst[0] = (uint16_t)(packed & 0xFFFF);
-                               dst[1] = (uint16_t)(packed >> 16);
-                               if (sub == 0) *reinterpret_cast<uint16_t *>(blk) = dbits;
-                           }
-                       });
-    }
+// RMSNorm + Q8_0 of the token into LDS (codes, fp16-rounded scale, code
+// sum); workgroup 0 also writes xn and the xq bytes to the workspace. x and
+// gamma arrive preloaded in `in`.
+template <bool TAIL>
+__device__ __forceinline__ void stage_normalized(const QkvArgs &a, const NormIn &in, XBlock *xs,
+                                                 float *red, bool write_trace) {
+    const int D = a.D;
+    norm_quant_finish<TAIL>(in, a.x, a.gamma, D, a.eps, red,
+                            [&](int c, float4 v, uint32_t packed, uint16_t dbits, int csum) {
+                                const int b = c >> 3, sub = c & 7;
+                                XBlock &xb = xs[b];
+                                xb.c[sub] = (int)packed;
+                                if (sub == 0) {
+                                    xb.d = half_bits_to_float(dbits);
+                                    xb.sum = csum;
+                                }
+                                if (write_trace) {
+                                    reinterpret_cast<float4 *>(a.xn)[c] = v;
+                                    uint8_t *blk = a.xq + (size_t)b * kQ8Bytes;
+                                    uint16_t *dst = reinterpret_cast<uint16_t *>(blk + 2 + 4 * sub);
+                                    dst[0] = (uint16_t)(packed & 0xFFFF);
+                                    dst[1] = (uint16_t)(packed >> 16);
+                                    if (sub == 0) *reinterpret_cast<uint16_t *>(blk) = dbits;
+                                }
+                            });
 }
 
-template <bool Q5, int LPR, int UPL, int R, bool PAIRED>
+// One token (the kernel serves m = 1). The loads go out in the order their
+// values are needed and none is conditional (rows and units past the end
+// re-read the last one; what they contribute is discarded), so that every
+// wait covers only what it needs: the memory counter retires loads in issue
+// order, and a load under a branch makes the compiler wait early for it and
+// for everything before it. Order: the position (device positions), x and
+// gamma, bias and RoPE factors, then the weights; the normalization and
+// quantization of x run while the weights are in flight.
+template <bool Q5, int LPR, int UPL, int R, bool PAIRED, bool TAIL>
 __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_seg, XBlock *xs,
                                          float *red) {
     using F = Fmt<Q5, PAIRED>;
     constexpr int RPW = kWave / LPR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPR, rsel = lane / LPR;
-    const int D = a.D, nb = D / kQK, hd = a.hd;
+    const int D = a.D, nb = D / kQK, hd = a.hd, half = hd >> 1;
     const int nunits = nb / F::blocks;
     const size_t row_bytes = (size_t)nb * (Q5 ? kQ5Bytes : kQ8Bytes);
     const uint8_t *W = seg == 0 ? a.wq : (seg == 1 ? a.wk : a.wv);
@@ -92,105 +97,92 @@ __device__ __forceinline__ void qkv_body(const QkvArgs &a, int seg, int wg_in_se
     const bool rotate = seg < 2;
     const int row0 = (wg_in_seg * kGemvWaves + wave) * (RPW * R);
 
-    // 1. the first token's x and gamma (the normalization needs them first),
-    // then the weights of all R rows: all in flight before any arithmetic
-    NormIn first;
-    norm_load(a.x, a.gamma, a.D, first);
+    // an invalid device position reads table row 0 and appends nothing
+    const int pv = a.pos.get(0);
+    const int p = max(pv, 0);
+    NormIn xin;
+    norm_load(a.x, a.gamma, D, xin);
+
+    int pr[R];
+    float bias_v[R], cs[R], sn[R];
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        const int lr = min(row0 + it * RPW + rsel, rows - 1);
+        pr[it] = rotate ? rope_row(lr, hd) : lr;
+        bias_v[it] = bias ? bias[pr[it]] : 0.0f;
+        const int i = (lr >> 1) % half;
+        cs[it] = a.cos_tab[(size_t)p * half + i];
+        sn[it] = a.sin_tab[(size_t)p * half + i];
+    }
     uint32_t wr[R][UPL][F::words];
 #pragma unroll
     for (int it = 0; it < R; it++) {
-        const int lr = row0 + it * RPW + rsel;
-        const int pr = rotate ? rope_row(lr, hd) : lr;
-        const uint8_t *rp = W + (size_t)pr * row_bytes;
+        const uint8_t *rp = W + (size_t)pr[it] * row_bytes;
 #pragma unroll
         for (int u = 0; u < UPL; u++) {
-            const int unit = sub + u * LPR;
-            if (lr < rows && unit < nunits) {
-                load_unit<Q5, PAIRED>(rp + (size_t)unit * F::bytes, wr[it][u]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < F::words; i++) wr[it][u][i] = 0;
-            }
+            const int unit = min(sub + u * LPR, nunits - 1);
+            load_unit<Q5, PAIRED>(rp + (size_t)unit * F::bytes, wr[it][u]);
         }
     }
+    // keep the scheduler from moving the normalization's arithmetic above
+    // the weight loads
+    __builtin_amdgcn_sched_barrier(0);
 
-    // bias and the first token's RoPE factors go out with the weight loads
-    // (an invalid position reads table row 0 and appends nothing)
-    const int half = hd >> 1;
-    const int p0 = max(a.pos.get(0), 0);
-    float bias_v[R], cs0[R], sn0[R];
+    // normalized, quantized activations into LDS (overlaps the weight loads)
+    stage_normalized<TAIL>(a, xin, xs, red, blockIdx.x == 0);
+
+    // dots, bias, RoPE, stores; units past the row take a zero activation
+    // block, so the re-read unit adds exactly zero
+    XBlock xb[UPL][F::blocks];
+#pragma unroll
+    for (int u = 0; u < UPL; u++) {
+        const int unit = sub + u * LPR;
+#pragma unroll
+        for (int b = 0; b < F::blocks; b++) {
+            if (unit < nunits)
+                xb[u][b] = xs[unit * F::blocks + b];
+            else
+                xb[u][b] = XBlock{{0, 0, 0, 0, 0, 0, 0, 0}, 0.0f, 0, {0, 0}};
+        }
+    }
+    float val[R];
+#pragma unroll
+    for (int it = 0; it < R; it++) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < UPL; u++) acc = unit_dot<Q5, PAIRED>(wr[it][u], xb[u], acc);
+        acc = row_reduce<LPR>(acc);
+        val[it] = acc + bias_v[it];
+    }
 #pragma unroll
     for (int it = 0; it < R; it++) {
         const int lr = row0 + it * RPW + rsel;
-        const int pr = rotate ? rope_row(lr, hd) : lr;
-        bias_v[it] = (bias && lr < rows) ? bias[pr] : 0.0f;
-        const int i = (lr >> 1) % half;
-        cs0[it] = rotate ? a.cos_tab[(size_t)p0 * half + i] : 0.0f;
-        sn0[it] = rotate ? a.sin_tab[(size_t)p0 * half + i] : 0.0f;
-    }
-
-    // 2. normalized, quantized activations into LDS (overlaps the loads)
-    stage_normalized(a, first, xs, red, blockIdx.x == 0);
-
-    // 3. dots, bias, RoPE, stores
-    for (int s = 0; s < a.m; s++) {
-        XBlock xb[UPL][F::blocks];
-#pragma unroll
-        for (int u = 0; u < UPL; u++) {
-            const int unit = sub + u * LPR;
-#pragma unroll
-            for (int b = 0; b < F::blocks; b++) {
-                if (unit < nunits)
-                    xb[u][b] = xs[(size_t)s * nb + unit * F::blocks + b];
-                else
-                    xb[u][b] = XBlock{{0, 0, 0, 0, 0, 0, 0, 0}, 0.0f, 0, {0, 0}};
+        float out = val[it];
+        if (rotate) {
+            // the partner of this row: the next/previous iteration when a
+            // row spans the wave, the neighbouring lane group otherwise
+            float other;
+            if constexpr (LPR == kWave) {
+                other = val[it ^ 1];
+            } else {
+                other = __shfl_xor(val[it], LPR);
             }
+            out = (lr & 1) ? other * sn[it] + val[it] * cs[it] : val[it] * cs[it] - other * sn[it];
         }
-        float val[R];
-#pragma unroll
-        for (int it = 0; it < R; it++) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int u = 0; u < UPL; u++) acc = unit_dot<Q5, PAIRED>(wr[it][u], xb[u], acc);
-            acc = row_reduce<LPR>(acc);
-            val[it] = acc + bias_v[it];
-        }
-        const int pv = a.pos.get(s);
-        const int p = max(pv, 0);
-#pragma unroll
-        for (int it = 0; it < R; it++) {
-            const int lr = row0 + it * RPW + rsel;
-            const int pr = rotate ? rope_row(lr, hd) : lr;
-            float out = val[it];
-            if (rotate) {
-                // the partner of this row: the next/previous iteration when a
-                // row spans the wave, the neighbouring lane group otherwise
-                float other;
-                if constexpr (LPR == kWave) {
-                    other = val[it ^ 1];
-                } else {
-                    other = __shfl_xor(val[it], LPR);
-                }
-                const int i = (lr >> 1) % half;
-                const float cs = s == 0 ? cs0[it] : a.cos_tab[(size_t)p * half + i];
-                const float sn = s == 0 ? sn0[it] : a.sin_tab[(size_t)p * half + i];
-                out = (lr & 1) ? other * sn + val[it] * cs : val[it] * cs - other * sn;
-            }
-            if (sub == 0 && lr < rows) {
-                const int g = pr / hd, d = pr % hd;
-                if (seg == 0) {
-                    a.q[(size_t)s * rows + pr] = out;
-                } else {
-                    (seg == 1 ? a.k : a.v)[(size_t)s * rows + pr] = out;
-                    const long long off = pv >= 0 ? cache_row(a.c, s, g, p) : -1;
-                    if (off >= 0) cache_put(a.c, seg == 1, off + d, out);
-                }
+        if (sub == 0 && lr < rows) {
+            const int g = pr[it] / hd, d = pr[it] % hd;
+            if (seg == 0) {
+                a.q[pr[it]] = out;
+            } else {
+                (seg == 1 ? a.k : a.v)[pr[it]] = out;
+                const long long off = pv >= 0 ? cache_row(a.c, 0, g, p) : -1;
+                if (off >= 0) cache_put(a.c, seg == 1, off + d, out);
             }
         }
     }
 }
 
-template <int LPR, int UPL, int R, bool PAIRED>
+template <int LPR, int UPL, int R, bool PAIRED, bool TAIL>
 __global__ __launch_bounds__(kGemvThreads) void k_qkv(QkvArgs a) {
     extern __shared__ XBlock xs[];
     __shared__ float red[2 * kGemvWaves];
@@ -198,9 +190,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_qkv(QkvArgs a) {
     const int seg = wg >= a.wg_v ? 2 : (wg >= a.wg_k ? 1 : 0);
     const int wg_in_seg = wg - (seg == 2 ? a.wg_v : (seg == 1 ? a.wg_k : 0));
     if (seg == 2)
-        qkv_body<false, LPR, UPL, R, PAIRED>(a, seg, wg_in_seg, xs, red);
+        qkv_body<false, LPR, UPL, R, PAIRED, TAIL>(a, seg, wg_in_seg, xs, red);
     else
-        qkv_body<true, LPR, UPL, R, PAIRED>(a, seg, wg_in_seg, xs, red);
+        qkv_body<true, LPR, UPL, R, PAIRED, TAIL>(a, seg, wg_in_seg, xs, red);
 }
 
 template <int LPR, int UPL, int R, bool PAIRED>
@@ -210,9 +202,13 @@ hipError_t launch_t(QkvArgs a, hipStream_t st) {
     const int nk = (a.KV * a.hd + rows_per_wg - 1) / rows_per_wg;
     a.wg_k = nq;
     a.wg_v = nq + nk;
-    const size_t lds = sizeof(XBlock) * (size_t)a.m * (a.D / kQK);
-    hipLaunchKernelGGL((k_qkv<LPR, UPL, R, PAIRED>), dim3(nq + 2 * nk), dim3(kGemvThreads), lds,
-                       st, a);
+    const size_t lds = sizeof(XBlock) * (size_t)(a.D / kQK);
+    if (a.D <= NormIn::KEEP * kGemvThreads * 4)
+        hipLaunchKernelGGL((k_qkv<LPR, UPL, R, PAIRED, false>), dim3(nq + 2 * nk),
+                           dim3(kGemvThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((k_qkv<LPR, UPL, R, PAIRED, true>), dim3(nq + 2 * nk),
+                           dim3(kGemvThreads), lds, st, a);
     return hipGetLastError();
 }
 
