@@ -214,7 +214,9 @@ hipError_t launch_t(QkvArgs a, hipStream_t st) {
 
 template <int LPR, bool PAIRED>
 hipError_t launch_upl(const QkvArgs &a, int upl, hipStream_t st) {
-    constexpr int R = LPR == kWave ? 4 : 2;   // rows per wave iteration set x R, even
+    // rows per wave: 2 (a RoPE pair), so that the workgroups are small and
+    // many; each CU's share of the weights, not the total, sets the time
+    constexpr int R = 2;
     if (upl <= 1) return launch_t<LPR, 1, R, PAIRED>(a, st);
     if (upl <= 2) return launch_t<LPR, 2, R, PAIRED>(a, st);
     return launch_t<LPR, 4, R, PAIRED>(a, st);
