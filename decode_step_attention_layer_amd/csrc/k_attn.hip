@@ -684,12 +684,14 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
         const long long target = 2LL * cus_of_current_device();
         if (total_tokens < max_tokens) total_tokens = max_tokens;
         const long long c = (total_tokens * KV + target - 1) / target;
-        // whole steps, rounded up; rounded down instead where that drops at
-        // most an eighth of a step (a sequence one token past a multiple of
-        // the step: the extra token gets a chunk of its own rather than
-        // making every chunk a step longer)
-        const long long dn = c / step * step;
-        p.chunk = (int)((dn >= step && c - dn <= step / 8) ? dn : (c + step - 1) / step * step);
+        p.chunk = (int)((c + step - 1) / step * step);
+        // between one and one and a half workgroups per compute unit, the
+        // units holding two set the time: twice the chunk gives every busy
+        // unit the same work in half the workgroups (and half the partials
+        // to merge)
+        const long long items = (total_tokens + p.chunk - 1) / p.chunk * KV;
+        const long long cus = cus_of_current_device();
+        if (items > cus && 2 * items <= 3 * cus) p.chunk *= 2;
     }
     if (p.chunk < step) p.chunk = step;
     p.nchunks = (max_tokens + p.chunk - 1) / p.chunk;
@@ -699,12 +701,11 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
 
 int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req) {
     // the largest nchunks attn_plan returns for any positions with at most
-    // max_tokens tokens per sequence: the chunk is at least 7/8 of
-    // max_tokens * KV / (2 CUs) (rounded down by at most an eighth of a step,
-    // only when it stays at least one step), so nchunks <= 8/7 * 2 CUs / KV + 1
+    // max_tokens tokens per sequence: the chunk is at least
+    // max_tokens * KV / (2 CUs), so nchunks <= ceil(2 CUs / KV)
     if (chunk_req > 0) return attn_plan(KV, G, max_tokens, max_tokens, chunk_req).nchunks;
     const int target = 2 * cus_of_current_device();
-    const int by_items = (8 * target + 7 * KV - 1) / (7 * KV) + 1;
+    const int by_items = (target + KV - 1) / KV;
     const int step = attn_step(G);
     const int by_tile = (max_tokens + step - 1) / step;
     return by_tile < by_items ? by_tile : by_items;
