@@ -611,6 +611,85 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
     }
 }
 
+// The merge for sequences of at most kMerge1Chunks chunks: one wavefront per
+// (head, sequence), no LDS and no barrier. A chunk's output row is held by
+// HD/4 lanes (4 values each); the chunks are dealt round-robin to the
+// 64 / (HD/4) lane groups. Every load goes out at once and none is
+// conditional (a slot past the last chunk re-reads the last one and is not
+// used): lane c's chunk (max, sum) pair, then the lane's output slices. The
+// global max and the denominator are wave reductions; each chunk's weight
+// is computed by lane c and read from it into scalar registers; the lane
+// groups' sums are combined with cross-lane exchanges.
+constexpr int kMerge1Chunks = 32;
+
+template <int HD>
+__global__ __launch_bounds__(kWave) void k_attn_merge1(MergeArgs a) {
+    constexpr int LG = HD / 4;                 // lanes per chunk group
+    constexpr int NGRP = kWave / LG;           // chunk groups
+    constexpr int PER = kMerge1Chunks / NGRP;  // chunk slots per lane
+    const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+    const int G = a.H / a.KV, g = h / G, j = h % G;
+    const int L = a.pos.get(s) + 1;
+    const int n = a.topk > 0 ? (L > 0 ? a.topk : 0) : L - window_start(L, a.window);
+    const int nc = (n + a.chunk - 1) / a.chunk;
+    const int ncl = nc > 0 ? nc - 1 : 0;
+    const size_t base = ((size_t)s * a.KV + g) * a.nchunks;
+    const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const int d4 = lane % LG, grp = lane / LG;
+
+    const float2 ml =
+        *reinterpret_cast<const float2 *>(&a.pml[((base + min(lane, ncl)) * G + j) * 2]);
+    float4 ov[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int c = min(grp + NGRP * i, ncl);
+        ov[i] = *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    const bool mine = lane < nc;
+    const float M = fmaxf(wave_max(mine ? ml.x : -INFINITY), sk);
+    // no attended row and no sink (a selection of absent entries): the
+    // weights are zero and so is the output
+    const float Mr = M == -INFINITY ? 0.0f : M;
+    const float w = mine ? exp2f(ml.x - Mr) : 0.0f;
+    float D = wave_sum(mine ? w * ml.y : 0.0f);
+    if (a.sink) D += exp2f(sk - Mr);
+
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int c = grp + NGRP * i;
+        // chunk c's weight: read from lane c into a scalar register (the
+        // lane index is a constant per group), no wait on a permute
+        float wc = readlane_f(w, NGRP * i);
+#pragma unroll
+        for (int q = 1; q < NGRP; q++) {
+            const float t = readlane_f(w, NGRP * i + q);
+            wc = grp == q ? t : wc;
+        }
+        if (c < nc)
+            acc = make_float4(fmaf(wc, ov[i].x, acc.x), fmaf(wc, ov[i].y, acc.y),
+                              fmaf(wc, ov[i].z, acc.z), fmaf(wc, ov[i].w, acc.w));
+    }
+#pragma unroll
+    for (int sh = LG; sh < kWave; sh <<= 1) {
+        acc.x += __shfl_xor(acc.x, sh);
+        acc.y += __shfl_xor(acc.y, sh);
+        acc.z += __shfl_xor(acc.z, sh);
+        acc.w += __shfl_xor(acc.w, sh);
+    }
+    if (grp == 0) {
+        // D == 0: nothing attended and no sink, the output is zero; a NaN D
+        // (a chunk that read an unmapped or unheld row) stays NaN
+        const float inv = D == 0.0f ? 0.0f : 1.0f / D;
+        const float4 v = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        const size_t oi = ((size_t)s * a.H + h) * HD + 4 * d4;
+        *reinterpret_cast<float4 *>(&a.out[oi]) = v;
+        if (a.out_q8) quantize_q8_0_x4(v, a.out_q8 + (oi / kQK) * kQ8Bytes, d4 & 7);
+    }
+}
+
 template <int HD, int G>
 hipError_t launch_t(const AttnArgs &a, int m, bool paged, hipStream_t st) {
     constexpr int NT = AttnShape<G>::threads;
@@ -770,10 +849,19 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
     b.sink = sp ? sp->sink : nullptr;
     b.out = out;
     b.out_q8 = out_q8;
-    if (hd == 64)
+    // at most 32 chunks per sequence: the one-wavefront merge (measured
+    // faster there; with more chunks its serial loads cost more than the
+    // barriers of the workgroup merge save)
+    if (plan.nchunks <= kMerge1Chunks) {
+        if (hd == 64)
+            hipLaunchKernelGGL(k_attn_merge1<64>, dim3(H, m), dim3(kWave), 0, st, b);
+        else
+            hipLaunchKernelGGL(k_attn_merge1<128>, dim3(H, m), dim3(kWave), 0, st, b);
+    } else if (hd == 64) {
         hipLaunchKernelGGL(k_attn_merge<64>, dim3(H, m), dim3(kMergeThreads), 0, st, b);
-    else
+    } else {
         hipLaunchKernelGGL(k_attn_merge<128>, dim3(H, m), dim3(kMergeThreads), 0, st, b);
+    }
     return hipGetLastError();
 }
 
