@@ -384,12 +384,15 @@ def recorded_traffic(kernel: str, workload: str, launches_bytes=None):
     csrc = os.path.join(ROOT, "decode_step_attention_layer_amd", "csrc")
     h = hashlib.sha256()
     src_file = {"k_attn_merge": "k_attn"}.get(kernel, kernel) + ".hip"
+    # the merge runs as k_attn_merge1 (one wavefront) when a sequence has at
+    # most 32 chunks: either record stands for it
+    names = ("k_attn_merge", "k_attn_merge1") if kernel == "k_attn_merge" else (kernel,)
     for f in (src_file, "ck_device.hpp", "ck_internal.hpp", "ck_gemv_common.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     src = h.hexdigest()[:16]
     for r in rec["records"]:
-        if r["kernel"] == kernel and r["workload"] == workload and r["src"] == src:
+        if r["kernel"] in names and r["workload"] == workload and r["src"] == src:
             return round(r["fetch_kib"] * 1024 * rec["fetch_scale"] +
                          r["write_kib"] * 1024 * rec["write_scale"])
     return None
