@@ -135,48 +135,78 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
     const size_t row_bytes = (size_t)nb * (Q5 ? kQ5Bytes : kQ8Bytes);
     const int row0 = tile * kTileRows;
 
-    // 1. every phase's weight dwords, coalesced: flat index f over
-    // [16 rows][n_p block pairs][words] of the phase
-    uint32_t raw[St::nph][St::per_lane];
+    // The loads go out in the order their values are needed, the weights
+    // unconditionally (the memory counter retires loads in issue order, and a
+    // load under a branch makes the compiler wait early for it and for every
+    // load issued before it): the activation blocks of this thread (up to
+    // two, when the batch has at most 2 * kMT blocks), the output thread's
+    // bias and residual, then every phase's weight dwords.
+    const int nxb = m * nb;
+    const bool xpre = nxb <= 2 * kMT;
+    uint32_t xr[2][9];
 #pragma unroll
-    for (int p = 0; p < St::nph; p++) {
-        const int pb = u0 + p * St::pu;
-        const int np = max(0, min(St::pu, uend - pb));
-        const int ndw = np * St::words;
+    for (int q = 0; q < 2; q++) {
+        const int b = min(tid + q * kMT, nxb - 1);
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)b * kQ8Bytes);
+        xr[q][0] = src[0];
 #pragma unroll
-        for (int i = 0; i < St::per_lane; i++) {
-            const int f = lane + kWave * i;
-            raw[p][i] = 0;
-            if (ndw > 0 && f < kTileRows * ndw) {
-                const int r = f / ndw, d = f - r * ndw;
-                if (row0 + r < sg.rows)
-                    raw[p][i] = *reinterpret_cast<const uint32_t *>(
-                        sg.W + (size_t)(row0 + r) * row_bytes + (size_t)pb * (2 * (Q5 ? kQ5Bytes : kQ8Bytes)) +
-                        4 * (size_t)d);
-            }
-        }
+        for (int i = 0; i < 8; i++)
+            xr[q][1 + i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
     }
-    // the output thread's bias and residual go out with the weights
     const int otok = tid / kTileRows, orow = row0 + tid % kTileRows;
     const bool writer = tid < m * kTileRows && orow < sg.rows;
     const float bias_o = (writer && sg.bias) ? sg.bias[orow] : 0.0f;
     const float res_o = (writer && sg.residual) ? sg.residual[(size_t)otok * sg.rows + orow] : 0.0f;
 
+    // every phase's weight dwords, coalesced: flat index f over [16 rows]
+    // [St::pu block pairs][words] of the phase; rows past the matrix re-read
+    // its last row and dwords past the row its last dword (neither reaches
+    // LDS or an output)
+    constexpr int kPh = St::pu * St::words;
+    const size_t pair_bytes = 2 * (Q5 ? kQ5Bytes : kQ8Bytes);
+    uint32_t raw[St::nph][St::per_lane];
+#pragma unroll
+    for (int p = 0; p < St::nph; p++) {
+        const int pb = u0 + p * St::pu;
+#pragma unroll
+        for (int i = 0; i < St::per_lane; i++) {
+            const int f = min(lane + kWave * i, kTileRows * kPh - 1);
+            const int r = f / kPh, d = f - r * kPh;
+            const int row = min(row0 + r, sg.rows - 1);
+            const size_t off = min((size_t)pb * pair_bytes + 4 * (size_t)d, row_bytes - 4);
+            raw[p][i] = *reinterpret_cast<const uint32_t *>(sg.W + (size_t)row * row_bytes + off);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // 2. the activations of all m tokens into LDS (codes, scale, code sum)
-    for (int b = tid; b < m * nb; b += kMT) {
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)b * kQ8Bytes);
+    auto put_x = [&](int b, const uint32_t *w) {
         XBlock xb;
-        xb.d = half_bits_to_float(src[0]);
+        xb.d = half_bits_to_float(w[0]);
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const uint32_t c = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
-            xb.c[i] = (int)c;
-            sum = __builtin_amdgcn_sdot4((int)c, 0x01010101, sum, false);
+            xb.c[i] = (int)w[1 + i];
+            sum = __builtin_amdgcn_sdot4((int)w[1 + i], 0x01010101, sum, false);
         }
         xb.sum = sum;
         xb.pad[0] = xb.pad[1] = 0;
         xs[b] = xb;
+    };
+    if (xpre) {
+#pragma unroll
+        for (int q = 0; q < 2; q++)
+            if (tid + q * kMT < nxb) put_x(tid + q * kMT, xr[q]);
+    } else {
+        for (int b = tid; b < nxb; b += kMT) {
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)b * kQ8Bytes);
+            uint32_t w[9];
+            w[0] = src[0];
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                w[1 + i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+            put_x(b, w);
+        }
     }
     __syncthreads();
 
@@ -190,14 +220,11 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
         const int pb = u0 + p * St::pu;
         const int np = max(0, min(St::pu, uend - pb));
         if (np == 0) break;
-        const int ndw = np * St::words;
 #pragma unroll
         for (int i = 0; i < St::per_lane; i++) {
             const int f = lane + kWave * i;
-            if (f < kTileRows * ndw) {
-                const int r = f / ndw, d = f - r * ndw;
-                reg[r * St::stride + d] = raw[p][i];
-            }
+            const int r = f / kPh, d = f - r * kPh;
+            if (f < kTileRows * kPh && d < np * St::words) reg[r * St::stride + d] = raw[p][i];
         }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
