@@ -26,10 +26,12 @@
 // (running max, sum, unnormalized output slice). No LDS staging and no
 // barrier inside the token loop. At the end the row groups' states are
 // combined by log-sum-exp through LDS into the chunk's (max, sum,
-// unnormalized output) per head, the partials. A second kernel, one
-// workgroup per (head, sequence), merges the chunks by log-sum-exp with all
-// chunks' loads in flight at once (the sink joins here), writes the attention
-// output and, optionally, its Q8_0 blocks. (Merging inside the first kernel
+// unnormalized output) per head, the partials. Chunks of 256 tokens or more
+// stream K/V with non-temporal loads (each row is read once). A second
+// kernel, one workgroup per (head, sequence) (one wavefront where a sequence
+// has at most 32 chunks), merges the chunks by log-sum-exp with all chunks'
+// loads in flight at once (the sink joins here), writes the attention output
+// and, optionally, its Q8_0 blocks. (Merging inside the first kernel
 // by the last workgroup to finish needs an agent-scope release per
 // workgroup, an L2 write-back on this GPU; measured, it cost more than the
 // kernel boundary.)

@@ -16,7 +16,8 @@
 // rows before any arithmetic, keeps them in registers and reuses them for all
 // m tokens. The quantized activations are staged once per workgroup into LDS
 // in a dword-aligned form (codes, scale as fp32, code sum for the Q5_0 offset)
-// while the weight loads are in flight.
+// while the weight loads are in flight (for one token, their loads are issued
+// before the weights').
 // Partial sums are reduced across the LPR lanes with DPP / ds_swizzle.
 #include "ck_device.hpp"
 #include "ck_gemv_common.hpp"

@@ -14,11 +14,11 @@
 //
 // Workgroup: 8 waves on one tile of 16 rows; wave w takes an eighth of the
 // rows' block pairs, loads them with coalesced dword loads (all before any
-// arithmetic) and redistributes them to the MFMA lane layout through its own
-// LDS region, in phases of 4 Q5_0 (2 Q8_0) block pairs; the activations are
-// staged in LDS once per workgroup (codes, scale, code sum), and the 8 partial
-// sums of each (token, row) are added through LDS in wave order
-// (deterministic).
+// arithmetic, after the activation blocks) and redistributes them to the MFMA
+// lane layout through its own LDS region, in phases of 4 Q5_0 (2 Q8_0) block
+// pairs; the activations are staged in LDS once per workgroup (codes, scale,
+// code sum) while the weights are in flight, and the 8 partial sums of each
+// (token, row) are added through LDS in wave order (deterministic).
 #include "ck_device.hpp"
 #include "ck_gemv_common.hpp"
 #include "ck_internal.hpp"
