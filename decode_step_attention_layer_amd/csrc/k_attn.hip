@@ -28,10 +28,10 @@
 // combined by log-sum-exp through LDS into the chunk's (max, sum,
 // unnormalized output) per head, the partials. Chunks of 256 tokens or more
 // stream K/V with non-temporal loads (each row is read once). A second
-// kernel, one workgroup per (head, sequence) (one wavefront where a sequence
-// has at most 32 chunks), merges the chunks by log-sum-exp with all chunks'
-// loads in flight at once (the sink joins here), writes the attention output
-// and, optionally, its Q8_0 blocks. (Merging inside the first kernel
+// kernel, one workgroup per (head, sequence) (one or two wavefronts where a
+// sequence has at most 64 chunks), merges the chunks by log-sum-exp with all
+// chunks' loads in flight at once (the sink joins here), writes the attention
+// output and, optionally, its Q8_0 blocks. (Merging inside the first kernel
 // by the last workgroup to finish needs an agent-scope release per
 // workgroup, an L2 write-back on this GPU; measured, it cost more than the
 // kernel boundary.)
@@ -655,41 +655,47 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
 // global max and the denominator are wave reductions; each chunk's weight
 // is computed by lane c and read from it into scalar registers; the lane
 // groups' sums are combined with cross-lane exchanges.
-constexpr int kMerge1Chunks = 32;
+constexpr int kMerge1Chunks = 32;   // chunks per wavefront
 
-template <int HD>
-__global__ __launch_bounds__(kWave) void k_attn_merge1(MergeArgs a) {
+// NWV wavefronts: wave w merges chunks [32w, 32w + 32) as above into its own
+// (max, denominator, weighted sum); with two waves the states are combined by
+// log-sum-exp through LDS after one barrier.
+template <int HD, int NWV>
+__global__ __launch_bounds__(kWave * NWV) void k_attn_merge1(MergeArgs a) {
     constexpr int LG = HD / 4;                 // lanes per chunk group
     constexpr int NGRP = kWave / LG;           // chunk groups
     constexpr int PER = kMerge1Chunks / NGRP;  // chunk slots per lane
-    const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+    const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x & (kWave - 1);
+    const int wave = NWV > 1 ? (int)(threadIdx.x >> 6) : 0;
     const int G = a.H / a.KV, g = h / G, j = h % G;
     const int L = a.pos.get(s) + 1;
     const int n = a.topk > 0 ? (L > 0 ? a.topk : 0) : L - window_start(L, a.window);
-    const int nc = (n + a.chunk - 1) / a.chunk;
-    const int ncl = nc > 0 ? nc - 1 : 0;
+    const int nc_all = (n + a.chunk - 1) / a.chunk;
+    const int c0 = wave * kMerge1Chunks;                       // this wave's first chunk
+    const int nc = min(max(nc_all - c0, 0), kMerge1Chunks);    // and its count
+    const int ncl = nc_all > 0 ? nc_all - 1 : 0;               // last valid chunk
     const size_t base = ((size_t)s * a.KV + g) * a.nchunks;
     const float sk = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     const int d4 = lane % LG, grp = lane / LG;
 
     const float2 ml =
-        *reinterpret_cast<const float2 *>(&a.pml[((base + min(lane, ncl)) * G + j) * 2]);
+        *reinterpret_cast<const float2 *>(&a.pml[((base + min(c0 + lane, ncl)) * G + j) * 2]);
     float4 ov[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) {
-        const int c = min(grp + NGRP * i, ncl);
+        const int c = min(c0 + grp + NGRP * i, ncl);
         ov[i] = *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
     }
     __builtin_amdgcn_sched_barrier(0);
 
     const bool mine = lane < nc;
-    const float M = fmaxf(wave_max(mine ? ml.x : -INFINITY), sk);
+    // one wave: the sink joins the max here; two: after the combination
+    const float Mw = fmaxf(wave_max(mine ? ml.x : -INFINITY), NWV == 1 ? sk : -INFINITY);
     // no attended row and no sink (a selection of absent entries): the
     // weights are zero and so is the output
-    const float Mr = M == -INFINITY ? 0.0f : M;
+    const float Mr = Mw == -INFINITY ? 0.0f : Mw;
     const float w = mine ? exp2f(ml.x - Mr) : 0.0f;
     float D = wave_sum(mine ? w * ml.y : 0.0f);
-    if (a.sink) D += exp2f(sk - Mr);
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -713,6 +719,35 @@ __global__ __launch_bounds__(kWave) void k_attn_merge1(MergeArgs a) {
         acc.y += __shfl_xor(acc.y, sh);
         acc.z += __shfl_xor(acc.z, sh);
         acc.w += __shfl_xor(acc.w, sh);
+    }
+    if constexpr (NWV == 1) {
+        if (a.sink) D += exp2f(sk - Mr);
+    } else {
+        // the waves' states: (max, denominator, weighted sum) relative to
+        // their own max, combined by log-sum-exp with the sink
+        __shared__ float4 sacc[NWV][LG];
+        __shared__ float smd[NWV][2];
+        if (grp == 0) sacc[wave][d4] = acc;
+        if (lane == 0) {
+            smd[wave][0] = Mw;
+            smd[wave][1] = D;
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        float M = sk;
+#pragma unroll
+        for (int v = 0; v < NWV; v++) M = fmaxf(M, smd[v][0]);
+        const float Mt = M == -INFINITY ? 0.0f : M;
+        D = a.sink ? exp2f(sk - Mt) : 0.0f;
+        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int v = 0; v < NWV; v++) {
+            const float sc = smd[v][0] == -INFINITY ? 0.0f : exp2f(smd[v][0] - Mt);
+            D = fmaf(sc, smd[v][1], D);
+            const float4 t = sacc[v][d4];
+            acc = make_float4(fmaf(sc, t.x, acc.x), fmaf(sc, t.y, acc.y), fmaf(sc, t.z, acc.z),
+                              fmaf(sc, t.w, acc.w));
+        }
     }
     if (grp == 0) {
         // D == 0: nothing attended and no sink, the output is zero; a NaN D
@@ -894,14 +929,20 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
     b.sink = sp ? sp->sink : nullptr;
     b.out = out;
     b.out_q8 = out_q8;
-    // at most 32 chunks per sequence: the one-wavefront merge (measured
-    // faster there; with more chunks its serial loads cost more than the
-    // barriers of the workgroup merge save)
+    // at most 32 chunks per sequence: the one-wavefront merge; up to 64: two
+    // wavefronts, 32 chunks each (measured faster than the workgroup merge
+    // at 22 and 43 chunks, neutral at 57; one wavefront for 43 or 57 chunks
+    // measured slower: its serial loads cost more than the barriers save)
     if (plan.nchunks <= kMerge1Chunks) {
         if (hd == 64)
-            hipLaunchKernelGGL(k_attn_merge1<64>, dim3(H, m), dim3(kWave), 0, st, b);
+            hipLaunchKernelGGL((k_attn_merge1<64, 1>), dim3(H, m), dim3(kWave), 0, st, b);
         else
-            hipLaunchKernelGGL(k_attn_merge1<128>, dim3(H, m), dim3(kWave), 0, st, b);
+            hipLaunchKernelGGL((k_attn_merge1<128, 1>), dim3(H, m), dim3(kWave), 0, st, b);
+    } else if (plan.nchunks <= 2 * kMerge1Chunks) {
+        if (hd == 64)
+            hipLaunchKernelGGL((k_attn_merge1<64, 2>), dim3(H, m), dim3(2 * kWave), 0, st, b);
+        else
+            hipLaunchKernelGGL((k_attn_merge1<128, 2>), dim3(H, m), dim3(2 * kWave), 0, st, b);
     } else if (hd == 64) {
         hipLaunchKernelGGL(k_attn_merge<64>, dim3(H, m), dim3(kMergeThreads), 0, st, b);
     } else {
