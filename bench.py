@@ -128,7 +128,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X "
-              "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+              "(sharding the layer across GPUs is not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
