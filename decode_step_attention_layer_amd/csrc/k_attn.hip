@@ -26,8 +26,9 @@
 // (running max, sum, unnormalized output slice). No LDS staging and no
 // barrier inside the token loop. At the end the row groups' states are
 // combined by log-sum-exp through LDS into the chunk's (max, sum,
-// unnormalized output) per head, the partials. Chunks of 256 tokens or more
-// stream K/V with non-temporal loads (each row is read once). A second
+// unnormalized output) per head, the partials. K/V rows stream with
+// non-temporal loads (each row is read once), except in short chunks of
+// large query groups with 128-wide heads. A second
 // kernel, one workgroup per (head, sequence) (one or two wavefronts where a
 // sequence has at most 64 chunks), merges the chunks by log-sum-exp with all
 // chunks' loads in flight at once (the sink joins here), writes the attention
@@ -760,17 +761,19 @@ __global__ __launch_bounds__(kWave * NWV) void k_attn_merge1(MergeArgs a) {
     }
 }
 
-constexpr int kNtChunk = 256;   // tokens per chunk from which K/V loads are non-temporal
+constexpr int kNtChunk = 256;   // chunks this long always stream (see launch_t)
 
 template <int HD, int G>
 hipError_t launch_t(const AttnArgs &a, int m, bool paged, hipStream_t st) {
     constexpr int NT = AttnShape<G>::threads;
     const dim3 grid(a.first[m], a.c.kv_heads);
     const int dt = a.c.dtype;
-    // long chunks stream K/V with non-temporal loads (measured: 47.9 against
-    // 55.5 us for 32,769 tokens x 8 KV heads); short chunks keep plain loads
-    // (at the 7B shape the step measured faster with them)
-    const bool nt = a.chunk >= kNtChunk;
+    // K/V rows stream with non-temporal loads (measured: 47.9 against 55.5
+    // us for 32,769 tokens x 8 KV heads; 9.7 against 10.6 us for a 4096-token
+    // window). The exception is short chunks of large query groups with
+    // 128-wide heads, where the streaming variant takes 11 more registers
+    // and measured slower per step (the 7B shape, 96-token chunks).
+    const bool nt = a.chunk >= kNtChunk || !(HD == 128 && G > 4);
 #define CK_ATTN_LAUNCH(P, D)                                                                   \
     do {                                                                                       \
         if (nt) hipLaunchKernelGGL((k_attn<HD, G, P, D, true>), grid, dim3(NT), 0, st, a);     \
