@@ -1,16 +1,21 @@
 """GPU parity of the whole decode layer (ck_decode_layer) against the oracle,
 at the five workloads' full sizes and in the configuration the benchmark times.
 
-Per layer, with the oracle run on the same input the GPU layer received:
-  * out and the attention output within 2e-3 x RMS (the required layer-output bound);
-    the normalized input differs from the oracle's only in its last bits, so
-    every Q8_0 code of xq that differs must be a rounding-boundary flip (off
-    by one, both scaled values within 1% of a quantum of the boundary); the
-    branch (out - residual) error is reported;
+Per layer (parity.check_layer), with the oracle run on the same input the GPU
+layer received:
   * stage by stage on identical inputs (the GPU's own intermediates read back
     from the workspace): xn within 1e-5, Q8_0 bytes of xn and of the attention
     output bit-exact, q/k/v within 1e-5, attention within 1e-4, O projection
     within 1e-5 of the branch RMS plus two ulps of the output;
+  * out and the attention output within 2e-3 x RMS of the plain oracle (the
+    required layer-output bound); every Q8_0 code of xq, and of the attention
+    output against the oracle run from the GPU's xq codes, that differs must
+    be a rounding-boundary flip (off by one, both scaled values within 1% of
+    a quantum of the boundary);
+  * the branch (out - residual) within 2e-3 x RMS(branch) of the oracle run
+    from the GPU's xq codes, plus for each counted aq flip the movement it
+    causes through Wo (|Wo[e, j]| times the code step), and of the plain
+    oracle, plus the oracle-evaluated effect of the xq flips;
   * every KV-cache slot except the appended one is byte-identical (NaN poison
     included), and the appended slot holds exactly the k, v the layer computed.
 The persistent variant runs here as one-layer persistent steps (the same
@@ -26,6 +31,7 @@ import pytest
 
 import oracle
 from decode_step_attention_layer_amd import synth
+import parity
 from gpu_helpers import assert_close_rms, cuda, host, rms
 
 pytestmark = pytest.mark.gpu
@@ -60,23 +66,14 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
     desc = stack.desc(variant, attn_chunk)
     ws = stack.workspace(desc)
     ws.fill_(0xFF)                       # NaN poison for any read of unwritten workspace
-    off = {n: ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, n)
-           for n in ("xn", "xq", "q", "k", "v", "attn", "aq")}
     m, D, H, KV, hd = cfg.m, cfg.D, cfg.H, cfg.KV, cfg.hd
     dims = dict(D=D, H=H, KV=KV, hd=hd, m=m, eps=cfg.eps)
     cos, sin = synth.rope_for(cfg)
     pos = stack.pos
-
-    def ocache(L, k, v):
-        if cfg.page_size:
-            return oracle.Cache(k, v, KV, hd, page_size=cfg.page_size,
-                                page_table=L.host["table"],
-                                max_pages_per_seq=cfg.max_pages_per_seq, num_pages=k.shape[0])
-        return oracle.Cache(k, v, KV, hd, capacity=cfg.capacity)
+    read = ws_reader(ck, desc, stack.max_ctx, ws, cfg)
 
     x_gpu_in = stack.x0
     x_host = stack.x0_host.copy()            # GPU chain input, host copy
-    x_orc = stack.x0_host.copy()             # independent oracle chain
     for li, L in enumerate(stack.layers):
         print(f"{name} variant={variant} layer {li}", flush=True)
         out = stack.bufs[li % 2]
@@ -84,130 +81,60 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
         torch.cuda.synchronize()
         got = host(out)
         wts = dict(L.host, rope_cos=cos, rope_sin=sin)
-
-        oc = ocache(L, L.host["k"].copy(), L.host["v"].copy())
-        ref, tr = oracle.decode_layer(dims, wts, oc, x_host, x_host, pos, trace=True)
-        tag = f"{name} layer {li}"
-
-        # stage by stage on identical inputs (the GPU's own intermediates)
-        xn = _ws_read(ws, off["xn"], 4 * m * D, np.float32).reshape(m, D)
-        xq = _ws_read(ws, off["xq"], m * D // 32 * 34, np.uint8).reshape(m, -1)
-        gq = _ws_read(ws, off["q"], 4 * m * H * hd, np.float32).reshape(m, H * hd)
-        gkk = _ws_read(ws, off["k"], 4 * m * KV * hd, np.float32).reshape(m, KV * hd)
-        gvv = _ws_read(ws, off["v"], 4 * m * KV * hd, np.float32).reshape(m, KV * hd)
-        at = _ws_read(ws, off["attn"], 4 * m * H * hd, np.float32).reshape(m, H * hd)
-        aq = _ws_read(ws, off["aq"], m * H * hd // 32 * 34, np.uint8).reshape(m, -1)
-        gk, gv = host(L.tensors["k"]), host(L.tensors["v"])
-        gcache = ocache(L, gk, gv)
-        for s in range(m):
-            xs = x_host[s]
-            assert_close_rms(xn[s], oracle.rmsnorm(xs, wts["gamma"], cfg.eps), 1e-5, tag + " xn")
-            assert np.array_equal(xq[s], oracle.quantize_q8_0(xn[s])), tag + " xq bytes"
-            q0 = oracle.gemv_q5_0(wts["wq"], xq[s], wts["bq"], None, H * hd, D)
-            k0 = oracle.gemv_q5_0(wts["wk"], xq[s], wts["bk"], None, KV * hd, D)
-            v0 = oracle.gemv_q8_0(wts["wv"], xq[s], wts["bv"], None, KV * hd, D)
-            q1, k1 = oracle.rope(q0, k0, cos, sin, pos[s], H, KV, hd)
-            assert_close_rms(gq[s], q1, 1e-5, tag + " q")
-            assert_close_rms(gkk[s], k1, 1e-5, tag + " k")
-            assert_close_rms(gvv[s], v0, 1e-5, tag + " v")
-            a0 = oracle.attention(gq[s], gcache, s, pos[s] + 1, H)
-            assert_close_rms(at[s], a0, 1e-4, tag + " attention")
-            assert np.array_equal(aq[s], oracle.quantize_q8_0(at[s])), tag + " aq bytes"
-            o0 = oracle.gemv_q5_0(wts["wo"], aq[s], wts["bo"], xs, D, H * hd)
-            # 1e-5 of the branch for the dot, plus the rounding of out = x + branch
-            # at the output's magnitude (two fp32 ulps)
-            bound = 1e-5 * rms(o0.astype(np.float64) - xs) + 2 * np.spacing(np.abs(o0))
-            assert np.all(np.abs(got[s].astype(np.float64) - o0) <= bound), tag + " O projection"
-
-        # oracle on the GPU's own input (an independently rounded pipeline):
-        # the output and the attention output within the 2e-3 layer-output bound;
-        # the normalized input differs only in its last bits, so every xq code
-        # that differs from the oracle's must be a rounding-boundary flip. A
-        # flip shifts q, k, v by about one quantum of one input, so downstream
-        # values (attention, its Q8_0 codes, the branch) legitimately differ by
-        # more than last bits; their exactness is the stage-by-stage check above.
-        assert_close_rms(got, ref, TOL, tag + " out")
-        nflip = 0
-        for s in range(m):
-            nflip += _check_flips(xq[s], tr["xq"][s], xn[s], tr["xn"][s], tag + " xq")
-            assert_close_rms(at[s], tr["attn"][s], TOL, tag + " attention (independent)")
-        br = assert_close_rms(got - x_host, ref - x_host, 1.0, tag + " branch")
-        print(f"{tag}: xq boundary flips {nflip}, branch rel err {br:.2e}")
-
-        # the cache: only the appended slot changed, and it holds this token's k, v
-        for gc, oc_arr, orig in ((gk, oc.k, L.host["k"]), (gv, oc.v, L.host["v"])):
-            appended = ~((oc_arr == orig) | (np.isnan(oc_arr) & np.isnan(orig)))
-            assert appended.sum() == m * KV * hd, tag + " oracle appended slot count"
-            assert np.array_equal(gc.view(np.uint32)[~appended],
-                                  orig.view(np.uint32)[~appended]), \
-                tag + " cache: a slot other than the appended one changed"
-            assert_close_rms(gc[appended], oc_arr[appended], TOL, tag + " appended k/v")
-        for s in range(m):
-            for g in range(KV):
-                row = gcache_row(cfg, L, s, g, pos[s])
-                assert np.array_equal(gk.reshape(-1)[row:row + hd], gkk[s, g * hd:(g + 1) * hd])
-                assert np.array_equal(gv.reshape(-1)[row:row + hd], gvv[s, g * hd:(g + 1) * hd])
-
-        # independent oracle chain for the end-to-end check
-        oc2 = ocache(L, L.host["k"].copy(), L.host["v"].copy())
-        x_orc = oracle.decode_layer(dims, wts, oc2, x_orc, x_orc, pos)
+        st = parity.check_layer(cfg, wts, lambda k, v: ocache(cfg, L, k, v), L.host["k"],
+                                L.host["v"], x_host, got, read(), host(L.tensors["k"]),
+                                host(L.tensors["v"]), pos,
+                                lambda s, g: gcache_row(cfg, L, s, g, pos[s]),
+                                f"{name} layer {li}")
+        print(f"{name} layer {li}: xq flips {st['xq_flips']}, aq flips {st['aq_flips']}, "
+              f"branch rel err {st['branch_cond']:.2e} (conditioned) / "
+              f"{st['branch_pure']:.2e} (plain oracle)")
         x_host = got
         x_gpu_in = out
-    # End to end over a stack, the bound is the oracle's own rounding-noise
-    # floor: the oracle chained again with every layer input nudged by +-1 ulp
-    # (the size of fp32 reassociation differences) diverges from itself by this
-    # much, because nudged values cross Q8_0 rounding boundaries in every layer.
-    bound = TOL
+    # End to end over a stack, against the independent oracle chain: the
+    # bound is the oracle's own rounding-noise floor, how far the oracle
+    # chained with every layer input nudged by +-1 ulp (the size of fp32
+    # reassociation differences) diverges from itself, because nudged values
+    # cross Q8_0 rounding boundaries in every layer.
+    def layer_fn(l, x):
+        Ll = stack.layers[l]
+        return oracle.decode_layer(dims, dict(Ll.host, rope_cos=cos, rope_sin=sin),
+                                   ocache(cfg, Ll, Ll.host["k"].copy(), Ll.host["v"].copy()),
+                                   x, x, pos)
+
     if len(stack.layers) > 1:
-        floor = _noise_floor(stack, dims, cos, sin, ocache, x_orc)
+        floor, x_orc = parity.nudged_floor(layer_fn, stack.x0_host, len(stack.layers))
         bound = max(TOL, 3.0 * floor)
         print(f"{name}: oracle +-1 ulp noise floor over {len(stack.layers)} layers {floor:.2e}")
+    else:
+        x_orc, bound = layer_fn(0, stack.x0_host.copy()), TOL
     e2e = assert_close_rms(x_host, x_orc, bound, f"{name} end to end")
     print(f"{name} variant={variant}: layers={len(stack.layers)} e2e rel err {e2e:.2e} "
           f"(bound {bound:.2e}, branch RMS {rms(x_orc - stack.x0_host):.3f})")
 
 
-def _q8_parts(b):
-    b = np.ascontiguousarray(b).reshape(-1, 34)
-    d = b[:, :2].copy().view("<f2")[:, 0].astype(np.float64)
-    return d, b[:, 2:].view(np.int8).astype(np.int64)
+def ocache(cfg, L, k, v):
+    if cfg.page_size:
+        return oracle.Cache(k, v, cfg.KV, cfg.hd, page_size=cfg.page_size,
+                            page_table=L.host["table"], max_pages_per_seq=cfg.max_pages_per_seq,
+                            num_pages=k.shape[0])
+    return oracle.Cache(k, v, cfg.KV, cfg.hd, capacity=cfg.capacity)
 
 
-def _check_flips(gpu_bytes, orc_bytes, gpu_vals, orc_vals, tag):
-    """Q8_0 blocks from two pipelines whose fp32 inputs differ in the last
-    bits: scales may differ by one binary16 step, codes by one, and only where
-    both pipelines' scaled values sit within 1% of a quantum of the rounding
-    boundary. Returns the number of differing codes."""
-    dg, qg = _q8_parts(gpu_bytes)
-    do, qo = _q8_parts(orc_bytes)
-    step = np.spacing(np.maximum(dg, do).astype(np.float16)).astype(np.float64)
-    assert np.all(np.abs(dg - do) <= step), tag + ": scale differs by more than one fp16 step"
-    assert np.abs(qg - qo).max(initial=0) <= 1, tag + ": a code differs by more than one"
-    vg = np.asarray(gpu_vals, np.float64).reshape(-1, 32)
-    vo = np.asarray(orc_vals, np.float64).reshape(-1, 32)
-    ag = np.abs(vg).max(axis=1, keepdims=True)
-    ao = np.abs(vo).max(axis=1, keepdims=True)
-    sg = np.where(ag > 0, vg * 127.0 / np.where(ag > 0, ag, 1), 0.0)
-    so = np.where(ao > 0, vo * 127.0 / np.where(ao > 0, ao, 1), 0.0)
-    flip = qg != qo
-    if flip.any():
-        assert np.all(np.abs(sg - so)[flip] < 0.01), tag + ": flip from a large value difference"
-        frac = np.abs(so[flip]) - np.floor(np.abs(so[flip]))
-        assert np.all(np.abs(frac - 0.5) < 0.01), tag + ": flip away from a rounding boundary"
-    return int(flip.sum())
+def ws_reader(ck, desc, max_ctx, ws, cfg):
+    """A function returning the layer intermediates kept in the workspace
+    (offsets from ck_decode_layer_ws_offset), as [m][...] host arrays."""
+    m, D, H, KV, hd = cfg.m, cfg.D, cfg.H, cfg.KV, cfg.hd
+    off = {n: ck.ck_decode_layer_ws_offset(desc, max_ctx, n)
+           for n in ("xn", "xq", "q", "k", "v", "attn", "aq")}
+    sizes = dict(xn=(4 * m * D, np.float32), xq=(m * D // 32 * 34, np.uint8),
+                 q=(4 * m * H * hd, np.float32), k=(4 * m * KV * hd, np.float32),
+                 v=(4 * m * KV * hd, np.float32), attn=(4 * m * H * hd, np.float32),
+                 aq=(m * H * hd // 32 * 34, np.uint8))
 
-
-def _noise_floor(stack, dims, cos, sin, ocache, x_clean):
-    g = np.random.default_rng(1234)
-    x = stack.x0_host.copy()
-    for L in stack.layers:
-        up = g.random(x.shape) < 0.5
-        x = np.where(up, np.nextafter(x, np.float32(np.inf)),
-                     np.nextafter(x, np.float32(-np.inf))).astype(np.float32)
-        c = ocache(L, L.host["k"].copy(), L.host["v"].copy())
-        x = oracle.decode_layer(dims, dict(L.host, rope_cos=cos, rope_sin=sin), c, x, x,
-                                stack.pos)
-    return float(np.max(np.abs(x.astype(np.float64) - x_clean))) / rms(x_clean)
+    def read():
+        return {n: _ws_read(ws, off[n], nb, dt).reshape(m, -1) for n, (nb, dt) in sizes.items()}
+    return read
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)

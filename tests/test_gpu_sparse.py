@@ -3,7 +3,9 @@ the oracle.
 
   * ck_attn_sparse on contiguous, paged and ring caches, one to four
     sequences, selections with duplicates and -1 padding, with and without a
-    sink: within 1e-4 x RMS of the oracle per sequence;
+    sink: within 1e-4 x RMS of the oracle per sequence; also with selections
+    split into more than 64 chunks (the workgroup merge, with and without a
+    sink);
   * with a fixed split, padding a selection with -1 (even whole chunks of it)
     changes nothing, bit for bit, and the selection of every token in order
     without a sink is the dense attention, bit for bit;
@@ -140,6 +142,38 @@ def test_sparse_attention(layout, m, H, KV, hd, pos, topk, R, with_sink):
         assert_close_rms(got[s], ref, 1e-4, f"{layout} sparse s={s}")
 
 
+MANY_CHUNK_CASES = [
+    # layout, m, H, KV, hd, positions, topk, chunk, sink: more than 64 chunks
+    # per sequence (the workgroup merge), past its first 16 preloaded slots per
+    # thread (16 x 8 chunks for 128-wide heads, 16 x 16 for 64-wide)
+    ("contig", 1, 28, 4, 128, [9000], 8000, 48, True),
+    ("contig", 1, 8, 2, 64, [20000], 18000, 64, True),
+    ("paged", 2, 32, 8, 128, [5000, 3000], 4500, 64, False),
+]
+
+
+@pytest.mark.parametrize("layout,m,H,KV,hd,pos,topk,chunk,with_sink", MANY_CHUNK_CASES, ids=str)
+def test_sparse_attention_many_chunks(layout, m, H, KV, hd, pos, topk, chunk, with_sink):
+    """Selections split into more chunks than the one- and two-wavefront
+    merges take: the workgroup merge, with and without a sink, against the
+    oracle within 1e-4."""
+    from decode_step_attention_layer_amd import ck
+
+    dev = cuda()
+    print(f"sparse many chunks {layout} m={m} H={H} hd={hd} topk={topk} chunk={chunk}", flush=True)
+    k, v, table, oc, geo = _build(layout, m, KV, hd, pos, 0, topk + chunk)
+    c, keep = _dev(ck, dev, KV, hd, k, v, table, geo)
+    g = np.random.default_rng(topk + 7)
+    sel = _selection(g, pos, topk)
+    q = synth.seeded_vector(topk + 3, m * H * hd)
+    sink = (g.standard_normal(H) * 2).astype(np.float32) if with_sink else None
+    got = _sparse(ck, dev, c, q, pos, sel, sink, m, H, KV, hd, chunk=chunk)
+    for s in range(m):
+        ref = oracle.attention_sparse(q[s * H * hd:(s + 1) * H * hd], oc, s, pos[s] + 1, H, sel[s],
+                                      sink)
+        assert_close_rms(got[s], ref, 1e-4, f"{layout} sparse many chunks s={s}")
+
+
 def test_padding_is_inert_and_full_selection_is_dense():
     import torch
     from decode_step_attention_layer_amd import ck
@@ -238,14 +272,17 @@ def test_sparse_decode_layer(name, topk, variant, steps):
 
 def test_graph_sparse_decode_loop():
     """The captured step reads its position and selection from device memory,
-    rewritten between replays; it equals the eager host-position steps."""
+    rewritten between replays; it equals the eager host-position steps, and at
+    every replayed step the output matches the oracle's sparse layer on a cache
+    of its own (appended at every step) within 2e-3, and only the appended slot
+    changed, holding what the oracle appended there."""
     import torch
     from decode_step_attention_layer_amd import ck
     from decode_step_attention_layer_amd.workload import DeviceStack
 
     dev = cuda()
     cfg = synth.CONFIGS["c2"]
-    a = DeviceStack(cfg, dev, layers=1)
+    a = DeviceStack(cfg, dev, layers=1, keep_host=True)
     b = a.clone()
     desc = a.desc(ck.CK_VARIANT_FUSED, attn_chunk=64)
     topk, steps = 80, 4
@@ -255,7 +292,8 @@ def test_graph_sparse_decode_loop():
     ws_b = torch.empty_like(ws_a)
     g = np.random.default_rng(5)
     sels = [_selection(g, [cfg.pos + i], topk) for i in range(steps)]
-    sink = _t(g.standard_normal(cfg.H).astype(np.float32), dev)
+    sink_h = g.standard_normal(cfg.H).astype(np.float32)
+    sink = _t(sink_h, dev)
     sel_dev = _t(sels[0], dev)
     pos_dev = torch.tensor([cfg.pos], dtype=torch.int32, device=dev)
     La, Lb = a.layers[0], b.layers[0]
@@ -270,8 +308,14 @@ def test_graph_sparse_decode_loop():
     torch.cuda.synchronize()
     with torch.cuda.graph(gr):
         step_b()
+    cos, sin = synth.rope_for(cfg)
+    wts = dict(La.host, rope_cos=cos, rope_sin=sin)
+    dims = dict(D=cfg.D, H=cfg.H, KV=cfg.KV, hd=cfg.hd, m=cfg.m, eps=cfg.eps)
+    oc = oracle.Cache(La.host["k"].copy(), La.host["v"].copy(), cfg.KV, cfg.hd,
+                      capacity=cfg.capacity)
     for i in range(steps):
         print(f"sparse graph replay {i}", flush=True)
+        kb, vb = host(Lb.tensors["k"]).copy(), host(Lb.tensors["v"]).copy()
         p = cfg.pos + i
         ref = torch.empty_like(out_b)
         ck.ck_decode_layer_sparse(desc, La.weights, La.cache, a.x0, a.x0, _t(sels[i], dev), topk,
@@ -281,6 +325,17 @@ def test_graph_sparse_decode_loop():
         gr.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_b, ref), f"replay {i} differs from the eager step"
+        tag = f"sparse graph replay {i} at {p}"
+        x_orc = oracle.decode_layer(dims, wts, oc, a.x0_host, a.x0_host, [p], sel=sels[i],
+                                    sink=sink_h)
+        assert_close_rms(host(out_b), x_orc, 2e-3, tag + " out")
+        for n_, x0_, o_ in (("k", kb, oc.k), ("v", vb, oc.v)):
+            x1_ = host(Lb.tensors[n_])
+            mask = np.zeros(x1_.shape, bool)
+            mask[0, :, p] = True
+            assert np.array_equal(x0_[~mask].view(np.uint32), x1_[~mask].view(np.uint32)), \
+                tag + f" {n_}: a slot other than the appended one changed"
+            assert_close_rms(x1_[mask], o_[mask], 2e-3, tag + f" {n_} appended slot")
     for n in ("k", "v"):
         assert np.array_equal(host(La.tensors[n]).view(np.uint32),
                               host(Lb.tensors[n]).view(np.uint32))

@@ -4,29 +4,30 @@ workload in one call), in the three variants.
   * chain and fused: bit-identical to the same variant called layer by layer
     through ck_decode_layer (the same kernels, verified stage by stage in
     test_gpu_layer.py);
-  * persistent (every layer in one persistent kernel): status word zero; end to
-    end against the independent oracle chain within max(2e-3, 3 x the chain's
-    rounding-noise floor) x RMS (the floor: the larger deviation of the oracle
-    chained with +-1-ulp nudged inputs and of the verified fused GPU chain,
-    from the oracle chain); the last
-    layer's intermediates left in the workspace checked stage by stage on the
-    GPU's own inputs (xq bytes exact, attention within 1e-4, its Q8_0 bytes
-    exact); every cache slot other than the appended ones byte-identical, and
-    the appended slots of every layer within max(2e-3, 3 x the same floor
-    taken for k and v over the layers up to that one, 3 x one code flip) of
-    the oracle chain's. One code flip: a rounding difference anywhere upstream
-    can move one Q8_0 code of a layer's quantized input by one, which moves
-    every appended k (v) element by up to max|W_k| (max|W_v|) times that
-    block's scale; the floor estimates need not happen to contain a flip
-    where the persistent chain has one;
+  * persistent (every layer in one persistent kernel): for n = 1 .. layers,
+    the step over the first n layers (one launch each) leaves layer n-1's
+    intermediates in the workspace, and that layer is checked stage by stage
+    on the GPU's own input (the output of the n-1 step) exactly as the layer
+    tests check a layer (parity.check_layer): xn, q/k/v, attention, O within
+    their per-op bounds, xq and aq bytes exact, the branch against the oracle
+    run from the GPU's xq codes plus the counted aq flips' effect, against
+    the plain oracle plus the xq flips' oracle-evaluated effect, out within
+    2e-3, only the appended cache slots changed; re-running a prefix
+    re-appends identical bytes; status word zero. End to end the step over
+    every layer matches the independent oracle chain within
+    max(2e-3, 3 x the oracle's own noise floor), the floor taken from the
+    oracle alone (its chain with +-1-ulp nudged layer inputs, two seeds);
   * two persistent steps in a row at successive positions: the second attends
     over the row the first appended, checked against the oracle on the GPU's
     own caches and input.
 """
+import hashlib
+
 import numpy as np
 import pytest
 
 import oracle
+import parity
 from decode_step_attention_layer_amd import synth
 from gpu_helpers import assert_close_rms, cuda, host, rms
 
@@ -47,77 +48,34 @@ def _dims(cfg):
     return dict(D=cfg.D, H=cfg.H, KV=cfg.KV, hd=cfg.hd, m=cfg.m, eps=cfg.eps)
 
 
-def _oracle_chain(stack, x0, nudge_seed=None):
-    """The oracle through every layer from x0 on fresh copies of the original
-    caches; with nudge_seed, every layer input is first moved by +-1 ulp.
-    Returns the output, per layer the appended (k, v) slots, and per layer
-    the largest Q8_0 block scale of the layer's quantized input."""
-    cfg = stack.cfg
-    cos, sin = synth.rope_for(cfg)
-    g = np.random.default_rng(nudge_seed) if nudge_seed is not None else None
-    x = x0.copy()
-    appended, dmax = [], []
-    for L in stack.layers:
-        if g is not None:
-            up = g.random(x.shape) < 0.5
-            x = np.where(up, np.nextafter(x, np.float32(np.inf)),
-                         np.nextafter(x, np.float32(-np.inf))).astype(np.float32)
-        xq = np.concatenate([oracle.quantize_q8_0(oracle.rmsnorm(r, L.host["gamma"], cfg.eps))
-                             for r in x])
-        dmax.append(float(np.max(np.abs(_block_scales(xq, 34)))))
-        c = _ocache(cfg, L, L.host["k"].copy(), L.host["v"].copy())
-        x = oracle.decode_layer(_dims(cfg), dict(L.host, rope_cos=cos, rope_sin=sin), c, x, x,
-                                stack.pos)
-        mask = _appended_mask(cfg, L, stack.pos)
-        appended.append((c.k.reshape(-1)[mask].copy(), c.v.reshape(-1)[mask].copy()))
-    return x, appended, dmax
-
-
-def _block_scales(blocks, nbytes):
-    """The binary16 scales (first two bytes) of Q8_0 (34-byte) or Q5_0
-    (22-byte) blocks."""
-    b = np.ascontiguousarray(blocks, np.uint8).reshape(-1, nbytes)
-    return b[:, :2].copy().view("<f2")[:, 0].astype(np.float64)
-
-
-def _max_weight(packed, q5):
-    """An upper bound of |w| over a Q5_0 (|code - 16| <= 16) or Q8_0
-    (|code| <= 128) weight matrix: the largest block scale times the code."""
-    return float(np.max(np.abs(_block_scales(packed, 22 if q5 else 34)))) * (16 if q5 else 128)
-
-
-def _rel_dev(a, b):
-    return float(np.max(np.abs(np.asarray(a, np.float64) - b))) / rms(b)
-
-
-def _appended_mask(cfg, L, pos):
-    """Boolean masks over the flattened cache of the slots a step appends."""
-    k = L.host["k"]
-    mask = np.zeros(k.size, bool)
+def _slot_row(cfg, L, s, g, t):
     hd, KV = cfg.hd, cfg.KV
-    for s in range(cfg.m):
-        for g in range(KV):
-            t = pos[s]
-            if cfg.page_size:
-                page = int(L.host["table"][s, t // cfg.page_size])
-                row = ((page * KV + g) * cfg.page_size + t % cfg.page_size) * hd
-            else:
-                row = ((s * KV + g) * cfg.capacity + t) * hd
-            mask[row:row + hd] = True
-    return mask
+    if cfg.page_size:
+        page = int(L.host["table"][s, t // cfg.page_size])
+        return ((page * KV + g) * cfg.page_size + t % cfg.page_size) * hd
+    return ((s * KV + g) * cfg.capacity + t) * hd
+
+
+def _digest(*arrays):
+    h = hashlib.sha1()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).view(np.uint8))
+    return h.hexdigest()
 
 
 def _step_check(name, layers=None):
     import torch
     from decode_step_attention_layer_amd import ck
     from decode_step_attention_layer_amd.workload import DeviceStack
+    from test_gpu_layer import ws_reader
 
     dev = cuda()
     cfg = synth.CONFIGS[name]
     stack = DeviceStack(cfg, dev, keep_host=True, spare_pages=4 if cfg.page_size else 0,
                         layers=layers)
-    m, D, H, hd = cfg.m, cfg.D, cfg.H, cfg.hd
-    tag = f"{name} x{stack.nlayers}"
+    nl = stack.nlayers
+    tag = f"{name} x{nl}"
+    cos, sin = synth.rope_for(cfg)
 
     # chain and fused: whole step == layer by layer, bit for bit
     for variant in (ck.CK_VARIANT_CHAIN, ck.CK_VARIANT_FUSED):
@@ -127,80 +85,58 @@ def _step_check(name, layers=None):
         torch.cuda.synchronize()
         assert torch.equal(whole, per_layer), f"{tag} variant {variant}: step != layer by layer"
         print(f"{tag} variant {variant}: whole step equals layer by layer", flush=True)
-    fused_out = host(whole)
-    fused_app = []
-    for L in stack.layers:
-        mask = _appended_mask(cfg, L, stack.pos)
-        fused_app.append((host(L.tensors["k"]).reshape(-1)[mask],
-                          host(L.tensors["v"]).reshape(-1)[mask]))
 
-    # persistent
+    # persistent: the step over the first n layers, n = 1 .. nl; the last
+    # layer of each checked stage by stage on the GPU's own input
     d = stack.desc(ck.CK_VARIANT_PERSISTENT)
     ws = stack.step_workspace(d)
     ws.fill_(0xFF)
-    print(f"{tag} persistent step", flush=True)
-    out = host(stack.decode_step(d, ws))
-    torch.cuda.synchronize()
-    assert stack.step_status(d, ws) == 0, f"{tag}: persistent step reported a timed-out wait"
+    read = ws_reader(ck, d, stack.max_ctx, ws, cfg)
+    w_all, c_all = stack.step_arrays()
+    out = torch.empty((cfg.m, cfg.D), dtype=torch.float32, device=dev)
+    x_in = stack.x0_host.copy()
+    digests = []
+    for n in range(1, nl + 1):
+        L = stack.layers[n - 1]
+        print(f"{tag} persistent step over {n} layers", flush=True)
+        ws.fill_(0xFF)
+        ck.ck_decode_step(d, [w_all[i] for i in range(n)], [c_all[i] for i in range(n)], stack.x0,
+                          stack.pos, out, ws, ws.numel())
+        torch.cuda.synchronize()
+        assert stack.step_status(d, ws) == 0, f"{tag} n={n}: a wait timed out"
+        got = host(out)
+        gk, gv = host(L.tensors["k"]), host(L.tensors["v"])
+        wts = dict(L.host, rope_cos=cos, rope_sin=sin)
+        st = parity.check_layer(cfg, wts, lambda k, v: _ocache(cfg, L, k, v), L.host["k"],
+                                L.host["v"], x_in, got, read(), gk, gv, stack.pos,
+                                lambda s, g: _slot_row(cfg, L, s, g, stack.pos[s]),
+                                f"{tag} persistent layer {n - 1}")
+        print(f"{tag} persistent layer {n - 1}: xq flips {st['xq_flips']}, aq flips "
+              f"{st['aq_flips']}, branch rel err {st['branch_cond']:.2e} / "
+              f"{st['branch_pure']:.2e}", flush=True)
+        digests.append(_digest(gk, gv))
+        x_in = got
+    # every later prefix re-appended the same bytes into the earlier layers
+    for i, L in enumerate(stack.layers):
+        assert _digest(host(L.tensors["k"]), host(L.tensors["v"])) == digests[i], \
+            f"{tag}: layer {i} cache changed when a longer step re-ran it"
 
-    # Bounds for a chain of layers: 3 x the rounding noise two independent
-    # estimates show, never below 2e-3: the oracle chained against itself with
-    # +-1-ulp nudged layer inputs, and the fused GPU chain (verified layer by
-    # layer, stage by stage) against the oracle chain. For the appended k and
-    # v of layer l, the larger deviation over layers 0..l (the noise only
-    # accumulates down the chain).
-    x_orc, app_orc, dmax = _oracle_chain(stack, stack.x0_host)
-    bound = TOL
-    kv_bounds = [(TOL, TOL)] * stack.nlayers
-    if stack.nlayers > 1:
-        x_nud, app_nud, _ = _oracle_chain(stack, stack.x0_host, 1234)
-        floor = max(_rel_dev(x_nud, x_orc), _rel_dev(fused_out, x_orc))
+    # end to end against the independent oracle chain; the bound from the
+    # oracle's own +-1-ulp noise floor only
+    def layer_fn(l, x):
+        Ll = stack.layers[l]
+        return oracle.decode_layer(_dims(cfg), dict(Ll.host, rope_cos=cos, rope_sin=sin),
+                                   _ocache(cfg, Ll, Ll.host["k"].copy(), Ll.host["v"].copy()),
+                                   x, x, stack.pos)
+
+    if nl > 1:
+        floor, x_orc = parity.nudged_floor(layer_fn, stack.x0_host, nl)
         bound = max(TOL, 3.0 * floor)
-        kv_bounds, fk, fv = [], 0.0, 0.0
-        for L, dq, (kn, vn), (kf, vf), (ko, vo) in zip(stack.layers, dmax, app_nud, fused_app,
-                                                       app_orc):
-            fk = max(fk, _rel_dev(kn, ko), _rel_dev(kf, ko))
-            fv = max(fv, _rel_dev(vn, vo), _rel_dev(vf, vo))
-            flip_k = _max_weight(L.host["wk"], True) * dq / rms(ko)
-            flip_v = _max_weight(L.host["wv"], False) * dq / rms(vo)
-            kv_bounds.append((max(TOL, 3.0 * fk, 3.0 * flip_k), max(TOL, 3.0 * fv, 3.0 * flip_v)))
-        print(f"{tag}: chain noise floor {floor:.2e}; one-flip k/v bound of the last layer "
-              f"{kv_bounds[-1][0]:.2e} / {kv_bounds[-1][1]:.2e}", flush=True)
-    e2e = assert_close_rms(out, x_orc, bound, f"{tag} persistent end to end")
-    rel_fused = assert_close_rms(out, fused_out, bound, f"{tag} persistent vs fused")
-    print(f"{tag} persistent: e2e rel err {e2e:.2e}, vs fused {rel_fused:.2e} (bound {bound:.2e})")
-
-    # the last layer's intermediates, on the GPU's own inputs
-    off = {n: ck.ck_decode_layer_ws_offset(d, stack.max_ctx, n)
-           for n in ("xn", "xq", "q", "attn", "aq")}
-
-    def rd(n, nbytes, dt):
-        return ws[off[n]: off[n] + nbytes].cpu().numpy().view(dt)
-
-    xn = rd("xn", 4 * m * D, np.float32).reshape(m, D)
-    xq = rd("xq", m * D // 32 * 34, np.uint8).reshape(m, -1)
-    gq = rd("q", 4 * m * H * hd, np.float32).reshape(m, H * hd)
-    at = rd("attn", 4 * m * H * hd, np.float32).reshape(m, H * hd)
-    aq = rd("aq", m * H * hd // 32 * 34, np.uint8).reshape(m, -1)
-    Ll = stack.layers[-1]
-    gcache = _ocache(cfg, Ll, host(Ll.tensors["k"]), host(Ll.tensors["v"]))
-    for s in range(m):
-        assert np.array_equal(xq[s], oracle.quantize_q8_0(xn[s])), f"{tag} last-layer xq bytes"
-        a0 = oracle.attention(gq[s], gcache, s, stack.pos[s] + 1, H)
-        assert_close_rms(at[s], a0, 1e-4, f"{tag} last-layer attention")
-        assert np.array_equal(aq[s], oracle.quantize_q8_0(at[s])), f"{tag} last-layer aq bytes"
-
-    # caches: only the appended slots changed; those match the oracle chain's
-    # within that layer's noise-floor bound
-    for li, L in enumerate(stack.layers):
-        mask = _appended_mask(cfg, L, stack.pos)
-        for j, (name_, orig) in enumerate((("k", L.host["k"]), ("v", L.host["v"]))):
-            got = host(L.tensors[name_]).reshape(-1)
-            orig = orig.reshape(-1)
-            assert np.array_equal(got.view(np.uint32)[~mask], orig.view(np.uint32)[~mask]), \
-                f"{tag} layer {li} {name_}: a slot other than the appended one changed"
-            assert_close_rms(got[mask], app_orc[li][j], kv_bounds[li][j],
-                             f"{tag} layer {li} appended {name_}")
+    else:
+        x_orc, bound, floor = layer_fn(0, stack.x0_host.copy()), TOL, 0.0
+    e2e = assert_close_rms(x_in, x_orc, bound, f"{tag} persistent end to end")
+    print(f"{tag} persistent: e2e rel err {e2e:.2e} (bound {bound:.2e}, oracle floor "
+          f"{floor:.2e})")
 
 
 def test_step_c1():

@@ -20,6 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
+import parity
 from decode_step_attention_layer_amd import synth
 from gpu_helpers import assert_close_rms, cuda, host
 
@@ -268,14 +269,18 @@ def test_layer_decode_loop_with_window(name, W, ring, steps, variant):
 @pytest.mark.parametrize("name,W,layers", [("c1", 8, None), ("c2", 64, 2)])
 def test_graph_decode_loop_on_a_ring(name, W, layers):
     """A captured step with device positions, replayed across the ring's wrap,
-    equals the eager host-position steps byte for byte."""
+    equals the eager host-position steps byte for byte; at every replayed step
+    the output matches the oracle's own decode loop on ring caches of its own
+    at that step's positions (within max(2e-3, 3 x the oracle's +-1-ulp noise
+    floor)), and only the slots pos % W changed, holding what the oracle
+    loop appended there."""
     import torch
     from decode_step_attention_layer_amd import ck
     from decode_step_attention_layer_amd.workload import DeviceStack
 
     dev = cuda()
     steps = W + 3 if W <= 8 else 6
-    a = DeviceStack(synth.CONFIGS[name], dev, layers=layers, window=W, ring=True)
+    a = DeviceStack(synth.CONFIGS[name], dev, layers=layers, window=W, ring=True, keep_host=True)
     b = a.clone()
     desc = a.desc(ck.CK_VARIANT_FUSED, attn_chunk=64)
     pos0 = list(a.pos)
@@ -292,13 +297,34 @@ def test_graph_decode_loop_on_a_ring(name, W, layers):
     with torch.cuda.graph(g):
         ck.ck_decode_step_devpos(desc, wts, cs, b.x0, pos_dev, max_ctx, out_b, ws_b, ws_b.numel())
         pos_dev.add_(1)
+    cfg = a.cfg
+    cos, sin = synth.rope_for(cfg)
+
+    def mk(l, k, v):
+        return oracle.Cache(k, v, cfg.KV, cfg.hd, capacity=W, ring=True, window=W)
+
+    orc = parity.OracleLoop(cfg, [L.host for L in a.layers], cos, sin, mk)
     for step in range(steps):
         print(f"{name} ring W={W} replay {step}", flush=True)
         a.pos = [p + step for p in pos0]
         ref = a.decode_step(desc, ws_a, out=torch.empty_like(out_b)).clone()
+        before = [(host(L.tensors["k"]).copy(), host(L.tensors["v"]).copy()) for L in b.layers]
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_b, ref), f"{name} step {step}: replay differs from the eager step"
+        tag = f"{name} ring W={W} replay {step} at {a.pos}"
+        x_orc, floor = orc.step(a.x0_host, a.pos)
+        bound = max(2e-3, 3.0 * floor)
+        assert_close_rms(host(out_b), x_orc, bound, tag + " out")
+        slot = a.pos[0] % W
+        for l, (L, (kb, vb), oc) in enumerate(zip(b.layers, before, orc.caches)):
+            for n_, x0_, o_ in (("k", kb, oc.k), ("v", vb, oc.v)):
+                x1_ = host(L.tensors[n_])
+                mask = np.zeros(x1_.shape, bool)
+                mask[0, :, slot] = True
+                assert np.array_equal(x0_[~mask].view(np.uint32), x1_[~mask].view(np.uint32)), \
+                    tag + f" layer {l} {n_}: a slot other than pos % W changed"
+                assert_close_rms(x1_[mask], o_[mask], bound, tag + f" layer {l} {n_} slot")
     for La, Lb in zip(a.layers, b.layers):
         for n in ("k", "v"):
             assert np.array_equal(host(La.tensors[n]).view(np.uint32),
