@@ -103,7 +103,9 @@ def _step_check(name, layers=None):
         ck.ck_decode_step(d, [w_all[i] for i in range(n)], [c_all[i] for i in range(n)], stack.x0,
                           stack.pos, out, ws, ws.numel())
         torch.cuda.synchronize()
-        assert stack.step_status(d, ws) == 0, f"{tag} n={n}: a wait timed out"
+        soff = ck.ck_decode_step_status_offset(d, n)      # the status word of an n-layer step
+        assert int(ws[soff:soff + 4].view(torch.int32).item()) == 0, \
+            f"{tag} n={n}: a wait timed out"
         got = host(out)
         gk, gv = host(L.tensors["k"]), host(L.tensors["v"])
         wts = dict(L.host, rope_cos=cos, rope_sin=sin)
