@@ -232,8 +232,10 @@ __device__ void qkv_item(const Ctx &cx, int item, XBlock *xs, float *red, int *f
         if (!wait_ge(prev + 2, (unsigned)a.no_items, cx.abort_word, flag)) return;
     }
     const float *xin = cx.l == 0 ? a.x : a.xbuf + (size_t)((cx.l - 1) & 1) * a.m * D;
-    // the first item of the layer also leaves xn and xq in the workspace
-    const bool trace = item == 0;
+    // the last layer's first item also leaves xn and xq in the workspace
+    // (one writer only: two workgroups of different XCDs writing the same
+    // lines with plain stores would leave whichever L2 writes back last)
+    const bool trace = item == 0 && cx.l == a.L - 1;
     for (int s = 0; s < a.m; s++)
         norm_quant_c(xin + (size_t)s * D, cx.l > 0, ly.gamma, D, a.eps, red, xs + s * nb,
                      trace ? a.xn + (size_t)s * D : nullptr,
