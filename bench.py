@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=sorted(DESCRIBE))
-    ap.add_argument("--variant", default="fused", choices=["fused", "chain", "persistent"])
+    ap.add_argument("--variant", default="fused",
+                    choices=["fused", "chain", "persistent", "two_launch"])
     ap.add_argument("--kv", default="f32", choices=["f32", "bf16", "fp8"],
                     help="KV-cache element type (fp8: E4M3 with one scale per tensor)")
     ap.add_argument("--window", type=int, default=0,
@@ -141,7 +142,8 @@ def main():
     ck.load()
     cfg = synth.CONFIGS[args.config]
     variant = {"fused": ck.CK_VARIANT_FUSED, "chain": ck.CK_VARIANT_CHAIN,
-               "persistent": ck.CK_VARIANT_PERSISTENT}[args.variant]
+               "persistent": ck.CK_VARIANT_PERSISTENT,
+               "two_launch": ck.CK_VARIANT_TWO_LAUNCH}[args.variant]
     persistent = variant == ck.CK_VARIANT_PERSISTENT
     t0 = time.time()
     kv_dtype = {"f32": synth.KV_F32, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}[args.kv]

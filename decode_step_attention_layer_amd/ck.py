@@ -24,6 +24,7 @@ CK_MAX_SEQS = 16
 CK_VARIANT_CHAIN = 0
 CK_VARIANT_FUSED = 1
 CK_VARIANT_PERSISTENT = 2
+CK_VARIANT_TWO_LAUNCH = 3
 CK_MAX_STEP_LAYERS = 32
 CK_KV_F32 = 0
 CK_KV_BF16 = 1
@@ -36,7 +37,7 @@ EXPORTS = (
     "ck_decode_layer",
     "ck_decode_layer_ws_offset", "ck_decode_step_workspace_size", "ck_decode_step",
     "ck_decode_step_status_offset", "ck_decode_layer_devpos", "ck_decode_step_devpos",
-    "ck_attn_sparse", "ck_decode_layer_sparse",
+    "ck_attn_sparse", "ck_decode_layer_sparse", "ck_decode_layer_part",
 )
 
 
@@ -105,6 +106,8 @@ def load():
         "ck_decode_layer_workspace_size": ([ctypes.POINTER(CkLayerDesc), I], S),
         "ck_decode_layer": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                              ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, P], I),
+        "ck_decode_layer_part": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
+                                  ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, I, P], I),
         "ck_decode_layer_ws_offset": ([ctypes.POINTER(CkLayerDesc), I, ctypes.c_char_p],
                                       ctypes.c_long),
         "ck_decode_step_workspace_size": ([ctypes.POINTER(CkLayerDesc), I, I], S),
@@ -250,6 +253,14 @@ def ck_decode_layer(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache
     _check(load().ck_decode_layer(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(cache),
                                   _ptr(x), _ptr(residual), _pos(pos), _ptr(out), _ptr(ws),
                                   ws_bytes, _stream(stream)), "ck_decode_layer")
+
+
+def ck_decode_layer_part(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache, x, residual,
+                         pos, out, ws, ws_bytes, part, stream=None):
+    _check(load().ck_decode_layer_part(ctypes.byref(desc), ctypes.byref(weights),
+                                       ctypes.byref(cache), _ptr(x), _ptr(residual), _pos(pos),
+                                       _ptr(out), _ptr(ws), ws_bytes, int(part), _stream(stream)),
+           "ck_decode_layer_part")
 
 
 def ck_decode_step_workspace_size(desc: CkLayerDesc, layers: int, max_ctx: int) -> int:

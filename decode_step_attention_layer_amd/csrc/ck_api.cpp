@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "../../include/ck.h"
+#include "ck_gemv_common.hpp"
 #include "ck_internal.hpp"
 
 using namespace ck;
@@ -18,6 +19,7 @@ bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 int hip_rc(hipError_t e) { return e == hipSuccess ? CK_OK : CK_EHIP; }
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 
 // Validates the cache descriptor and builds the kernel view.
 int cache_view(const ck_kv_cache *kv, CacheView *out) {
@@ -127,7 +129,7 @@ hipError_t gemv_any(const GemvArgs &g, hipStream_t st) {
 }
 
 struct WsLayout {
-    size_t xn, xq, q, k, v, attn, aq, part, total;
+    size_t xn, xq, q, k, v, attn, aq, aqx, cnt, part, total;
 };
 
 WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
@@ -142,6 +144,10 @@ WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
     w.v = o; o = up256(o + sizeof(float) * m * KD);
     w.attn = o; o = up256(o + sizeof(float) * m * HD);
     w.aq = o; o = up256(o + m * (HD / CK_QK) * CK_Q8_0_BYTES);
+    // the two-launch variant: the staged Q8_0 blocks of the attention output
+    // and the counters of its second launch (the status word last)
+    w.aqx = o; o = up256(o + m * (HD / CK_QK) * sizeof(XBlock));
+    w.cnt = o; o = up256(o + sizeof(unsigned) * ato_counter_words(d->m, d->KV));
     const int maxc = attn_max_chunks(d->KV, d->H / d->KV, max_ctx, d->attn_chunk);
     w.part = o; o = up256(o + attn_partials_bytes(d->m, d->H, d->head_dim, maxc));
     w.total = o;
@@ -155,7 +161,7 @@ int check_desc(const ck_layer_desc *d) {
     if (d->D % CK_QK || (d->H * d->head_dim) % CK_QK || d->head_dim % 2 || d->H % d->KV)
         return CK_EINVAL;
     if (d->variant != CK_VARIANT_CHAIN && d->variant != CK_VARIANT_FUSED &&
-        d->variant != CK_VARIANT_PERSISTENT)
+        d->variant != CK_VARIANT_PERSISTENT && d->variant != CK_VARIANT_TWO_LAUNCH)
         return CK_EINVAL;
     if (d->attn_chunk < 0 || !(d->eps >= 0.0f)) return CK_EINVAL;
     if (!attn_shape_supported(d->H / d->KV, d->head_dim)) return CK_EUNSUPPORTED;
@@ -391,9 +397,13 @@ long ck_decode_step_status_offset(const ck_layer_desc *desc, int layers) {
 
 namespace {
 
+// phases: 1 = steps 1-6 (RMSNorm through the KV append; q, k, v left in the
+// workspace), 2 = steps 7-8 (attention through the O projection, from them),
+// 3 = the whole layer.
 int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                       const float *x, const float *residual, const PosIn &pin, float *out,
-                      void *ws, size_t ws_bytes, void *stream, const SparseSel *sp = nullptr);
+                      void *ws, size_t ws_bytes, void *stream, const SparseSel *sp = nullptr,
+                      int phases = 3);
 
 int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                      int layers, const float *x, const PosIn &pin, float *out, void *ws,
@@ -551,6 +561,10 @@ long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const cha
         return -1;
     }
     WsLayout w = ws_layout(desc, max_ctx);
+    if (!strcmp(name, "status"))
+        return desc->variant == CK_VARIANT_TWO_LAUNCH
+                   ? (long)(w.cnt + sizeof(unsigned) * ato_status_word(desc->m, desc->KV))
+                   : -1;
     if (!strcmp(name, "xn")) return (long)w.xn;
     if (!strcmp(name, "xq")) return (long)w.xq;
     if (!strcmp(name, "q")) return (long)w.q;
@@ -567,10 +581,11 @@ namespace {
 
 int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                       const float *x, const float *residual, const PosIn &pin, float *out,
-                      void *ws, size_t ws_bytes, void *stream, const SparseSel *sp) {
+                      void *ws, size_t ws_bytes, void *stream, const SparseSel *sp, int phases) {
     int rc = check_desc(desc);
     if (rc) return rc;
-    if (sp && desc->variant == CK_VARIANT_PERSISTENT) return CK_EUNSUPPORTED;
+    if (phases < 1 || phases > 3) return CK_EINVAL;
+    if ((sp || phases != 3) && desc->variant == CK_VARIANT_PERSISTENT) return CK_EUNSUPPORTED;
     if (desc->variant == CK_VARIANT_PERSISTENT) {
         // a one-layer persistent step; its residual is its input
         if (residual != x) return CK_EINVAL;
@@ -615,16 +630,27 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     uint8_t *aq = base + L.aq;
     void *part = base + L.part;
     const int HD = d.H * d.head_dim, KD = d.KV * d.head_dim;
-    const bool fused = d.variant == CK_VARIANT_FUSED;
+    const float scale = 1.0f / sqrtf((float)d.head_dim);
+    // the two-launch layer: Q/K/V (clearing the counters of the second
+    // launch), then attention + merge + O in one launch; selections and
+    // shapes it does not take run as the fused variant
+    const bool two = d.variant == CK_VARIANT_TWO_LAUNCH && !sp &&
+                     ato_supported(d.H, d.head_dim, plan.nchunks);
+    const bool fused = d.variant == CK_VARIANT_FUSED || d.variant == CK_VARIANT_TWO_LAUNCH;
+    unsigned *cnt = reinterpret_cast<unsigned *>(base + L.cnt);
+    const int ncnt = two ? ato_counters(d.m, d.KV) : 0;
+    const int zstride = ato_counter_stride();
 
     hipError_t e;
-    if (fused && qkv_shape_supported(d.D, d.m)) {
+    if (!(phases & 1)) {
+        // steps 7-8 only: q, k and v are in the workspace already
+    } else if (fused && qkv_shape_supported(d.D, d.m)) {
         // steps 1-6 in one kernel: RMSNorm, Q8_0, Q/K/V projections + bias,
         // RoPE, KV append
         e = launch_qkv(x, w->gamma, d.eps, d.D, d.H, d.KV, d.head_dim, d.m,
                        static_cast<const uint8_t *>(w->wq), static_cast<const uint8_t *>(w->wk),
                        static_cast<const uint8_t *>(w->wv), w->bq, w->bk, w->bv, w->rope_cos,
-                       w->rope_sin, p, c, q, k, v, xn, xq, st);
+                       w->rope_sin, p, c, q, k, v, xn, xq, st, cnt, ncnt, zstride);
         if (e != hipSuccess) return CK_EHIP;
     } else {
         // steps 1-2: RMSNorm and the one Q8_0 quantization shared by Q, K and V
@@ -651,7 +677,8 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
 
         // steps 5-6: RoPE on q and k, then the append of (k, v) at pos
         if (fused) {
-            e = launch_rope_append(q, k, v, w->rope_cos, w->rope_sin, c, p, d.m, d.H, st);
+            e = launch_rope_append(q, k, v, w->rope_cos, w->rope_sin, c, p, d.m, d.H, st, cnt,
+                                   ncnt, zstride);
         } else {
             e = launch_rope(q, k, w->rope_cos, w->rope_sin, p, d.m, d.H, d.KV, d.head_dim, st);
             if (e == hipSuccess) e = launch_kv_append(c, k, v, p, d.m, st);
@@ -659,9 +686,17 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
         if (e != hipSuccess) return CK_EHIP;
     }
 
+    if (!(phases & 2)) return CK_OK;
+    if (two) {
+        // steps 7-8 in one launch: attention, merge + Q8_0, O projection +
+        // bo + residual
+        return hip_rc(launch_ato(q, c, p, d.m, d.H, scale, plan, part, attn, aq, base + L.aqx,
+                                 static_cast<const uint8_t *>(w->wo), w->bo, residual, out, d.D,
+                                 cnt, st));
+    }
+
     // step 7: attention over pos + 1 tokens, or the selection (fused: the
     // merge also quantizes)
-    const float scale = 1.0f / sqrtf((float)d.head_dim);
     e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, plan, part, st, sp);
     if (e != hipSuccess) return CK_EHIP;
     if (!fused) {
@@ -702,6 +737,15 @@ int ck_decode_layer_sparse(const ck_layer_desc *desc, const ck_layer_weights *w,
     const SparseSel sp{sel, topk, sink};
     const PosIn pin = pos_host ? PosIn{pos_host, nullptr, 0} : PosIn{nullptr, pos_dev, max_ctx};
     return decode_layer_impl(desc, w, kv, x, residual, pin, out, ws, ws_bytes, stream, &sp);
+}
+
+int ck_decode_layer_part(const ck_layer_desc *desc, const ck_layer_weights *w,
+                         const ck_kv_cache *kv, const float *x, const float *residual,
+                         const int32_t *pos_host, float *out, void *ws, size_t ws_bytes, int part,
+                         void *stream) {
+    if (!pos_host || (part != 1 && part != 2)) return CK_EINVAL;
+    return decode_layer_impl(desc, w, kv, x, residual, PosIn{pos_host, nullptr, 0}, out, ws,
+                             ws_bytes, stream, nullptr, part);
 }
 
 int ck_decode_layer_devpos(const ck_layer_desc *desc, const ck_layer_weights *w,

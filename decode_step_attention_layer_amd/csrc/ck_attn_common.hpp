@@ -1,0 +1,501 @@
+// ck_attn_common.hpp — the split-K grouped-query decode attention item,
+// shared by the attention kernel (k_attn.hip) and the attention + merge + O
+// projection kernel (k_ato.hip): argument block, workgroup shape, per-lane
+// K/V row slices, the LDS state and the body that computes one chunk's
+// online-softmax partial for every query head of a KV head.
+//
+// What it computes (C-Kernel-Engine "mega_fused_attention_decode_q5_0.c",
+// MAIN KERNEL STEP 7): for query head h, KV head g = h*KV/H, tokens t <= pos,
+//   out_h = sum_t softmax_t(scale * q_h . K_g[t]) V_g[t],
+// split into chunks of tokens whose partials (running max in log2 units, sum
+// of exponentials, unnormalized output) a log-sum-exp pass merges.
+#pragma once
+
+#include <type_traits>
+
+#include "ck_device.hpp"
+#include "ck_internal.hpp"
+
+namespace ck {
+
+namespace attn {
+
+constexpr int kMaxG = 8;
+constexpr int kMaxChunks = 4096;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+    const float *q;       // [m][H][HD]
+    CacheView c;
+    Positions pos;
+    float scale;
+    int chunk;            // tokens per chunk, a multiple of the kernel's step
+    int nchunks;
+    int H;
+    float *po;            // [m][KV][nchunks][G][HD]  unnormalized outputs
+    float *pml;           // [m][KV][nchunks][G][2]   (max in log2 units, sum)
+    int m;
+    int first[kMaxSeqs + 1];  // first work item of each sequence; first[m] = items
+    // sparse attention (sel not null): sequence s attends the token positions
+    // sel[s*topk .. s*topk + topk) (-1 = absent) instead of its tokens; chunks
+    // then split the selection entries
+    const int32_t *sel;
+    int topk;
+};
+
+constexpr int kPagesLds = 512;   // page ids of a chunk staged in LDS
+constexpr int kSelLds = 1024;    // selection entries of a chunk staged in LDS
+// Workgroup shape: 4 waves; per step a wave loads 4 rows per round, 4 rounds
+// (a 64-token step), or 3 rounds (48 tokens) for large query groups, whose
+// per-lane accumulators leave fewer registers for loads. Two workgroups fit
+// a compute unit either way. The attention plan sizes chunks in whole steps.
+template <int G>
+struct AttnShape {
+    static constexpr int waves = 4;
+    static constexpr int rounds = G > 4 ? 3 : 4;
+    static constexpr int sub = rounds;              // rows per online-softmax batch
+    static constexpr int threads = waves * 64;
+    static constexpr int step = waves * 4 * rounds;
+};
+
+// How one wave holds K/V rows: a row is read by LPR lanes, F = HD/LPR
+// elements each, so one load round covers 64/LPR rows. fp32 rows of 128 are
+// read as two 16-byte pieces per lane (columns 4i.. and 64+4i..), so that one
+// load instruction covers 256 contiguous bytes of each of its rows; otherwise
+// a lane's F elements are contiguous (columns F*i..). fp8 rows use 8 lanes
+// where the query group is small (16 codes, one 16-byte load a lane), so that
+// a step holds twice the rows for the same load instructions: with a quarter
+// of fp32's bytes per row, the rows per step set the bytes in flight (bf16
+// would need 32 bytes a lane, more registers than two workgroups per CU
+// leave). WORDS: raw words per lane per row.
+template <int DT, int HD, int G>
+struct RowGeo {
+    static constexpr int EB = DT == CK_KV_F32 ? 4 : (DT == CK_KV_BF16 ? 2 : 1);
+    static constexpr int LPR = (DT == CK_KV_FP8_E4M3 && G <= 4) ? 8 : 16;
+    static constexpr int F = HD / LPR;
+    static constexpr int RPR = kWave / LPR;            // rows per load round
+    static constexpr int WORDS = F * EB / 4;
+    static constexpr bool SPLIT = DT == CK_KV_F32 && F == 8;
+};
+
+
+// One lane's slice of a K or V row.
+template <int DT, int HD, int G>
+struct Slice {
+    typedef RowGeo<DT, HD, G> Geo;
+    static constexpr int F = Geo::F;
+    static constexpr int EB = Geo::EB;
+    static constexpr int WORDS = Geo::WORDS;
+    uint32_t w[WORDS];
+
+    __device__ static __forceinline__ int col(int li, int e) {
+        if constexpr (Geo::SPLIT) return e < 4 ? 4 * li + e : 64 + 4 * li + (e - 4);
+        else return F * li + e;
+    }
+    // NT: non-temporal loads (the rows are read once; measured faster where
+    // the chunks are long and the kernel streams). The plain path keeps its
+    // own code: the vector-typed loads of the streaming path change the
+    // register allocation of the short-chunk kernels.
+    template <bool NT>
+    __device__ __forceinline__ void load(const void *base, long long off, int li) {
+        if constexpr (NT) {
+            typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+            auto ld4 = [](const void *q) { return __builtin_nontemporal_load(static_cast<const u4 *>(q)); };
+            if constexpr (Geo::SPLIT) {
+                const float *p = static_cast<const float *>(base) + off + 4 * li;
+                const u4 a = ld4(p);
+                const u4 b = ld4(p + 64);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+            } else {
+                const uint8_t *p = static_cast<const uint8_t *>(base) + (off + (long long)F * li) * EB;
+                if constexpr (WORDS == 8) {
+                    const u4 a = ld4(p);
+                    const u4 b = ld4(p + 16);
+                    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+                } else if constexpr (WORDS == 4) {
+                    const u4 a = ld4(p);
+                    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                } else if constexpr (WORDS == 2) {
+                    const u2 a = __builtin_nontemporal_load(reinterpret_cast<const u2 *>(p));
+                    w[0] = a.x; w[1] = a.y;
+                } else {
+                    static_assert(WORDS == 1, "slice size");
+                    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+                }
+            }
+        } else if constexpr (Geo::SPLIT) {
+            const float *p = static_cast<const float *>(base) + off + 4 * li;
+            const uint4 a = *reinterpret_cast<const uint4 *>(p);
+            const uint4 b = *reinterpret_cast<const uint4 *>(p + 64);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else {
+            const uint8_t *p = static_cast<const uint8_t *>(base) + (off + (long long)F * li) * EB;
+            if constexpr (WORDS == 8) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(p);
+                const uint4 b = *reinterpret_cast<const uint4 *>(p + 16);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+            } else if constexpr (WORDS == 4) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(p);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            } else if constexpr (WORDS == 2) {
+                const uint2 a = *reinterpret_cast<const uint2 *>(p);
+                w[0] = a.x; w[1] = a.y;
+            } else {
+                static_assert(WORDS == 1, "slice size");
+                w[0] = *reinterpret_cast<const uint32_t *>(p);
+            }
+        }
+    }
+    // fp32 values (fp8: the code values; the tensor's scale is applied by
+    // the caller, to q for K and to the output for V)
+    __device__ __forceinline__ void to_f32(float (&f)[F]) const {
+        if constexpr (DT == CK_KV_F32) {
+#pragma unroll
+            for (int e = 0; e < F; e++) f[e] = __uint_as_float(w[e]);
+        } else if constexpr (DT == CK_KV_BF16) {
+#pragma unroll
+            for (int i = 0; i < WORDS; i++) {
+                f[2 * i] = __uint_as_float(w[i] << 16);
+                f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        } else {
+            // v_cvt_pk_f32_fp8 decodes OCP E4M3 on gfx950 (checked against the
+            // format's definition over all 256 codes, NaN included)
+#pragma unroll
+            for (int i = 0; i < WORDS; i++) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+                f[4 * i] = lo[0];
+                f[4 * i + 1] = lo[1];
+                f[4 * i + 2] = hi[0];
+                f[4 * i + 3] = hi[1];
+            }
+        }
+    }
+};
+
+template <int HD, int G, int NS>
+struct Smem {
+    // the online-softmax state of every row group (NS of them): unnormalized
+    // outputs, running max (log2 units), sum of exponentials; then the
+    // weight of each state in the combination
+    float ro[NS][G][HD];
+    float rm[NS][G];
+    float rl[NS][G];
+    float rw[NS][G];
+    int pages[kPagesLds];                   // paged caches: the chunk's page ids
+    int sel[kSelLds];                       // sparse: the chunk's selection entries
+    int bad;
+};
+
+// Row groups of a workgroup (the states combined at the end of an item).
+template <int DT, int HD, int G>
+constexpr int kAttnNS = AttnShape<G>::waves * RowGeo<DT, HD, G>::RPR;
+
+// A partial's store: plain, or device-coherent (a relaxed agent-scope store:
+// written through to where workgroups of other XCDs read it in the same
+// launch).
+template <bool COH>
+__device__ __forceinline__ void part_store(float *p, float v) {
+    if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// One work item: the chunk `item` (counted over every sequence's chunks, back
+// to back) of KV head g. Each K/V row is held by a group of LPR lanes
+// (RowGeo), so a wave covers 64/LPR rows per load round and keeps its rows
+// in registers: no LDS staging and no barrier inside the token loop. Scores:
+// per lane the partial dot products of its slice with every query head of
+// the group (q slice in registers), summed over the row group with DPP.
+// Every row group keeps its own online softmax (running max, sum,
+// unnormalized output of its slice) over the rows it sees; at the end the
+// row groups' states are combined by log-sum-exp through LDS and the chunk's
+// partial is stored (COH: with device-coherent stores). Returns false, having
+// stored nothing, for an item past its sequence's chunks (device positions).
+template <int HD, int G, bool PAGED, int DT, bool STREAM, bool COH>
+__device__ __forceinline__ bool attn_item(const AttnArgs &a, int item, int g,
+                                          Smem<HD, G, kAttnNS<DT, HD, G>> &sm) {
+    static_assert(HD % 64 == 0 && G >= 1 && G <= kMaxG, "shape");
+    typedef Slice<DT, HD, G> SL;
+    typedef RowGeo<DT, HD, G> GEO;
+    constexpr int F = SL::F;
+    constexpr int LPR = GEO::LPR;
+    constexpr int RPR = GEO::RPR;
+    constexpr int NW = AttnShape<G>::waves;
+    constexpr int NT = AttnShape<G>::threads;
+    constexpr int NR = AttnShape<G>::rounds;
+    constexpr int WROWS = NR * RPR;                  // rows per wave per step
+    constexpr int STEP = WROWS * NW;                 // tokens per workgroup step
+    constexpr int NS = NW * RPR;                     // row groups of the workgroup
+    static_assert(NS == kAttnNS<DT, HD, G>, "state groups");
+
+    int s = 0;
+    while (s + 1 < a.m && item >= a.first[s + 1]) s++;
+    const int cidx = item - a.first[s];
+    const int L = a.pos.get(s) + 1;
+    const bool sparse = a.sel != nullptr;
+    // The chunk's rows [t0, t1): tokens, counted from the window's first token
+    // (0 without a window); sparse, the selection entries.
+    int t0, t1;
+    if (sparse) {
+        t0 = cidx * a.chunk;
+        if (t0 >= a.topk || L <= 0) return false;
+        t1 = min(a.topk, t0 + a.chunk);
+    } else {
+        t0 = window_start(L, a.c.window) + cidx * a.chunk;
+        if (t0 >= L) return false;   // device positions: items past this sequence's chunks
+        t1 = min(L, t0 + a.chunk);
+    }
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & (LPR - 1), rg = lane / LPR;
+    const int KV = a.c.kv_heads;
+
+    if (tid == 0) sm.bad = 0;
+    // paged: the chunk's page ids in one batch of loads, so that row
+    // addresses do not wait on table reads (chunks with more pages than the
+    // LDS slots read the table per row)
+    int pg0 = 0;
+    bool pages_in_lds = false;
+    if (PAGED && !sparse) {
+        const int ps = a.c.page_size;
+        pg0 = t0 / ps;
+        const int npg = (t1 - 1) / ps - pg0 + 1;
+        pages_in_lds = npg <= kPagesLds;
+        if (pages_in_lds)
+            for (int i = tid; i < npg; i += NT)
+                sm.pages[i] = a.c.table[(long long)s * a.c.max_pages + pg0 + i];
+    }
+    // sparse: the chunk's selection entries, read once
+    const int32_t *sel_s = sparse ? a.sel + (size_t)s * a.topk : nullptr;
+    const bool sel_in_lds = sparse && t1 - t0 <= kSelLds;
+    if (sel_in_lds)
+        for (int i = tid; i < t1 - t0; i += NT) sm.sel[i] = sel_s[t0 + i];
+    __syncthreads();
+
+    const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
+    bool bad = false;
+    // element offset of token t's row (t < t1); an unmapped page reads page 0
+    // of the pool and marks the chunk bad
+    auto row_off = [&](int t) -> long long {
+        if constexpr (PAGED) {
+            long long off = -1;
+            if (pages_in_lds) {
+                const int ps = a.c.page_size;
+                const int page = sm.pages[t / ps - pg0];
+                if (page >= 0 && page < a.c.num_pages)
+                    off = (((long long)page * KV + g) * ps + t % ps) * (long long)HD;
+            } else {
+                off = cache_row(a.c, s, g, t);
+            }
+            if (off < 0) bad = true;      // unmapped page: the sum becomes NaN
+            return off < 0 ? 0 : off;
+        } else {
+            // ring: slot t % capacity (t < L, so t is never negative)
+            const int slot = a.c.ring ? t % a.c.capacity : t;
+            return (long long)(seq_base + (size_t)slot * HD);
+        }
+    };
+    // Rows past the chunk re-read its last row (their scores are masked), so
+    // that every load is issued unconditionally: no branch around the loads
+    // and no wait on the loads still in flight. okbits: bit r set where row r
+    // is attended. Sparse: an absent entry (-1) reads the first row of the
+    // buffer and is masked; an entry past the sequence or no longer held by
+    // a ring marks the chunk bad.
+    uint32_t okbits = 0;
+    auto fetch = [&](SL (&k)[NR], SL (&v)[NR], int st) {
+        okbits = 0;
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            const int row = st + wave * WROWS + r * RPR + rg;
+            const int e = min(row, t1 - 1);
+            bool ok = row < t1;
+            long long off;
+            if (sparse) {
+                const int t = sel_in_lds ? sm.sel[e - t0] : sel_s[e];
+                bool held = t >= 0 && t < L;
+                if (!PAGED && a.c.ring) held = held && t >= L - a.c.capacity;
+                if (t >= 0 && !held) bad = true;
+                ok = ok && held;
+                off = held ? row_off(t) : (long long)seq_base;
+            } else {
+                off = row_off(e);
+            }
+            okbits |= (ok ? 1u : 0u) << r;
+            k[r].template load<STREAM>(a.c.k, off, li);
+            v[r].template load<STREAM>(a.c.v, off, li);
+        }
+    };
+
+    SL ka[NR], va[NR];
+    fetch(ka, va, t0);                               // first rows in flight before q
+
+    // the q slice of every head of the group, pre-scaled so that scores are
+    // in log2 units
+    float qr[G][F];
+    {
+        // fp8: the K scale folded in here (scores = q . (code * k_scale))
+        const float qs = a.scale * kLog2e * (DT == CK_KV_FP8_E4M3 ? a.c.k_scale : 1.0f);
+        const float *qg = a.q + ((size_t)s * a.H + (size_t)g * G) * HD;
+#pragma unroll
+        for (int j = 0; j < G; j++) {
+#pragma unroll
+            for (int e = 0; e < F; e += 4) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(qg + j * HD + SL::col(li, e));
+                qr[j][e] = v4.x * qs;
+                qr[j][e + 1] = v4.y * qs;
+                qr[j][e + 2] = v4.z * qs;
+                qr[j][e + 3] = v4.w * qs;
+            }
+        }
+    }
+
+    float m[G], l[G], o[G][F];
+#pragma unroll
+    for (int j = 0; j < G; j++) {
+        m[j] = -INFINITY;
+        l[j] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < F; e++) o[j][e] = 0.0f;
+    }
+
+    // The online softmax advances over the step's rows in batches of SUB
+    // rows (scores, running max and sum, then P.V), which bounds the score
+    // registers whatever the rows per step.
+    constexpr int SUB = AttnShape<G>::sub;
+    // MASKED: some row of the step lies outside the chunk (or is an absent
+    // selection entry) somewhere in the wave; steps where every row is
+    // attended skip the masking selects.
+    auto compute = [&](const SL (&k)[NR], const SL (&v)[NR], auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+        for (int r0 = 0; r0 < NR; r0 += SUB) {
+            float sc[SUB][G];
+            bool ok[SUB];                            // row inside the chunk
+#pragma unroll
+            for (int r = 0; r < SUB; r++) {
+                ok[r] = (okbits >> (r0 + r)) & 1u;
+                float kf[F];
+                k[r0 + r].to_f32(kf);
+#pragma unroll
+                for (int j = 0; j < G; j++) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < F; e++) acc = fmaf(qr[j][e], kf[e], acc);
+                    sc[r][j] = group_sum<LPR>(acc);
+                    if constexpr (MASKED) sc[r][j] = ok[r] ? sc[r][j] : -INFINITY;
+                }
+            }
+            float p[SUB][G];
+#pragma unroll
+            for (int j = 0; j < G; j++) {
+                float mx = sc[0][j];
+#pragma unroll
+                for (int r = 1; r < SUB; r++) mx = fmaxf(mx, sc[r][j]);
+                const float mn = fmaxf(m[j], mx);
+                const float mr = mn == -INFINITY ? 0.0f : mn;
+                const float alpha = exp2f(m[j] - mr);
+                float ps = 0.0f;
+#pragma unroll
+                for (int r = 0; r < SUB; r++) {
+                    p[r][j] = exp2f(sc[r][j] - mr);
+                    ps += p[r][j];
+                }
+                l[j] = l[j] * alpha + ps;
+                m[j] = mn;
+#pragma unroll
+                for (int e = 0; e < F; e++) o[j][e] *= alpha;
+            }
+#pragma unroll
+            for (int r = 0; r < SUB; r++) {
+                float vf[F];
+                v[r0 + r].to_f32(vf);
+                // a row past the chunk (a re-read of its last row) adds
+                // nothing, also where that row holds an infinity
+                if constexpr (MASKED) {
+#pragma unroll
+                    for (int e = 0; e < F; e++) vf[e] = ok[r] ? vf[e] : 0.0f;
+                }
+#pragma unroll
+                for (int j = 0; j < G; j++) {
+#pragma unroll
+                    for (int e = 0; e < F; e++) o[j][e] = fmaf(p[r][j], vf[e], o[j][e]);
+                }
+            }
+        }
+    };
+
+    // One register set per step: a step's loads are all issued, then waited
+    // for and computed on. (A second set for the next step's loads does not
+    // stay in flight across the loop: the compiler waits for every load at
+    // the loop head.)
+    // The unmasked copy of the step costs registers; it is kept where two
+    // workgroups per CU still fit (small query groups, fp32 and bf16 rows).
+    constexpr bool kTwoBodies = G <= 4 && DT != CK_KV_FP8_E4M3;
+    constexpr uint32_t kAllRows = (1u << NR) - 1u;
+    for (int st = t0;;) {
+        if (kTwoBodies && __builtin_amdgcn_ballot_w64(okbits != kAllRows) == 0)
+            compute(ka, va, std::integral_constant<bool, !kTwoBodies>{});
+        else
+            compute(ka, va, std::true_type{});
+        st += STEP;
+        if (st >= t1) break;
+        fetch(ka, va, st);
+    }
+
+    // Every row group's state goes to LDS as it is (no cross-lane exchange),
+    // then the chunk's state is their log-sum-exp combination: per head the
+    // largest max M, each state's weight 2^(m - M), the weighted sums.
+    const int sid = wave * RPR + rg;
+    if (bad) sm.bad = 1;
+#pragma unroll
+    for (int j = 0; j < G; j++) {
+#pragma unroll
+        for (int e = 0; e < F; e += 4)
+            *reinterpret_cast<float4 *>(&sm.ro[sid][j][SL::col(li, e)]) =
+                make_float4(o[j][e], o[j][e + 1], o[j][e + 2], o[j][e + 3]);
+        if (li == 0) {
+            sm.rm[sid][j] = m[j];
+            sm.rl[sid][j] = l[j];
+        }
+    }
+    __syncthreads();
+    const size_t part = ((size_t)s * KV + g) * a.nchunks + cidx;
+    // one lane per (head, state), the NS states of a head in one aligned lane
+    // group: the max and the weighted sum are group reductions
+    static_assert(NS <= kWave && (NS & (NS - 1)) == 0 && G * NS <= NT, "state groups");
+    if (tid < G * NS) {
+        const int j = tid / NS, i = tid % NS;
+        const float mi = sm.rm[i][j];
+        const float M = group_max<NS>(mi);
+        const float Mr = M == -INFINITY ? 0.0f : M;
+        const float w = exp2f(mi - Mr);
+        sm.rw[i][j] = w;
+        const float ls = group_sum<NS>(sm.rl[i][j] * w);
+        if (i == 0) {
+            part_store<COH>(&a.pml[(part * G + j) * 2 + 0], M);
+            part_store<COH>(&a.pml[(part * G + j) * 2 + 1], sm.bad ? NAN : ls);
+        }
+    }
+    __syncthreads();
+    // fp8: the V scale applied once to the weighted sum of code values
+    const float vsc = DT == CK_KV_FP8_E4M3 ? a.c.v_scale : 1.0f;
+    for (int idx = tid; idx < G * HD; idx += NT) {
+        const int j = idx / HD, c = idx % HD;
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NS; i++) acc = fmaf(sm.ro[i][j][c], sm.rw[i][j], acc);
+        part_store<COH>(&a.po[part * G * HD + idx], acc * vsc);
+    }
+    return true;
+}
+
+}  // namespace attn
+
+}  // namespace ck

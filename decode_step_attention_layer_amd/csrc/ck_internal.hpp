@@ -159,7 +159,8 @@ hipError_t launch_qkv(const float *x, const float *gamma, float eps, int D, int 
                       int m, const uint8_t *wq, const uint8_t *wk, const uint8_t *wv,
                       const float *bq, const float *bk, const float *bv, const float *cos_tab,
                       const float *sin_tab, const Positions &pos, const CacheView &c, float *q,
-                      float *k, float *v, float *xn, uint8_t *xq, hipStream_t st);
+                      float *k, float *v, float *xn, uint8_t *xq, hipStream_t st,
+                      unsigned *zero = nullptr, int nzero = 0, int zstride = 1);
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
 // Small-M GEMV on the int8 matrix cores (k_gemv_mfma.hip): batches of 4..16
 // tokens; same arguments and results as launch_gemv.
@@ -169,9 +170,12 @@ hipError_t launch_rope(float *q, float *k, const float *cos_tab, const float *si
                        const Positions &pos, int m, int H, int KV, int hd, hipStream_t st);
 hipError_t launch_kv_append(const CacheView &c, const float *k, const float *v,
                             const Positions &pos, int m, hipStream_t st);
+// zero/nzero/zstride (optional): words this launch clears (zero[i * zstride],
+// i < nzero), the counters of the attention + merge + O launch that follows.
 hipError_t launch_rope_append(float *q, float *k, const float *v, const float *cos_tab,
                               const float *sin_tab, const CacheView &c, const Positions &pos, int m,
-                              int H, hipStream_t st);
+                              int H, hipStream_t st, unsigned *zero = nullptr, int nzero = 0,
+                              int zstride = 1);
 
 // Attention geometry: tokens per chunk and chunks per (sequence, KV head).
 struct AttnPlan {
@@ -188,6 +192,12 @@ long long total_tokens(const Positions &p, int m, int window);
 bool attn_shape_supported(int G, int hd);
 bool attn_chunks_supported(int nchunks);
 size_t attn_partials_bytes(int m, int H, int hd, int nchunks);
+// The attention launch's work items: first[s] is sequence s's first item,
+// first[m] (returned) the count. Host positions give each sequence exactly
+// its chunks; device positions (or a selection, when `uniform`) give every
+// sequence plan.nchunks items, those past its length returning at once.
+int attn_first(const Positions &pos, int window, const AttnPlan &plan, int m, bool uniform,
+               int *first);
 // Sparse attention: per sequence, topk token positions (device, [m][topk],
 // -1 = absent) replace the sequence's tokens; sink (device, [H], nullable)
 // holds logits that join the softmax denominator only.
@@ -205,6 +215,19 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
 hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
                             void *partials, hipStream_t st, const SparseSel *sp = nullptr);
+
+// Attention + merge + Q8_0 + O projection in one launch (k_ato.hip): the
+// second launch of the two-launch layer. Its counters (ato_counter_words)
+// must be zero when it starts: the launch before it clears them.
+size_t ato_counter_words(int m, int KV);  // words of the counter region
+int ato_counters(int m, int KV);          // counters in it, ato_counter_stride() words apart
+int ato_counter_stride();
+size_t ato_status_word(int m, int KV);    // word index of the status word
+bool ato_supported(int H, int hd, int nchunks);
+hipError_t launch_ato(const float *q, const CacheView &c, const Positions &pos, int m, int H,
+                      float scale, const AttnPlan &plan, void *partials, float *attn_out,
+                      uint8_t *aq, void *aqx, const uint8_t *wo, const float *bo,
+                      const float *residual, float *out, int D, unsigned *cnt, hipStream_t st);
 
 // Persistent decode step (k_step.hip): every layer of a step in one launch.
 struct StepLayer {

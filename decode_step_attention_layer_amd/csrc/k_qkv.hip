@@ -37,6 +37,8 @@ struct QkvArgs {
     float *xn;              // [m][D]   written by workgroup 0
     uint8_t *xq;            // [m][D/32] Q8_0 blocks, written by workgroup 0
     int wg_k, wg_v;         // first workgroups of the K and V segments
+    unsigned *zero;         // nullable: nzero words, zstride apart, that workgroup 0
+    int nzero, zstride;     // clears (the counters of the launch that follows)
 };
 
 // Physical row of logical row r of a rotated segment: consecutive logical
@@ -187,6 +189,10 @@ __global__ __launch_bounds__(kGemvThreads) void k_qkv(QkvArgs a) {
     extern __shared__ XBlock xs[];
     __shared__ float red[2 * kGemvWaves];
     const int wg = blockIdx.x;
+    if (wg == 0)
+        for (int i = threadIdx.x; i < a.nzero; i += kGemvThreads)
+            __hip_atomic_store(a.zero + (size_t)i * a.zstride, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
     const int seg = wg >= a.wg_v ? 2 : (wg >= a.wg_k ? 1 : 0);
     const int wg_in_seg = wg - (seg == 2 ? a.wg_v : (seg == 1 ? a.wg_k : 0));
     if (seg == 2)
@@ -248,7 +254,8 @@ hipError_t launch_qkv(const float *x, const float *gamma, float eps, int D, int 
                       int m, const uint8_t *wq, const uint8_t *wk, const uint8_t *wv,
                       const float *bq, const float *bk, const float *bv, const float *cos_tab,
                       const float *sin_tab, const Positions &pos, const CacheView &c, float *q,
-                      float *k, float *v, float *xn, uint8_t *xq, hipStream_t st) {
+                      float *k, float *v, float *xn, uint8_t *xq, hipStream_t st,
+                      unsigned *zero, int nzero, int zstride) {
     QkvArgs a;
     a.x = x;
     a.gamma = gamma;
@@ -274,6 +281,9 @@ hipError_t launch_qkv(const float *x, const float *gamma, float eps, int D, int 
     a.xn = xn;
     a.xq = xq;
     a.wg_k = a.wg_v = 0;
+    a.zero = zero;
+    a.nzero = zero ? nzero : 0;
+    a.zstride = zstride;
     const int nb = D / kQK;
     return (nb % 2 == 0) ? launch_lpr<true>(a, nb / 2, st) : launch_lpr<false>(a, nb, st);
 }

@@ -65,7 +65,12 @@ __global__ __launch_bounds__(256) void k_rope_append(float *__restrict__ q, floa
                                                      const float *__restrict__ v,
                                                      const float *__restrict__ cos_tab,
                                                      const float *__restrict__ sin_tab,
-                                                     CacheView c, Positions pos, int H) {
+                                                     CacheView c, Positions pos, int H,
+                                                     unsigned *zero, int nzero, int zstride) {
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < nzero; i += blockDim.x)
+            __hip_atomic_store(zero + (size_t)i * zstride, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
     const int s = blockIdx.y;
     const int KV = c.kv_heads, hd = c.head_dim, half = hd >> 1;
     const int nq = H * half, nk = KV * half, nv = KV * hd;
@@ -102,10 +107,10 @@ __global__ __launch_bounds__(256) void k_rope_append(float *__restrict__ q, floa
 
 hipError_t launch_rope_append(float *q, float *k, const float *v, const float *cos_tab,
                               const float *sin_tab, const CacheView &c, const Positions &pos, int m,
-                              int H, hipStream_t st) {
+                              int H, hipStream_t st, unsigned *zero, int nzero, int zstride) {
     const int n = H * (c.head_dim / 2) + c.kv_heads * (c.head_dim / 2) + c.kv_heads * c.head_dim;
     hipLaunchKernelGGL(k_rope_append, dim3((n + 255) / 256, m), dim3(256), 0, st, q, k, v, cos_tab,
-                       sin_tab, c, pos, H);
+                       sin_tab, c, pos, H, zero, zero ? nzero : 0, zstride);
     return hipGetLastError();
 }
 

@@ -103,6 +103,11 @@ typedef struct ck_kv_cache {
 #define CK_VARIANT_CHAIN 0       /* one kernel per step (the unfused chain) */
 #define CK_VARIANT_FUSED 1       /* steps fused into four kernels per layer */
 #define CK_VARIANT_PERSISTENT 2  /* every layer of a step in one persistent kernel */
+#define CK_VARIANT_TWO_LAUNCH 3  /* two launches per layer: RMSNorm + Q8_0 + Q/K/V + RoPE +
+                                    append; then attention, merge + Q8_0 and the O
+                                    projection in one launch whose workgroups hand over
+                                    through device-coherent counters (sparse selections and
+                                    shapes it does not take run as CK_VARIANT_FUSED) */
 
 #define CK_MAX_STEP_LAYERS 32
 
@@ -260,6 +265,20 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w,
                     const int32_t *pos_host, float *out, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* The layer of ck_decode_layer in two calls on the same workspace, for
+ * callers that interleave other work with the halves or time them apart:
+ * part 1 runs steps 1-6 (RMSNorm, Q8_0, Q/K/V projections, RoPE, KV append)
+ * and leaves q, k and v in the workspace; part 2 runs steps 7-8 (attention,
+ * Q8_0 of its output, O projection + bias + residual) from them. Same
+ * arguments as ck_decode_layer in both calls (part 1 does not write out;
+ * part 2 does not read x); part 1 then part 2 on one stream, with nothing
+ * else using the workspace in between, equals ck_decode_layer. Chain, fused
+ * and two-launch variants (CK_EUNSUPPORTED for the persistent one). */
+int ck_decode_layer_part(const ck_layer_desc *desc, const ck_layer_weights *w,
+                         const ck_kv_cache *kv, const float *x, const float *residual,
+                         const int32_t *pos_host, float *out, void *ws, size_t ws_bytes, int part,
+                         void *stream);
+
 /* A whole decode step: `layers` layers of the same shape, layer l reading the
  * previous layer's output (x for layer 0) with that input as its residual:
  *   x_{l+1} = ck_decode_layer(layer l, x_l, residual = x_l),  out = x_layers.
@@ -314,6 +333,9 @@ long ck_decode_step_status_offset(const ck_layer_desc *desc, int layers);
  * workspace of a step (they do not depend on the number of layers), where
  * the intermediates of the step's last layer remain. */
 long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const char *name);
+/* "status" (CK_VARIANT_TWO_LAUNCH only, else -1): the uint32 status word of
+ * the layer's second launch, zero after a call whose waits completed and
+ * non-zero if one timed out (read it after synchronizing). */
 
 #ifdef __cplusplus
 }

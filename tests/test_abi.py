@@ -126,6 +126,27 @@ def test_layer_validation_and_workspace(ck):
                              pos_bad, FAKE + 4096, FAKE, n, None) == ck.CK_EINVAL
 
 
+def test_layer_part_validation(ck):
+    L = ck.load()
+    good = ck.layer_desc(256, 4, 2, 64, 1)
+    n = ck.ck_decode_layer_workspace_size(good, 17)
+    w = ck.CkLayerWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, 64)
+    c = ck.CkKVCache(FAKE, FAKE, 2, 64, 64, 0, None, 0, 0)
+    pos = (ctypes.c_int32 * 1)(16)
+    for part in (0, 3):
+        assert L.ck_decode_layer_part(ctypes.byref(good), ctypes.byref(w), ctypes.byref(c), FAKE,
+                                      FAKE, pos, FAKE + 4096, FAKE, n, part, None) == ck.CK_EINVAL
+    pers = ck.layer_desc(256, 4, 2, 64, 1, variant=ck.CK_VARIANT_PERSISTENT)
+    assert L.ck_decode_layer_part(ctypes.byref(pers), ctypes.byref(w), ctypes.byref(c), FAKE,
+                                  FAKE, pos, FAKE + 4096, FAKE, 1 << 20, 1, None) == \
+        ck.CK_EUNSUPPORTED
+    # the two-launch variant is accepted by the descriptor checks
+    two = ck.layer_desc(256, 4, 2, 64, 1, variant=ck.CK_VARIANT_TWO_LAUNCH)
+    assert ck.ck_decode_layer_workspace_size(two, 17) > 0
+    assert ck.ck_decode_layer_ws_offset(two, 17, "status") > 0
+    assert ck.ck_decode_layer_ws_offset(good, 17, "status") == -1
+
+
 def test_no_fallback_when_library_missing(tmp_path, monkeypatch):
     from decode_step_attention_layer_amd import ck as ckmod
 

@@ -90,7 +90,7 @@ def _caches(stack):
     return [(host(L.tensors["k"]).copy(), host(L.tensors["v"]).copy()) for L in stack.layers]
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2], ids=["chain", "fused", "persistent"])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3], ids=["chain", "fused", "persistent", "two_launch"])
 @pytest.mark.parametrize("name,layers", [("c1", None), ("c2", 3), ("c5", None)])
 def test_devpos_step_equals_host_positions(name, layers, variant):
     import torch
@@ -134,7 +134,7 @@ def test_devpos_step_equals_host_positions(name, layers, variant):
         assert torch.equal(ya, yb)
 
 
-@pytest.mark.parametrize("variant", [1, 2], ids=["fused", "persistent"])
+@pytest.mark.parametrize("variant", [1, 2, 3], ids=["fused", "persistent", "two_launch"])
 @pytest.mark.parametrize("name,layers", [("c1", None), ("c2", 2), ("c5", None)])
 def test_graph_decode_loop_with_device_positions(name, layers, variant):
     import torch

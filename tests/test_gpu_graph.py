@@ -9,7 +9,8 @@ from gpu_helpers import cuda
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,variant", [("c1", 1), ("c1", 0), ("c2", 1), ("c5", 1)])
+@pytest.mark.parametrize("name,variant", [("c1", 1), ("c1", 0), ("c2", 1), ("c5", 1), ("c1", 3),
+                                          ("c2", 3), ("c5", 3)])
 def test_graph_replay_equals_eager(name, variant):
     import torch
     from decode_step_attention_layer_amd import synth
@@ -63,3 +64,37 @@ def test_graph_replay_persistent_step(name):
         again = stack.decode_step(desc, ws)
         torch.cuda.synchronize()
         assert torch.equal(again, eager)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c5"])
+@pytest.mark.parametrize("variant", [0, 1, 3], ids=["chain", "fused", "two_launch"])
+def test_layer_in_two_parts_equals_the_layer(name, variant):
+    """ck_decode_layer_part 1 (steps 1-6) then 2 (steps 7-8) on one workspace
+    equals ck_decode_layer bit for bit: output, cache bytes and the
+    intermediates the workspace keeps (the layer itself is checked against
+    the oracle in test_gpu_layer.py)."""
+    import torch
+    from decode_step_attention_layer_amd import ck, synth
+    from decode_step_attention_layer_amd.workload import DeviceStack
+
+    dev = cuda()
+    a = DeviceStack(synth.CONFIGS[name], dev, layers=1)
+    b = a.clone()
+    desc = a.desc(variant)
+    wa, wb = a.workspace(desc), b.workspace(desc)
+    ya = torch.empty((a.cfg.m, a.cfg.D), dtype=torch.float32, device=dev)
+    yb = torch.empty_like(ya)
+    La, Lb = a.layers[0], b.layers[0]
+    ck.ck_decode_layer(desc, La.weights, La.cache, a.x0, a.x0, a.pos, ya, wa, wa.numel())
+    for part in (1, 2):
+        ck.ck_decode_layer_part(desc, Lb.weights, Lb.cache, b.x0, b.x0, b.pos, yb, wb,
+                                wb.numel(), part)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb)
+    for n in ("k", "v"):
+        assert torch.equal(La.tensors[n].view(torch.int32), Lb.tensors[n].view(torch.int32))
+    from test_gpu_layer import ws_reader
+    ra = ws_reader(ck, desc, a.max_ctx, wa, a.cfg)()
+    rb = ws_reader(ck, desc, b.max_ctx, wb, b.cfg)()
+    for n in ra:
+        assert np.array_equal(ra[n].view(np.uint8), rb[n].view(np.uint8)), n

@@ -230,7 +230,7 @@ def _layer_check(name, dtype, variant):
     assert_close_rms(host(out), ref, 2e-3, f"{name} layer output")
 
 
-@pytest.mark.parametrize("variant", [0, 1], ids=["chain", "fused"])
+@pytest.mark.parametrize("variant", [0, 1, 3], ids=["chain", "fused", "two_launch"])
 @pytest.mark.parametrize("dtype", DTYPES, ids=IDS)
 @pytest.mark.parametrize("name", ["c1", "c4", "c5"])
 def test_layer_with_reduced_cache(name, dtype, variant):

@@ -19,7 +19,9 @@ layer received:
   * every KV-cache slot except the appended one is byte-identical (NaN poison
     included), and the appended slot holds exactly the k, v the layer computed.
 The persistent variant runs here as one-layer persistent steps (the same
-kernel as a whole step, with one layer's items). End to end, the GPU chain of
+kernel as a whole step, with one layer's items); the two-launch variant
+(attention, merge and O projection in one launch) also leaves its status
+word zero. End to end, the GPU chain of
 all layers matches the independent oracle chain
 within max(2e-3, 3 x the oracle's own +-1-ulp noise floor) x RMS: chaining
 quantized layers turns last-bit differences into occasional code flips in
@@ -37,8 +39,8 @@ from gpu_helpers import assert_close_rms, cuda, host, rms
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-VARIANTS = [0, 1, 2]
-VARIANT_IDS = ["chain", "fused", "persistent"]
+VARIANTS = [0, 1, 2, 3]
+VARIANT_IDS = ["chain", "fused", "persistent", "two_launch"]
 
 
 def gcache_row(cfg, L, s, g, t):
@@ -80,6 +82,10 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
         ck.ck_decode_layer(desc, L.weights, L.cache, x_gpu_in, x_gpu_in, pos, out, ws, ws.numel())
         torch.cuda.synchronize()
         got = host(out)
+        if variant == 3:
+            soff = ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, "status")
+            assert soff >= 0 and int(ws[soff:soff + 4].view(torch.int32).item()) == 0, \
+                f"{name} layer {li}: a wait of the second launch timed out"
         wts = dict(L.host, rope_cos=cos, rope_sin=sin)
         st = parity.check_layer(cfg, wts, lambda k, v: ocache(cfg, L, k, v), L.host["k"],
                                 L.host["v"], x_host, got, read(), host(L.tensors["k"]),

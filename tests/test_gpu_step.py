@@ -1,7 +1,7 @@
 """GPU parity of a whole decode step (ck_decode_step: every layer of a
 workload in one call), in the three variants.
 
-  * chain and fused: bit-identical to the same variant called layer by layer
+  * chain, fused and two-launch: bit-identical to the same variant called layer by layer
     through ck_decode_layer (the same kernels, verified stage by stage in
     test_gpu_layer.py);
   * persistent (every layer in one persistent kernel): for n = 1 .. layers,
@@ -78,7 +78,7 @@ def _step_check(name, layers=None):
     cos, sin = synth.rope_for(cfg)
 
     # chain and fused: whole step == layer by layer, bit for bit
-    for variant in (ck.CK_VARIANT_CHAIN, ck.CK_VARIANT_FUSED):
+    for variant in (ck.CK_VARIANT_CHAIN, ck.CK_VARIANT_FUSED, ck.CK_VARIANT_TWO_LAUNCH):
         d = stack.desc(variant)
         per_layer = stack.step(d, stack.workspace(d)).clone()
         whole = stack.decode_step(d, stack.step_workspace(d)).clone()

@@ -207,6 +207,9 @@ LAYER_CASES = [
     ("c2", 300, False, 2, 0),
     ("c3", 1000, True, 2, 1),
     ("c3", 1000, False, 2, 1),
+    ("c1", 8, True, 12, 3),        # the two-launch variant
+    ("c2", 256, True, 3, 3),
+    ("c3", 1000, False, 2, 3),
 ]
 
 
