@@ -37,7 +37,8 @@ EXPORTS = (
     "ck_decode_layer",
     "ck_decode_layer_ws_offset", "ck_decode_step_workspace_size", "ck_decode_step",
     "ck_decode_step_status_offset", "ck_decode_layer_devpos", "ck_decode_step_devpos",
-    "ck_attn_sparse", "ck_decode_layer_sparse", "ck_decode_layer_part",
+    "ck_attn_sparse", "ck_decode_layer_sparse", "ck_decode_layer_noalloc",
+    "ck_decode_layer_noalloc_limit", "ck_decode_layer_part",
 )
 
 
@@ -108,6 +109,10 @@ def load():
                              ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, P], I),
         "ck_decode_layer_part": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                                   ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, I, P], I),
+        "ck_decode_layer_noalloc": ([ctypes.POINTER(CkLayerDesc),
+                                     ctypes.POINTER(CkLayerWeights), ctypes.POINTER(CkKVCache),
+                                     P, P, IP, P, P], I),
+        "ck_decode_layer_noalloc_limit": ([], S),
         "ck_decode_layer_ws_offset": ([ctypes.POINTER(CkLayerDesc), I, ctypes.c_char_p],
                                       ctypes.c_long),
         "ck_decode_step_workspace_size": ([ctypes.POINTER(CkLayerDesc), I, I], S),
@@ -261,6 +266,17 @@ def ck_decode_layer_part(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKV
                                        ctypes.byref(cache), _ptr(x), _ptr(residual), _pos(pos),
                                        _ptr(out), _ptr(ws), ws_bytes, int(part), _stream(stream)),
            "ck_decode_layer_part")
+
+
+def ck_decode_layer_noalloc(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache, x,
+                            residual, pos, out, stream=None):
+    _check(load().ck_decode_layer_noalloc(ctypes.byref(desc), ctypes.byref(weights),
+                                          ctypes.byref(cache), _ptr(x), _ptr(residual), _pos(pos),
+                                          _ptr(out), _stream(stream)), "ck_decode_layer_noalloc")
+
+
+def ck_decode_layer_noalloc_limit() -> int:
+    return int(load().ck_decode_layer_noalloc_limit())
 
 
 def ck_decode_step_workspace_size(desc: CkLayerDesc, layers: int, max_ctx: int) -> int:

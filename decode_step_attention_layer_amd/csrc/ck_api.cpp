@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ck.h"
 #include "ck_gemv_common.hpp"
 #include "ck_internal.hpp"
@@ -756,5 +758,65 @@ int ck_decode_layer_devpos(const ck_layer_desc *desc, const ck_layer_weights *w,
     return decode_layer_impl(desc, w, kv, x, residual, PosIn{nullptr, pos_dev, max_ctx}, out,
                              ws, ws_bytes, stream);
 }
+
+}  // extern "C"
+
+// ------------------------------------------------- allocation-free layer --
+// The workspace of ck_decode_layer_noalloc: a library-owned device array of
+// CK_NOALLOC_SCRATCH_BYTES. Every GPU the library runs on holds its own copy
+// at its own address until the process ends. In host code `scratch` only
+// names the array; its device address comes from hipGetSymbolAddress, taken
+// once per device (with that device current) and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[CK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device).
+int scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CK_EHIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CK_EHIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return CK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ck_decode_layer_noalloc(const ck_layer_desc *desc, const ck_layer_weights *w,
+                            const ck_kv_cache *kv, const float *x, const float *residual,
+                            const int32_t *pos_host, float *out, void *stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!pos_host) return CK_EINVAL;
+    int mx = 0;
+    for (int s = 0; s < desc->m; s++) {
+        if (pos_host[s] < 0) return CK_EINVAL;
+        if (pos_host[s] + 1 > mx) mx = pos_host[s] + 1;
+    }
+    // the workspace this call needs, against the array's size (before any
+    // device call, so that a refusal touches nothing)
+    const size_t need = ck_decode_layer_workspace_size(desc, mx);
+    if (need == 0) return CK_EINVAL;
+    if (need > (size_t)CK_NOALLOC_SCRATCH_BYTES) return CK_ENOSPC;
+    void *ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc) return rc;
+    return decode_layer_impl(desc, w, kv, x, residual, PosIn{pos_host, nullptr, 0}, out, ws,
+                             (size_t)CK_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+size_t ck_decode_layer_noalloc_limit(void) { return (size_t)CK_NOALLOC_SCRATCH_BYTES; }
 
 }  // extern "C"

@@ -14,14 +14,17 @@
  *  - Pointers named *_host are host memory; every other pointer is device
  *    memory (hipMalloc'd or a torch CUDA tensor), 16-byte aligned.
  *  - The caller owns every buffer: weights, cache, inputs, outputs and the
- *    workspace. The library never allocates, frees or synchronizes.
+ *    workspace. The library never allocates, frees or synchronizes. (The one
+ *    exception is ck_decode_layer_noalloc, whose workspace is a device array
+ *    the library owns; see there.)
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; results are valid after the stream is synchronized.
  *  - Arguments are validated on the host before anything is launched. The
  *    return value is CK_OK or a negative CK_E* code; on an error nothing has
  *    been enqueued. A launch failure reported by the runtime returns CK_EHIP.
  *  - The library keeps no state between calls and is safe to call from
- *    several host threads on different streams.
+ *    several host threads on different streams (ck_decode_layer_noalloc
+ *    excepted: its calls on one GPU share one workspace).
  *  - m, the number of tokens (one per sequence), is at most CK_MAX_SEQS.
  *
  * Block layouts (little-endian, packed, no padding), 32 values per block:
@@ -336,6 +339,27 @@ long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const cha
 /* "status" (CK_VARIANT_TWO_LAUNCH only, else -1): the uint32 status word of
  * the layer's second launch, zero after a call whose waits completed and
  * non-zero if one timed out (read it after synchronizing). */
+
+/* Allocation-free decode layer, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): ck_decode_layer, same arguments, results and variants,
+ * with the workspace taken from a device array the library owns instead of
+ * a caller's buffer. The array holds CK_NOALLOC_SCRATCH_BYTES (16 MiB); each
+ * GPU the library runs on keeps its own copy until the process ends. A call
+ * whose workspace (ck_decode_layer_workspace_size at the largest position
+ * + 1) exceeds that returns CK_ENOSPC before touching the device. The call
+ * allocates and frees nothing; the first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) once. Nothing in the array
+ * has to start at zero: what a call's kernels count they clear themselves.
+ * Every call on one GPU shares that GPU's array and leaves it holding the
+ * last call's intermediates: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller. */
+#define CK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int ck_decode_layer_noalloc(const ck_layer_desc *desc, const ck_layer_weights *w,
+                            const ck_kv_cache *kv, const float *x, const float *residual,
+                            const int32_t *pos_host, float *out, void *stream);
+/* CK_NOALLOC_SCRATCH_BYTES as built into the library. */
+size_t ck_decode_layer_noalloc_limit(void);
 
 #ifdef __cplusplus
 }

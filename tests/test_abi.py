@@ -147,6 +147,29 @@ def test_layer_part_validation(ck):
     assert ck.ck_decode_layer_ws_offset(good, 17, "status") == -1
 
 
+def test_noalloc_refuses_before_touching_the_device(ck):
+    """The allocation-free layer checks its workspace need against the
+    library's array before any device call: an oversized call is CK_ENOSPC,
+    bad arguments CK_EINVAL (no GPU here, so reaching the device would fail
+    differently)."""
+    L = ck.load()
+    assert ck.ck_decode_layer_noalloc_limit() == 16 << 20
+    w = ck.CkLayerWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE,
+                          1 << 20)
+    big = ck.layer_desc(4096, 32, 8, 128, 16)
+    c = ck.CkKVCache(FAKE, FAKE, 8, 128, 1 << 20, 0, None, 0, 0)
+    far = (ctypes.c_int32 * 16)(*([(1 << 20) - 1] * 16))
+    assert ck.ck_decode_layer_workspace_size(big, 1 << 20) > ck.ck_decode_layer_noalloc_limit()
+    assert L.ck_decode_layer_noalloc(ctypes.byref(big), ctypes.byref(w), ctypes.byref(c), FAKE,
+                                     FAKE, far, FAKE + 4096, None) == ck.CK_ENOSPC
+    neg = (ctypes.c_int32 * 1)(-1)
+    small = ck.layer_desc(256, 4, 2, 64, 1)
+    assert L.ck_decode_layer_noalloc(ctypes.byref(small), ctypes.byref(w), ctypes.byref(c), FAKE,
+                                     FAKE, neg, FAKE + 4096, None) == ck.CK_EINVAL
+    assert L.ck_decode_layer_noalloc(None, ctypes.byref(w), ctypes.byref(c), FAKE, FAKE, neg,
+                                     FAKE + 4096, None) == ck.CK_EINVAL
+
+
 def test_no_fallback_when_library_missing(tmp_path, monkeypatch):
     from decode_step_attention_layer_amd import ck as ckmod
 
