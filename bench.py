@@ -63,6 +63,9 @@ def parse():
                     help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default workload only: skip the other variants, the long-context "
+                         "record and the streaming probe")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -121,44 +124,50 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the layer is built and timed on a single MI355X "
-              "(sharding the layer across GPUs is not implemented).", file=sys.stderr)
-        sys.exit(2)
+VARIANTS = ("chain", "fused", "persistent", "two_launch")
 
-    import numpy as np
-    import torch
 
-    from decode_step_attention_layer_amd import ck, synth
+def variant_code(ck, name):
+    return {"fused": ck.CK_VARIANT_FUSED, "chain": ck.CK_VARIANT_CHAIN,
+            "persistent": ck.CK_VARIANT_PERSISTENT,
+            "two_launch": ck.CK_VARIANT_TWO_LAUNCH}[name]
+
+
+def build_stacks(cfg, kv_dtype, keep_host, window=0, ring=False, topk=0):
+    """The workload on the GPU, plus replicas when one step's bytes would fit
+    three times in the last-level cache (rotated so that each step reads from
+    HBM)."""
+    from decode_step_attention_layer_amd import synth
     from decode_step_attention_layer_amd.workload import DeviceStack
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    ck.load()
-    cfg = synth.CONFIGS[args.config]
-    variant = {"fused": ck.CK_VARIANT_FUSED, "chain": ck.CK_VARIANT_CHAIN,
-               "persistent": ck.CK_VARIANT_PERSISTENT,
-               "two_launch": ck.CK_VARIANT_TWO_LAUNCH}[args.variant]
-    persistent = variant == ck.CK_VARIANT_PERSISTENT
     t0 = time.time()
-    kv_dtype = {"f32": synth.KV_F32, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}[args.kv]
-    stack = DeviceStack(cfg, "cuda:0", keep_host=not args.no_cpu, kv_dtype=kv_dtype,
-                        window=args.window, ring=args.ring, topk=args.topk)
-    log(f"[bench] {args.config}: {stack.nlayers} layers on device in {time.time() - t0:.1f}s")
-    nbytes = synth.algorithmic_bytes(cfg, stack.lens, kv_dtype, args.window, args.topk)
+    stack = DeviceStack(cfg, "cuda:0", keep_host=keep_host, kv_dtype=kv_dtype, window=window,
+                        ring=ring, topk=topk)
+    log(f"[bench] {cfg.name}: {stack.nlayers} layers on device in {time.time() - t0:.1f}s")
+    nbytes = synth.algorithmic_bytes(cfg, stack.lens, kv_dtype, window, topk)
     step_bytes = nbytes["total"] * stack.nlayers
     replicas = 1
     if step_bytes < 3 * MALL_BYTES:
         replicas = min(8, math.ceil(3 * MALL_BYTES / step_bytes))
     stacks = [stack] + [stack.clone() for _ in range(replicas - 1)]
-    desc = stack.desc(variant, args.attn_chunk)
+    return stacks, nbytes, step_bytes
+
+
+def time_steps(stacks, desc, steps, warmup, eager=False):
+    """Decode steps of the stacks (rotated) with the given layer descriptor:
+    eager warm-up, one HIP graph per replica (checked equal to the eager
+    step), then `steps` replays timed with HIP events on the launch stream,
+    one event between consecutive steps. Returns (per-step times in ms,
+    workspaces)."""
+    import torch
+
+    from decode_step_attention_layer_amd import ck
+
+    stack = stacks[0]
+    cfg = stack.cfg
+    replicas = len(stacks)
     stream = torch.cuda.current_stream()
-    if persistent:
+    if desc.variant == ck.CK_VARIANT_PERSISTENT:
         # every layer of the step in one persistent kernel (ck_decode_step)
         wss = [s.step_workspace(desc) for s in stacks]
         outs = [torch.empty((cfg.m, cfg.D), dtype=torch.float32, device="cuda:0")
@@ -174,15 +183,13 @@ def main():
         def one_step(j):
             return stacks[j].step(desc, wss[j])
 
-    # ---- eager warm-up (also the reference for the graph replays)
-    for i in range(max(1, args.warmup)):
+    for _ in range(max(1, warmup)):
         for j in range(replicas):
             one_step(j)
     torch.cuda.synchronize()
     ref = outs[0].clone()
-
     graphs = []
-    if not args.eager:
+    if not eager:
         for j in range(replicas):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -199,26 +206,92 @@ def main():
         else:
             one_step(i % replicas)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         run_step(i)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         run_step(i)
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    ms_step = ms / args.steps
-    us_layer = ms_step * 1e3 / stack.nlayers
-    value = step_bytes / (ms_step * 1e-3) / 1e9
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     assert torch.isfinite(outs[0]).all(), "non-finite layer output"
-    if persistent:
+    if desc.variant == ck.CK_VARIANT_PERSISTENT:
         for s, ws in zip(stacks, wss):
             assert s.step_status(desc, ws) == 0, "a persistent step timed out"
+    if desc.variant == ck.CK_VARIANT_TWO_LAUNCH:
+        off = ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, "status")
+        for ws in wss:
+            assert int(ws[off:off + 4].view(torch.int32).item()) == 0, "a wait timed out"
+    return ms, wss
+
+
+def pct(v, q):
+    import numpy as np
+
+    return float(np.percentile(np.asarray(v, float), q))
+
+
+def stream_probe():
+    """The box's achievable streaming-read bandwidth: libck's plain read
+    kernel (ck_read_probe: 16-byte non-temporal loads, four workgroups per
+    compute unit) over 2 GiB, timed with HIP events on the launch stream;
+    the best of 6 launches."""
+    import torch
+
+    from decode_step_attention_layer_amd import ck
+
+    n = 2 << 30
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    best = None
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        ck.ck_read_probe(x, n, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del x
+    torch.cuda.empty_cache()
+    return {"GBs": round(n / (best * 1e-3) / 1e9, 1), "bytes": n,
+            "frac_of_peak": round(n / (best * 1e-3) / 1e9 / PEAK_GBS, 4),
+            "kind": "ck_read_probe over 2 GiB (plain streaming read), best of 6"}
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the layer is built and timed on a single MI355X "
+              "(sharding the layer across GPUs is not implemented).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_step_attention_layer_amd import ck, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ck.load()
+    cfg = synth.CONFIGS[args.config]
+    kv_dtype = {"f32": synth.KV_F32, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}[args.kv]
+    stacks, nbytes, step_bytes = build_stacks(cfg, kv_dtype, not args.no_cpu, args.window,
+                                              args.ring, args.topk)
+    stack = stacks[0]
+    desc = stack.desc(variant_code(ck, args.variant), args.attn_chunk)
+    ms, wss = time_steps(stacks, desc, args.steps, args.warmup, args.eager)
+    ms_step = sum(ms) / len(ms)
+    us_layer = ms_step * 1e3 / stack.nlayers
+    value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.2f} us, {us_layer:.2f} us/layer, {value:.0f} GB/s")
 
-    if persistent:
+    if desc.variant == ck.CK_VARIANT_PERSISTENT:
         # the step is one kernel (k_step, after a counter-clearing kernel of
         # about a microsecond): its launches are the timed region itself
         roof = {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_GBS, "unit": "GB/s",
@@ -226,6 +299,12 @@ def main():
                 "us_per_launch": round(ms_step * 1e3, 3), "bytes_per_launch": step_bytes}
     else:
         roof = roofline(args, stacks, desc, wss[0], nbytes)
+    extras = {}
+    default_run = (args.config == "c3" and args.kv == "f32" and not args.window and not args.topk
+                   and not args.eager and not args.no_extras)
+    if default_run:
+        extras = extra_records(args, stacks, step_bytes, args.variant, us_layer)
+    del wss
     cpu = None if args.no_cpu else cpu_baseline(args, stack, nbytes)
 
     line = {
@@ -252,16 +331,74 @@ def main():
             "launch": "eager" if args.eager else "hip-graph",
             "layers": stack.nlayers,
             "tokens_per_step": cfg.m,
-            "replicas": replicas,
+            "replicas": len(stacks),
         },
         "us_per_layer": round(us_layer, 3),
         "us_per_token": round(ms_step * 1e3 / cfg.m, 3),
+        "step_us": {"mean": round(ms_step * 1e3, 2), "median": round(pct(ms, 50) * 1e3, 2),
+                    "p10": round(pct(ms, 10) * 1e3, 2), "p90": round(pct(ms, 90) * 1e3, 2)},
         "bytes_per_step": step_bytes,
         "frac_of_peak": round(value / PEAK_GBS, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    line.update(extras)
     print(json.dumps(line), flush=True)
+
+
+def extra_records(args, stacks, step_bytes, variant, us_layer):
+    """Beside the default workload's line: the same stack in every variant
+    (the fused layer against the unfused chain, the persistent step and the
+    two-launch layer), the long-context layer (the second target workload)
+    with its attention kernel's roofline, and the streaming-read probe."""
+    import torch
+
+    from decode_step_attention_layer_amd import ck, synth
+
+    steps, warm = max(10, min(args.steps, 30)), max(2, min(args.warmup, 5))
+    stack = stacks[0]
+    var = {}
+    for v in VARIANTS:
+        if v == variant:
+            var[v] = {"us_per_layer": round(us_layer, 3)}
+            continue
+        d = stack.desc(variant_code(ck, v), args.attn_chunk)
+        ms, wss = time_steps(stacks, d, steps, warm)
+        del wss
+        m = sum(ms) / len(ms)
+        var[v] = {"us_per_layer": round(m * 1e3 / stack.nlayers, 3),
+                  "median_us_per_layer": round(pct(ms, 50) * 1e3 / stack.nlayers, 3),
+                  "GBs": round(step_bytes / (m * 1e-3) / 1e9, 1)}
+        log(f"[bench] c3 {v}: {var[v]['us_per_layer']:.2f} us/layer")
+    torch.cuda.synchronize()
+    del stacks[1:]
+    torch.cuda.empty_cache()
+
+    # the long-context layer
+    cfg4 = synth.CONFIGS["c4"]
+    st4, nb4, sb4 = build_stacks(cfg4, synth.KV_F32, False)
+    d4 = st4[0].desc(variant_code(ck, variant), 0)
+    ms4, ws4 = time_steps(st4, d4, max(20, steps), warm)
+    m4 = sum(ms4) / len(ms4)
+    g4 = sb4 / (m4 * 1e-3) / 1e9
+    class A:   # the roofline's view of the arguments for this workload
+        kernel_reps = args.kernel_reps
+        config, kv, window, ring, topk = "c4", "f32", 0, False, 0
+    r4 = roofline(A, st4, d4, ws4[0], nb4) if d4.variant != ck.CK_VARIANT_PERSISTENT else None
+    secondary = {"workload": workload_text(A),
+                 "variant": variant,
+                 "us_per_layer": round(m4 * 1e3, 3),
+                 "median_us_per_layer": round(pct(ms4, 50) * 1e3, 3),
+                 "p10_us": round(pct(ms4, 10) * 1e3, 2), "p90_us": round(pct(ms4, 90) * 1e3, 2),
+                 "GBs": round(g4, 1), "frac_of_peak": round(g4 / PEAK_GBS, 4),
+                 "bytes_per_layer": sb4,
+                 "attention": None if r4 is None else {
+                     "kernel": r4["kernel"], "us_per_launch": r4["us_per_launch"],
+                     "GBs": r4["achieved"], "frac": r4["frac"], "traffic": r4["traffic"]}}
+    log(f"[bench] c4: {m4 * 1e3:.2f} us/layer, {g4:.0f} GB/s")
+    del st4, ws4
+    torch.cuda.empty_cache()
+    return {"variants_c3": var, "secondary": secondary, "stream_probe": stream_probe()}
 
 
 def _time_launches(fn, reps):
@@ -314,7 +451,9 @@ def roofline(args, stacks, desc, ws, nbytes):
     off = lambda n: ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, n)
     base = ws.data_ptr()
     q, aq = base + off("q"), base + off("aq")
-    nws = ck.ck_attn_workspace_size(m, H, KV, hd, stack.max_ctx, desc.attn_chunk)
+    # the split the layer plans for these positions, passed explicitly
+    chunk, _ = ck.ck_decode_layer_attn_plan(desc, units[0].cache, stack.pos, stack.topk)
+    nws = ck.ck_attn_workspace_size(m, H, KV, hd, stack.max_ctx, chunk)
     part = torch.empty(nws, dtype=torch.uint8, device=ws.device)
     out = torch.empty((m, D), dtype=torch.float32, device=ws.device)
     scale = 1.0 / math.sqrt(hd)
@@ -322,21 +461,23 @@ def roofline(args, stacks, desc, ws, nbytes):
     if stack.topk:
         # the sparse attention has no separate partial entry point: the pair
         # of kernels (partial and merge) is timed
-        nws = ck.ck_attn_workspace_size(m, H, KV, hd, stack.topk, desc.attn_chunk)
+        nws = ck.ck_attn_workspace_size(m, H, KV, hd, stack.topk, chunk)
         part = torch.empty(nws, dtype=torch.uint8, device=ws.device)
         att_out = torch.empty((m, H * hd), dtype=torch.float32, device=ws.device)
 
         def sparse_attn():
             L = nxt(0)
             ck.ck_attn_sparse(q, L.cache, stack.pos, L.tensors["sel"], stack.topk,
-                              L.tensors["sink"], att_out, m, H, scale, desc.attn_chunk, part, nws)
+                              L.tensors["sink"], att_out, m, H, scale, chunk, part, nws)
         attn_us = _time_launches(sparse_attn, args.kernel_reps)
         attn_name = "k_attn+k_attn_merge"
     else:
         attn_us = _time_launches(lambda: ck.ck_attn_partial(
-            q, nxt(0).cache, stack.pos, m, H, scale, desc.attn_chunk, part, nws),
+            q, nxt(0).cache, stack.pos, m, H, scale, chunk, part, nws),
             args.kernel_reps)
-        attn_name = "k_attn"
+        # query groups over 4 heads attending an fp32 cache run on the matrix
+        # cores (a kernel of its own name)
+        attn_name = "k_attn_mfma" if H // KV > 4 and args.kv == "f32" else "k_attn"
 
     def o_gemv():
         L = nxt(1)
@@ -358,7 +499,8 @@ def roofline(args, stacks, desc, ws, nbytes):
             "traffic_unit": "bytes per launch",
             "kernel": name,
             "us_per_launch": round(us, 3), "bytes_per_launch": b,
-            "other": {"k_attn_us": round(attn_us, 3), "k_attn_GBs": round(att_gbs, 1),
+            "other": {"attn_chunk": chunk, "k_attn_us": round(attn_us, 3),
+                      "k_attn_GBs": round(att_gbs, 1),
                       "o_gemv_us": round(wo_us, 3), "o_gemv_GBs": round(wo_gbs, 1)}}
 
 
@@ -385,11 +527,12 @@ def recorded_traffic(kernel: str, workload: str, launches_bytes=None):
     rec = json.loads(mt.group(1))
     csrc = os.path.join(ROOT, "decode_step_attention_layer_amd", "csrc")
     h = hashlib.sha256()
-    src_file = {"k_attn_merge": "k_attn"}.get(kernel, kernel) + ".hip"
+    src_file = {"k_attn_merge": "k_attn", "k_attn_mfma": "k_attn"}.get(kernel, kernel) + ".hip"
     # the merge runs as k_attn_merge1 (one wavefront) when a sequence has at
     # most 32 chunks: either record stands for it
     names = ("k_attn_merge", "k_attn_merge1") if kernel == "k_attn_merge" else (kernel,)
-    for f in (src_file, "ck_device.hpp", "ck_internal.hpp", "ck_gemv_common.hpp"):
+    for f in (src_file, "ck_device.hpp", "ck_internal.hpp", "ck_gemv_common.hpp",
+              "ck_attn_common.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     src = h.hexdigest()[:16]
@@ -400,14 +543,39 @@ def recorded_traffic(kernel: str, workload: str, launches_bytes=None):
     return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, stack, nbytes):
     """The oracle (plain single-threaded C) on the host cores, on a bounded
     sample of the same workload: whole layers, cycling over the stack's layers
-    with the first layer's input, until the time budget is spent."""
+    with the first layer's input, until the time budget is spent. The process
+    is pinned to one core while the sample runs."""
     import numpy as np
 
     import oracle
     from decode_step_attention_layer_amd import synth
+
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[-1]
+    os.sched_setaffinity(0, {core})
+    try:
+        res = _cpu_sample(args, stack, nbytes, oracle, synth)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    res.update({"pinned_core": core, "nproc": os.cpu_count(), "cores_allowed": len(allowed),
+                "cpu_model": cpu_model()})
+    return res
+
+
+def _cpu_sample(args, stack, nbytes, oracle, synth):
 
     cfg = stack.cfg
     cos, sin = synth.rope_for(cfg)
@@ -438,7 +606,8 @@ def cpu_baseline(args, stack, nbytes):
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "us_per_layer": round(t_spent * 1e6 / done, 1),
             "sample": f"{done} whole-layer calls of the {workload_key(args)} workload "
-                      f"(layers cycled, first-layer input), {t_spent:.1f} s single-threaded"}
+                      f"(layers cycled, first-layer input), {t_spent:.1f} s single-threaded "
+                      f"on one pinned core"}
 
 
 if __name__ == "__main__":

@@ -38,7 +38,8 @@ EXPORTS = (
     "ck_decode_layer_ws_offset", "ck_decode_step_workspace_size", "ck_decode_step",
     "ck_decode_step_status_offset", "ck_decode_layer_devpos", "ck_decode_step_devpos",
     "ck_attn_sparse", "ck_decode_layer_sparse", "ck_decode_layer_noalloc",
-    "ck_decode_layer_noalloc_limit", "ck_decode_layer_part",
+    "ck_decode_layer_noalloc_limit", "ck_decode_layer_part", "ck_read_probe",
+    "ck_decode_layer_attn_plan",
 )
 
 
@@ -107,6 +108,9 @@ def load():
         "ck_decode_layer_workspace_size": ([ctypes.POINTER(CkLayerDesc), I], S),
         "ck_decode_layer": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                              ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, P], I),
+        "ck_read_probe": ([P, S, P, P], I),
+        "ck_decode_layer_attn_plan": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkKVCache),
+                                       IP, I, IP, IP], I),
         "ck_decode_layer_part": ([ctypes.POINTER(CkLayerDesc), ctypes.POINTER(CkLayerWeights),
                                   ctypes.POINTER(CkKVCache), P, P, IP, P, P, S, I, P], I),
         "ck_decode_layer_noalloc": ([ctypes.POINTER(CkLayerDesc),
@@ -258,6 +262,19 @@ def ck_decode_layer(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache
     _check(load().ck_decode_layer(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(cache),
                                   _ptr(x), _ptr(residual), _pos(pos), _ptr(out), _ptr(ws),
                                   ws_bytes, _stream(stream)), "ck_decode_layer")
+
+
+def ck_read_probe(src, nbytes, sink, stream=None):
+    _check(load().ck_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "ck_read_probe")
+
+
+def ck_decode_layer_attn_plan(desc: CkLayerDesc, cache: CkKVCache, pos, topk=0):
+    """(chunk, nchunks) of the attention a layer call plans at these positions."""
+    chunk, nchunks = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().ck_decode_layer_attn_plan(ctypes.byref(desc), ctypes.byref(cache), _pos(pos),
+                                            int(topk), ctypes.byref(chunk), ctypes.byref(nchunks)),
+           "ck_decode_layer_attn_plan")
+    return chunk.value, nchunks.value
 
 
 def ck_decode_layer_part(desc: CkLayerDesc, weights: CkLayerWeights, cache: CkKVCache, x, residual,

@@ -246,7 +246,16 @@ const char *ck_strerror(int code) {
     return "unknown error";
 }
 
-int ck_version(void) { return (0 << 16) | 1; }
+int ck_version(void) { return (0 << 16) | 2; }
+
+int ck_read_probe(const void *src, size_t bytes, void *sink, void *stream) {
+    if (!src || !sink || bytes == 0 || bytes % 16 || !al(src, 16) || !al(sink, 4))
+        return CK_EINVAL;
+    // a few workgroups per compute unit, each over one contiguous slice
+    const int nwg = 4 * num_cus();
+    return hip_rc(launch_read_probe(src, bytes, static_cast<unsigned *>(sink), nwg,
+                                    (hipStream_t)stream));
+}
 
 int ck_rmsnorm(const float *x, const float *gamma, float *y, int m, int D, float eps, void *stream) {
     if (!x || !gamma || !y || m < 1 || D <= 0 || !(eps >= 0.0f)) return CK_EINVAL;
@@ -315,7 +324,8 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
     AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, attended(mx, c.window),
-                            total_tokens(p, m, c.window), chunk);
+                            total_tokens(p, m, c.window), chunk,
+                            attn_matrix_path(H / c.kv_heads, c.dtype, false));
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream));
@@ -581,6 +591,20 @@ long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const cha
 
 namespace {
 
+// The attention split of one non-persistent layer call: it covers each
+// sequence's window only, or its selection. The chain and fused layers launch
+// the attention kernel (on the matrix cores for some shapes); the two-launch
+// layer plans for its own vector attention.
+AttnPlan layer_attn_plan(const ck_layer_desc &d, const CacheView &c, const Positions &p, int mx,
+                         const SparseSel *sp) {
+    const int amx = sp ? sp->topk : attended(mx, c.window);
+    const long long atot = sp ? (long long)d.m * sp->topk
+                              : (p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window));
+    const bool matrix = (d.variant == CK_VARIANT_CHAIN || d.variant == CK_VARIANT_FUSED) &&
+                        attn_matrix_path(d.H / d.KV, c.dtype, sp != nullptr);
+    return attn_plan(d.KV, d.H / d.KV, amx, atot, d.attn_chunk, matrix);
+}
+
 int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                       const float *x, const float *residual, const PosIn &pin, float *out,
                       void *ws, size_t ws_bytes, void *stream, const SparseSel *sp, int phases) {
@@ -612,11 +636,7 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     WsLayout L = ws_layout(desc, mx);
-    // the attention covers each sequence's window only, or its selection
-    const int amx = sp ? sp->topk : attended(mx, c.window);
-    const long long atot = sp ? (long long)d.m * sp->topk
-                              : (p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window));
-    const AttnPlan plan = attn_plan(d.KV, d.H / d.KV, amx, atot, d.attn_chunk);
+    const AttnPlan plan = layer_attn_plan(d, c, p, mx, sp);
     if (!attn_chunks_supported(plan.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < L.part + attn_partials_bytes(d.m, d.H, d.head_dim, plan.nchunks))
         return CK_ENOSPC;
@@ -739,6 +759,35 @@ int ck_decode_layer_sparse(const ck_layer_desc *desc, const ck_layer_weights *w,
     const SparseSel sp{sel, topk, sink};
     const PosIn pin = pos_host ? PosIn{pos_host, nullptr, 0} : PosIn{nullptr, pos_dev, max_ctx};
     return decode_layer_impl(desc, w, kv, x, residual, pin, out, ws, ws_bytes, stream, &sp);
+}
+
+int ck_decode_layer_attn_plan(const ck_layer_desc *desc, const ck_kv_cache *kv,
+                              const int32_t *pos_host, int topk, int *chunk, int *nchunks) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!pos_host || !chunk || !nchunks || topk < 0) return CK_EINVAL;
+    const ck_layer_desc &d = *desc;
+    CacheView c;
+    rc = cache_view(kv, &c);
+    if (rc) return rc;
+    if (c.kv_heads != d.KV || c.head_dim != d.head_dim) return CK_EINVAL;
+    if (topk && d.variant == CK_VARIANT_PERSISTENT) return CK_EUNSUPPORTED;
+    Positions p;
+    int mx;
+    long long total;
+    rc = resolve_positions(PosIn{pos_host, nullptr, 0}, d.m, cache_tokens(kv), &p, &mx, &total);
+    if (rc) return rc;
+    AttnPlan pl;
+    if (d.variant == CK_VARIANT_PERSISTENT) {
+        // the persistent step plans over every held token (no window)
+        pl = attn_plan(d.KV, d.H / d.KV, mx, total, d.attn_chunk);
+    } else {
+        const SparseSel sp{nullptr, topk, nullptr};
+        pl = layer_attn_plan(d, c, p, mx, topk ? &sp : nullptr);
+    }
+    *chunk = pl.chunk;
+    *nchunks = pl.nchunks;
+    return CK_OK;
 }
 
 int ck_decode_layer_part(const ck_layer_desc *desc, const ck_layer_weights *w,

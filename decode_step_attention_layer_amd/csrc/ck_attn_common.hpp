@@ -184,7 +184,11 @@ struct Smem {
     // the online-softmax state of every row group (NS of them): unnormalized
     // outputs, running max (log2 units), sum of exponentials; then the
     // weight of each state in the combination
-    float ro[NS][G][HD];
+    // rows padded by 4 floats: unpadded, the states of a wave's row groups
+    // (G*HD floats apart, a multiple of the 256 bytes the LDS banks span)
+    // all landed on the same banks (counters: 48% of the LDS cycles in
+    // conflict)
+    float ro[NS][G][HD + 4];
     float rm[NS][G];
     float rl[NS][G];
     float rw[NS][G];
@@ -492,6 +496,243 @@ __device__ __forceinline__ bool attn_item(const AttnArgs &a, int item, int g,
 #pragma unroll
         for (int i = 0; i < NS; i++) acc = fmaf(sm.ro[i][j][c], sm.rw[i][j], acc);
         part_store<COH>(&a.po[part * G * HD + idx], acc * vsc);
+    }
+    return true;
+}
+
+// --------------------------------------------------------------------------
+// The item on the fp32 matrix cores, for query groups of 5..8 heads over an
+// fp32 cache (no selection). There the group makes the scores Q K^T and the
+// weighted sum P V small dense contractions, and the vector path above is
+// bound by instruction issue: every score needs a 16-lane reduction, and
+// with one wave per SIMD nothing hides the dependent chains. Here a wave
+// takes 16 tokens per tile, and v_mfma_f32_16x16x4f32 computes
+//   S^T[token][head] = sum_d K[token][d] q[head][d]     (HD/4 instructions)
+//   O^T[dim][head]  += sum_t V[t][dim] P[t][head]        (HD/4 instructions)
+// with the group's heads in the 16 columns (heads >= G are zero). Lane l
+// (hl = l % 16, kq = l / 16) holds, by the operand layout of the
+// instruction (checked on the device): for the scores, K of token hl at
+// dims KD*kq .. KD*kq + KD - 1 and q of head hl at the same dims (the k
+// index of step i is dim KD*kq + i: a contraction may visit its index in
+// any order); it receives the scores of tokens 4*kq + r (r < 4) for head
+// hl. For P V, step s (< 4) contracts tokens 4*kq + s, so the lane's own
+// probability p[s] is its B operand, and its A operand is V of that token
+// at dims VD*hl .. VD*hl + VD - 1 for the VD output tiles (tile T covers
+// dims VD*m + T, m < 16): the lane ends holding, for head hl, the contiguous
+// dims 4*VD*kq .. 4*VD*kq + 4*VD - 1. K and V pieces are contiguous per
+// lane; the softmax statistics of a head are reduced over r in the lane and
+// over kq with two cross-lane exchanges. Each wave keeps one online softmax
+// per head; the NW waves' states are combined through LDS as above. A
+// workgroup has one wave per 16-token tile of its chunk (at most 4; longer
+// chunks give a wave every NW-th tile).
+template <int HD, int G, int NW>
+struct SmemM {
+    float ro[NW][G][HD + 4];
+    float rm[NW][G];
+    float rl[NW][G];
+    float rw[NW][G];
+    int pages[kPagesLds];
+    int bad;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int HD, int G, int NW, bool PAGED, bool STREAM, bool COH>
+__device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int g,
+                                               SmemM<HD, G, NW> &sm) {
+    static_assert(HD == 64 || HD == 128, "head size");
+    static_assert(G >= 1 && G <= 16 && NW >= 1 && NW <= 4, "query group, waves");
+    constexpr int NT = NW * kWave;
+    constexpr int KD = HD / 4;      // dims of a K row per lane (one per MFMA step)
+    constexpr int VD = HD / 16;     // dims of a V row per lane; output tiles
+    int s = 0;
+    while (s + 1 < a.m && item >= a.first[s + 1]) s++;
+    const int cidx = item - a.first[s];
+    const int L = a.pos.get(s) + 1;
+    const int t0 = window_start(L, a.c.window) + cidx * a.chunk;
+    if (t0 >= L) return false;       // device positions: items past this sequence's chunks
+    const int t1 = min(L, t0 + a.chunk);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane & 15, kq = lane >> 4;
+    const int KV = a.c.kv_heads;
+
+    if (tid == 0) sm.bad = 0;
+    int pg0 = 0;
+    bool pages_in_lds = false;
+    if (PAGED) {
+        const int ps = a.c.page_size;
+        pg0 = t0 / ps;
+        const int npg = (t1 - 1) / ps - pg0 + 1;
+        pages_in_lds = npg <= kPagesLds;
+        if (pages_in_lds)
+            for (int i = tid; i < npg; i += NT)
+                sm.pages[i] = a.c.table[(long long)s * a.c.max_pages + pg0 + i];
+    }
+    __syncthreads();
+    const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
+    bool bad = false;
+    auto row_off = [&](int t) -> long long {
+        if constexpr (PAGED) {
+            long long off = -1;
+            if (pages_in_lds) {
+                const int ps = a.c.page_size;
+                const int page = sm.pages[t / ps - pg0];
+                if (page >= 0 && page < a.c.num_pages)
+                    off = (((long long)page * KV + g) * ps + t % ps) * (long long)HD;
+            } else {
+                off = cache_row(a.c, s, g, t);
+            }
+            if (off < 0) bad = true;
+            return off < 0 ? 0 : off;
+        } else {
+            const int slot = a.c.ring ? t % a.c.capacity : t;
+            return (long long)(seq_base + (size_t)slot * HD);
+        }
+    };
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    auto ld4 = [](const float *p) -> float4 {
+        if constexpr (STREAM) {
+            const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(p));
+            return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                               __uint_as_float(v.w));
+        } else {
+            return *reinterpret_cast<const float4 *>(p);
+        }
+    };
+    const float *Kc = static_cast<const float *>(a.c.k);
+    const float *Vc = static_cast<const float *>(a.c.v);
+
+    // q of head hl (zero for the padding heads), dims KD*kq.., in log2 units
+    float qr[KD];
+    {
+        const float qs = a.scale * kLog2e;
+        const float *qh = a.q + ((size_t)s * a.H + (size_t)g * G + min(hl, G - 1)) * HD + KD * kq;
+        const float z = hl < G ? qs : 0.0f;
+#pragma unroll
+        for (int i = 0; i < KD; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(qh + i);
+            qr[i] = v.x * z;
+            qr[i + 1] = v.y * z;
+            qr[i + 2] = v.z * z;
+            qr[i + 3] = v.w * z;
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 o[VD];
+#pragma unroll
+    for (int T = 0; T < VD; T++) o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ntile = (t1 - t0 + 15) / 16;
+    for (int tile = wave; tile < ntile; tile += NW) {
+        const int tb = t0 + 16 * tile;
+        // every load first, unconditional (tokens past the chunk re-read its
+        // last row and are masked)
+        float kr[KD];
+        {
+            const float *kp = Kc + row_off(min(tb + hl, t1 - 1)) + KD * kq;
+#pragma unroll
+            for (int i = 0; i < KD; i += 4) {
+                const float4 v = ld4(kp + i);
+                kr[i] = v.x;
+                kr[i + 1] = v.y;
+                kr[i + 2] = v.z;
+                kr[i + 3] = v.w;
+            }
+        }
+        float vr[4][VD];
+#pragma unroll
+        for (int sidx = 0; sidx < 4; sidx++) {
+            const float *vp = Vc + row_off(min(tb + 4 * kq + sidx, t1 - 1)) + VD * hl;
+#pragma unroll
+            for (int T = 0; T < VD; T += 4) {
+                const float4 v = ld4(vp + T);
+                vr[sidx][T] = v.x;
+                vr[sidx][T + 1] = v.y;
+                vr[sidx][T + 2] = v.z;
+                vr[sidx][T + 3] = v.w;
+            }
+        }
+        // scores of tokens tb + 4kq + r for head hl
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KD; i++) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i], qr[i], sc, 0, 0, 0);
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) sv[r] = (tb + 4 * kq + r < t1) ? sc[r] : -INFINITY;
+        float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m_run, mt);
+        const float mr = mn == -INFINITY ? 0.0f : mn;
+        const float alpha = exp2f(m_run - mr);
+        float p[4], ps = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            p[r] = exp2f(sv[r] - mr);
+            ps += p[r];
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l_run = l_run * alpha + ps;
+        m_run = mn;
+        // V of a token past the chunk adds nothing (it re-reads a row that
+        // may hold anything, an infinity included)
+#pragma unroll
+        for (int sidx = 0; sidx < 4; sidx++) {
+            const bool ok = tb + 4 * kq + sidx < t1;
+#pragma unroll
+            for (int T = 0; T < VD; T++) vr[sidx][T] = ok ? vr[sidx][T] : 0.0f;
+        }
+#pragma unroll
+        for (int T = 0; T < VD; T++) {
+            o[T] *= alpha;
+#pragma unroll
+            for (int sidx = 0; sidx < 4; sidx++)
+                o[T] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[sidx][T], p[sidx], o[T], 0, 0, 0);
+        }
+    }
+
+    // the waves' states through LDS: o[T][r] is dim VD*(4kq + r) + T
+    if (bad) sm.bad = 1;
+    if (hl < G) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+#pragma unroll
+            for (int T = 0; T < VD; T += 4)
+                *reinterpret_cast<float4 *>(&sm.ro[wave][hl][VD * (4 * kq + r) + T]) =
+                    make_float4(o[T][r], o[T + 1][r], o[T + 2][r], o[T + 3][r]);
+        if (kq == 0) {
+            sm.rm[wave][hl] = m_run;
+            sm.rl[wave][hl] = l_run;
+        }
+    }
+    __syncthreads();
+    const size_t part = ((size_t)s * KV + g) * a.nchunks + cidx;
+    if (tid < G) {
+        const int j = tid;
+        float M = sm.rm[0][j];
+#pragma unroll
+        for (int w = 1; w < NW; w++) M = fmaxf(M, sm.rm[w][j]);
+        const float Mr = M == -INFINITY ? 0.0f : M;
+        float ls = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+            const float wt = exp2f(sm.rm[w][j] - Mr);
+            sm.rw[w][j] = wt;
+            ls = fmaf(sm.rl[w][j], wt, ls);
+        }
+        part_store<COH>(&a.pml[(part * G + j) * 2 + 0], M);
+        part_store<COH>(&a.pml[(part * G + j) * 2 + 1], sm.bad ? NAN : ls);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * HD; idx += NT) {
+        const int j = idx / HD, c = idx % HD;
+        float acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) acc = fmaf(sm.ro[w][j][c], sm.rw[w][j], acc);
+        part_store<COH>(&a.po[part * G * HD + idx], acc);
     }
     return true;
 }

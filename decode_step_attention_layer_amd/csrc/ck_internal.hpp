@@ -185,7 +185,15 @@ struct AttnPlan {
 // Chunks are whole steps of the attention kernel (attn_step tokens, which
 // depends on the query group size G).
 int attn_step(int G);
-AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req);
+// Whether the attention launch of a query group of G heads runs on the
+// matrix cores: groups over 4 heads attending an fp32 cache with no selection.
+bool attn_matrix_path(int G, int dtype, bool selection);
+// `matrix`: the plan is for that kernel. Its automatic chunks are not doubled
+// (the doubling evens out the vector kernel's load across compute units);
+// callers whose plan another call must reproduce without the cache type (a
+// separate merge) leave it false.
+AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req,
+                   bool matrix = false);
 int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req);
 // Tokens attended over all sequences (host positions), under a window.
 long long total_tokens(const Positions &p, int m, int window);
@@ -228,6 +236,11 @@ hipError_t launch_ato(const float *q, const CacheView &c, const Positions &pos, 
                       float scale, const AttnPlan &plan, void *partials, float *attn_out,
                       uint8_t *aq, void *aqx, const uint8_t *wo, const float *bo,
                       const float *residual, float *out, int D, unsigned *cnt, hipStream_t st);
+
+// A plain streaming read of `bytes` (a multiple of 16) by nwg workgroups
+// (k_probe.hip); sink: nwg words, written only for an impossible value.
+hipError_t launch_read_probe(const void *src, size_t bytes, unsigned *sink, int nwg,
+                             hipStream_t st);
 
 // Persistent decode step (k_step.hip): every layer of a step in one launch.
 struct StepLayer {

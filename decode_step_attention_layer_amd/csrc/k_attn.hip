@@ -36,6 +36,7 @@
 // by the last workgroup to finish needs an agent-scope release per
 // workgroup, an L2 write-back on this GPU; measured, it cost more than the
 // kernel boundary.)
+
 #include "ck_attn_common.hpp"
 
 namespace ck {
@@ -50,6 +51,36 @@ template <int HD, int G, bool PAGED, int DT, bool STREAM>
 __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
     __shared__ Smem<HD, G, kAttnNS<DT, HD, G>> sm;
     attn_item<HD, G, PAGED, DT, STREAM, false>(a, blockIdx.x, blockIdx.y, sm);
+}
+
+// The same on the fp32 matrix cores (query groups of 5 to 8 heads, fp32
+// cache, no selection): same grid, same partials.
+template <int HD, int G, int NW, bool PAGED, bool STREAM>
+__global__ __launch_bounds__(NW * kWave) void k_attn_mfma(AttnArgs a) {
+    __shared__ SmemM<HD, G, NW> sm;
+    attn_item_mfma<HD, G, NW, PAGED, STREAM, false>(a, blockIdx.x, blockIdx.y, sm);
+}
+
+// one wave per 16-token tile of a chunk, at most four
+template <int HD, int G, int NW>
+void launch_mfma_nw(const AttnArgs &a, dim3 grid, bool paged, bool nt, hipStream_t st) {
+    const dim3 blk(NW * kWave);
+    if (paged) {
+        if (nt) hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, true, true>), grid, blk, 0, st, a);
+        else hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, true, false>), grid, blk, 0, st, a);
+    } else {
+        if (nt) hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, false, true>), grid, blk, 0, st, a);
+        else hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, false, false>), grid, blk, 0, st, a);
+    }
+}
+
+template <int HD, int G>
+void launch_mfma(const AttnArgs &a, dim3 grid, bool paged, bool nt, hipStream_t st) {
+    const int tiles = (a.chunk + 15) / 16;
+    if (tiles <= 1) launch_mfma_nw<HD, G, 1>(a, grid, paged, nt, st);
+    else if (tiles == 2) launch_mfma_nw<HD, G, 2>(a, grid, paged, nt, st);
+    else if (tiles == 3) launch_mfma_nw<HD, G, 3>(a, grid, paged, nt, st);
+    else launch_mfma_nw<HD, G, 4>(a, grid, paged, nt, st);
 }
 
 struct MergeArgs {
@@ -319,6 +350,13 @@ hipError_t launch_t(const AttnArgs &a, int m, bool paged, hipStream_t st) {
     // 128-wide heads, where the streaming variant takes 11 more registers
     // and measured slower per step (the 7B shape, 96-token chunks).
     const bool nt = a.chunk >= kNtChunk || !(HD == 128 && G > 4);
+    if constexpr (G >= 5) {
+        // query groups of 5 to 8 heads over an fp32 cache: the matrix cores
+        if (attn_matrix_path(G, dt, a.sel != nullptr)) {
+            launch_mfma<HD, G>(a, grid, paged, nt, st);
+            return hipGetLastError();
+        }
+    }
 #define CK_ATTN_LAUNCH(P, D)                                                                   \
     do {                                                                                       \
         if (nt) hipLaunchKernelGGL((k_attn<HD, G, P, D, true>), grid, dim3(NT), 0, st, a);     \
@@ -377,9 +415,17 @@ bool attn_shape_supported(int G, int hd) {
 
 bool attn_chunks_supported(int nchunks) { return nchunks >= 1 && nchunks <= kMaxChunks; }
 
-int attn_step(int G) { return G > 4 ? AttnShape<8>::step : AttnShape<1>::step; }
+// Query groups over 4 heads run on the matrix cores in tiles of 16 tokens
+// (fp32 caches; other caches keep the vector kernel, whose 48-token steps
+// then mask the rows past a chunk).
+int attn_step(int G) { return G > 4 ? 16 : AttnShape<1>::step; }
 
-AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req) {
+bool attn_matrix_path(int G, int dtype, bool selection) {
+    return G > 4 && dtype == CK_KV_F32 && !selection;
+}
+
+AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req,
+                   bool matrix) {
     AttnPlan p;
     const int step = attn_step(G);
     if (chunk_req > 0) {
@@ -395,10 +441,13 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
         // between one and one and a half workgroups per compute unit, the
         // units holding two set the time: twice the chunk gives every busy
         // unit the same work in half the workgroups (and half the partials
-        // to merge)
+        // to merge). The matrix-core kernel is left as it is: its time per
+        // chunk grows with the chunk's 16-token tiles (measured at 4097
+        // tokens x 4 KV heads, 128-wide heads: 9.97 us at 48-token chunks
+        // against 11.27 at 96, where the vector kernel gains from 96).
         const long long items = (total_tokens + p.chunk - 1) / p.chunk * KV;
         const long long cus = cus_of_current_device();
-        if (items > cus && 2 * items <= 3 * cus) p.chunk *= 2;
+        if (!matrix && items > cus && 2 * items <= 3 * cus) p.chunk *= 2;
     }
     if (p.chunk < step) p.chunk = step;
     p.nchunks = (max_tokens + p.chunk - 1) / p.chunk;

@@ -209,7 +209,11 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
  * out_q8 is not NULL, also writes the Q8_0 blocks of out (the quantization
  * done before the O projection). Both validate like ck_attn_decode_gqa; the
  * merge must see the same pos_host, m, H, KV, hd and chunk as the partial,
- * and as window the window of the partial's cache (0 = none). */
+ * and as window the window of the partial's cache (0 = none). The automatic
+ * split (chunk 0) of this pair depends on neither the cache type nor the
+ * kernel, so it can differ from ck_attn_decode_gqa's, which for query groups
+ * over 4 heads on an fp32 cache sizes chunks for its matrix-core kernel:
+ * with equal explicit chunks the two give identical bits. */
 int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, int m, int H,
                     float scale, int chunk, void *partials, size_t bytes, void *stream);
 int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, int m, int H,
@@ -267,6 +271,17 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w,
                     const ck_kv_cache *kv, const float *x, const float *residual,
                     const int32_t *pos_host, float *out, void *ws, size_t ws_bytes,
                     void *stream);
+
+/* The attention split a layer call plans for the given host positions
+ * (ck_decode_layer, its devpos form at those positions, the step's layers;
+ * topk > 0: ck_decode_layer_sparse with that many selected tokens): *chunk
+ * tokens per chunk and *nchunks chunks for the longest sequence. Passing
+ * *chunk to ck_attn_partial or ck_attn_decode_gqa runs the attention as the
+ * layer does. Host-side only; CK_EINVAL / CK_EUNSUPPORTED as the layer call
+ * would for the descriptor, cache and positions (topk with the persistent
+ * variant: CK_EUNSUPPORTED). */
+int ck_decode_layer_attn_plan(const ck_layer_desc *desc, const ck_kv_cache *kv,
+                              const int32_t *pos_host, int topk, int *chunk, int *nchunks);
 
 /* The layer of ck_decode_layer in two calls on the same workspace, for
  * callers that interleave other work with the halves or time them apart:
@@ -339,6 +354,14 @@ long ck_decode_layer_ws_offset(const ck_layer_desc *desc, int max_ctx, const cha
 /* "status" (CK_VARIANT_TWO_LAUNCH only, else -1): the uint32 status word of
  * the layer's second launch, zero after a call whose waits completed and
  * non-zero if one timed out (read it after synchronizing). */
+
+/* Measurement utility: a plain streaming read of `bytes` (a multiple of 16)
+ * at src with 16-byte non-temporal loads, four workgroups per compute unit
+ * each over one contiguous slice: the achievable HBM read bandwidth to set
+ * beside the nominal peak. sink: device memory of 4 * (4 * compute units)
+ * bytes, written only in the impossible case that the folded words match a
+ * fixed pattern. */
+int ck_read_probe(const void *src, size_t bytes, void *sink, void *stream);
 
 /* Allocation-free decode layer, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that

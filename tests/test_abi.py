@@ -67,6 +67,73 @@ def test_gemv_validation(ck):
     assert L.ck_rmsnorm(FAKE, None, FAKE, 1, 64, 1e-6, st) == ck.CK_EINVAL
 
 
+def test_read_probe_validation(ck):
+    L = ck.load()
+    assert L.ck_read_probe(None, 4096, FAKE, None) == ck.CK_EINVAL
+    assert L.ck_read_probe(FAKE, 4096, None, None) == ck.CK_EINVAL
+    assert L.ck_read_probe(FAKE, 0, FAKE, None) == ck.CK_EINVAL
+    assert L.ck_read_probe(FAKE, 4100, FAKE, None) == ck.CK_EINVAL      # not whole 16 bytes
+    assert L.ck_read_probe(FAKE + 8, 4096, FAKE, None) == ck.CK_EINVAL  # src not 16-aligned
+    assert L.ck_read_probe(FAKE, 4096, FAKE + 2, None) == ck.CK_EINVAL  # sink not 4-aligned
+
+
+def _up256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_layer_attention_plan(ck):
+    """The split a layer plans (host-side; with no GPU visible the plan takes
+    256 compute units): whole 16-token tiles for query groups over 4 heads,
+    the automatic chunk left undoubled for the matrix-core kernel of the chain
+    and fused layers and doubled where the vector kernel runs (other cache
+    types, the two-launch and persistent layers); every plan covers the
+    longest sequence and fits the attention workspace sized for it."""
+    V = (ck.CK_VARIANT_CHAIN, ck.CK_VARIANT_FUSED, ck.CK_VARIANT_TWO_LAUNCH,
+         ck.CK_VARIANT_PERSISTENT)
+    d = lambda v, H=28, KV=4, m=1, chunk=0: ck.layer_desc(H * 128, H, KV, 128, m, variant=v,
+                                                         attn_chunk=chunk)
+    c32 = ck.CkKVCache(FAKE, FAKE, 4, 128, 8192, 0, None, 0, 0)
+    cbf = ck.CkKVCache(FAKE, FAKE, 4, 128, 8192, 0, None, 0, 0, ck.CK_KV_BF16)
+    plan = ck.ck_decode_layer_attn_plan
+    # 4097 tokens x 4 KV heads over 2 x 256 workgroups: 33 tokens, 3 tiles
+    assert plan(d(ck.CK_VARIANT_FUSED), c32, [4096]) == (48, 86)
+    assert plan(d(ck.CK_VARIANT_CHAIN), c32, [4096]) == (48, 86)
+    assert plan(d(ck.CK_VARIANT_TWO_LAUNCH), c32, [4096]) == (96, 43)
+    assert plan(d(ck.CK_VARIANT_PERSISTENT), c32, [4096]) == (96, 43)
+    assert plan(d(ck.CK_VARIANT_FUSED), cbf, [4096]) == (96, 43)
+    # an explicit chunk is rounded up to whole steps: 16 tokens for groups of
+    # 7 heads, 64 for groups of 4
+    assert plan(d(ck.CK_VARIANT_FUSED, chunk=40), c32, [4096]) == (48, 86)
+    c8 = ck.CkKVCache(FAKE, FAKE, 8, 128, 40000, 0, None, 0, 0)
+    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8, chunk=40), c8, [4096]) == (64, 65)
+    for H, KV, cache in ((28, 4, c32), (28, 4, cbf), (32, 8, c8)):
+        step = 16 if H // KV > 4 else 64
+        for v in V:
+            for pos in ([0], [15], [16], [47], [1023], [4096], [8190], [100, 7000, 3]):
+                if max(pos) >= cache.capacity:
+                    continue
+                m = len(pos)
+                chunk, n = plan(d(v, H=H, KV=KV, m=m), cache, pos)
+                assert chunk % step == 0 and chunk >= step, (H, v, pos, chunk)
+                assert (n - 1) * chunk < max(pos) + 1 <= n * chunk, (H, v, pos, chunk, n)
+                need = _up256(4 * m * H * n * 128) + _up256(4 * m * H * n * 2)
+                assert need <= ck.ck_attn_workspace_size(m, H, KV, 128, max(pos) + 1, 0)
+        # a selection of 256 tokens: the plan covers the selection
+        chunk, n = plan(d(ck.CK_VARIANT_FUSED, H=H, KV=KV), cache, [2000], topk=256)
+        assert (n - 1) * chunk < 256 <= n * chunk
+    L = ck.load()
+    out = (ctypes.c_int32 * 1)()
+    pos = (ctypes.c_int32 * 1)(4096)
+    assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_PERSISTENT)),
+                                       ctypes.byref(c32), pos, 16, out, out) == ck.CK_EUNSUPPORTED
+    assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_FUSED)), ctypes.byref(c32),
+                                       pos, 0, None, out) == ck.CK_EINVAL
+    assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_FUSED)), ctypes.byref(c32),
+                                       (ctypes.c_int32 * 1)(8192), 0, out, out) == ck.CK_EINVAL
+    assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_FUSED, KV=7, H=28)),
+                                       ctypes.byref(c32), pos, 0, out, out) == ck.CK_EINVAL
+
+
 def test_rope_and_append_validation(ck):
     L = ck.load()
     pos = (ctypes.c_int32 * 2)(5, 64)

@@ -17,7 +17,10 @@ layer received:
     causes through Wo (|Wo[e, j]| times the code step), and of the plain
     oracle, plus the oracle-evaluated effect of the xq flips;
   * every KV-cache slot except the appended one is byte-identical (NaN poison
-    included), and the appended slot holds exactly the k, v the layer computed.
+    included), and the appended slot holds exactly the k, v the layer computed;
+  * chain and fused: the attention called on its own at the split the layer
+    reports planning (ck_decode_layer_attn_plan) reproduces the layer's
+    attention output bit for bit.
 The persistent variant runs here as one-layer persistent steps (the same
 kernel as a whole step, with one layer's items); the two-launch variant
 (attention, merge and O projection in one launch) also leaves its status
@@ -82,6 +85,8 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
         ck.ck_decode_layer(desc, L.weights, L.cache, x_gpu_in, x_gpu_in, pos, out, ws, ws.numel())
         torch.cuda.synchronize()
         got = host(out)
+        if variant in (0, 1):
+            _attention_at_reported_plan(ck, desc, stack, L, ws, pos, f"{name} layer {li}")
         if variant == 3:
             soff = ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, "status")
             assert soff >= 0 and int(ws[soff:soff + 4].view(torch.int32).item()) == 0, \
@@ -117,6 +122,30 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
     e2e = assert_close_rms(x_host, x_orc, bound, f"{name} end to end")
     print(f"{name} variant={variant}: layers={len(stack.layers)} e2e rel err {e2e:.2e} "
           f"(bound {bound:.2e}, branch RMS {rms(x_orc - stack.x0_host):.3f})")
+
+
+def _attention_at_reported_plan(ck, desc, stack, L, ws, pos, tag):
+    """The chain and fused layers run the attention kernels: called on their
+    own, on the layer's q (from the workspace) and the appended cache, at the
+    split ck_decode_layer_attn_plan reports, they give the layer's attention
+    output bit for bit (the scale rounded as the layer rounds it)."""
+    import torch
+
+    cfg = stack.cfg
+    m, H, KV, hd = cfg.m, cfg.H, cfg.KV, cfg.hd
+    chunk, nchunks = ck.ck_decode_layer_attn_plan(desc, L.cache, pos)
+    assert (nchunks - 1) * chunk < max(pos) + 1 <= nchunks * chunk, (tag, chunk, nchunks)
+    qoff = ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, "q")
+    aoff = ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, "attn")
+    nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, chunk)
+    aw = torch.empty(nws, dtype=torch.uint8, device=ws.device)
+    ao = torch.empty(m * H * hd, dtype=torch.float32, device=ws.device)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(hd)))
+    ck.ck_attn_decode_gqa(ws.data_ptr() + qoff, L.cache, pos, ao, m, H, scale, chunk, aw, nws)
+    torch.cuda.synchronize()
+    layer_attn = _ws_read(ws, aoff, 4 * m * H * hd, np.float32)
+    assert np.array_equal(host(ao).view(np.uint32), layer_attn.view(np.uint32)), \
+        f"{tag}: attention at the reported split (chunk {chunk}) differs from the layer's"
 
 
 def ocache(cfg, L, k, v):

@@ -324,27 +324,31 @@ def test_attention_split_count_independent():
 
 def test_attention_two_pass_entry_points_match():
     """ck_attn_partial + ck_attn_merge give exactly what ck_attn_decode_gqa
-    gives (same kernels), and the merge's Q8_0 output is the quantizer's."""
+    gives (same kernels), and the merge's Q8_0 output is the quantizer's.
+    Groups of 4 heads with the automatic split; groups of 8 (the matrix-core
+    kernel, whose automatic split differs between the two) with an explicit
+    one."""
     dev = cuda()
     ck = _ck()
-    m, H, KV, hd, L = 3, 32, 8, 128, 900
+    m, KV, hd, L = 3, 8, 128, 900
     cfg, k, v, table, pos, oc = _caches(True, m, KV, hd, L, 6)
     pos = [p - 1 for p in pos]
     c, kd, vd, td = _dev_cache(ck, dev, cfg, k, v, table)
-    q = _t(synth.seeded_vector(5, m * H * hd), dev)
     import torch
 
-    nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, 0)
-    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
-    a = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
-    b = torch.empty_like(a)
-    bq = torch.empty(m * H * hd // 32 * 34, dtype=torch.uint8, device=dev)
-    ck.ck_attn_decode_gqa(q, c, pos, a, m, H, 1.0 / np.sqrt(hd), 0, ws, nws)
-    ck.ck_attn_partial(q, c, pos, m, H, 1.0 / np.sqrt(hd), 0, ws, nws)
-    ck.ck_attn_merge(ws, nws, pos, m, H, KV, hd, 0, b, bq)
-    _sync()
-    assert torch.equal(a, b)
-    assert np.array_equal(host(bq), oracle.quantize_q8_0(host(b)))
+    for H, chunk in ((32, 0), (64, 64)):
+        q = _t(synth.seeded_vector(5, m * H * hd), dev)
+        nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, chunk)
+        ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+        a = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        bq = torch.empty(m * H * hd // 32 * 34, dtype=torch.uint8, device=dev)
+        ck.ck_attn_decode_gqa(q, c, pos, a, m, H, 1.0 / np.sqrt(hd), chunk, ws, nws)
+        ck.ck_attn_partial(q, c, pos, m, H, 1.0 / np.sqrt(hd), chunk, ws, nws)
+        ck.ck_attn_merge(ws, nws, pos, m, H, KV, hd, chunk, b, bq)
+        _sync()
+        assert torch.equal(a, b), H
+        assert np.array_equal(host(bq), oracle.quantize_q8_0(host(b)))
 
 
 def test_attention_workspace_reuse():
