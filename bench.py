@@ -83,12 +83,15 @@ def parse():
 
 def workload_key(args) -> str:
     """Short name of the timed workload: the configuration, plus the cache's
-    element type, window and ring when they differ from the defaults."""
+    element type, window, ring, selection and layer variant when they differ
+    from the defaults."""
     key = args.config if args.kv == "f32" else f"{args.config}-{args.kv}"
     if args.window:
         key += f"-w{args.window}" + ("-ring" if args.ring else "")
     if args.topk:
         key += f"-top{args.topk}"
+    if getattr(args, "variant", "fused") != "fused":
+        key += f"-{args.variant}"
     return key
 
 

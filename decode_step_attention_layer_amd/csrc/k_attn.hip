@@ -28,9 +28,13 @@
 // combined by log-sum-exp through LDS into the chunk's (max, sum,
 // unnormalized output) per head, the partials. K/V rows stream with
 // non-temporal loads (each row is read once), except in short chunks of
-// large query groups with 128-wide heads. A second
-// kernel, one workgroup per (head, sequence) (one or two wavefronts where a
-// sequence has at most 64 chunks), merges the chunks by log-sum-exp with all
+// large query groups with 128-wide heads. Query groups of 5 to 8 heads over
+// an fp32 cache (no selection) take the same grid and partials on the fp32
+// matrix cores (k_attn_mfma): per 16-token tile, the scores of the whole
+// group and the value sums are 16x16x4 MFMA contractions, one wave per tile
+// of the chunk (at most four). A second
+// kernel, one workgroup per (head, sequence) (one wavefront per 32 chunks
+// where a sequence has at most 128), merges the chunks by log-sum-exp with all
 // chunks' loads in flight at once (the sink joins here), writes the attention
 // output and, optionally, its Q8_0 blocks. (Merging inside the first kernel
 // by the last workgroup to finish needs an agent-scope release per
@@ -529,25 +533,33 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
     b.sink = sp ? sp->sink : nullptr;
     b.out = out;
     b.out_q8 = out_q8;
-    // at most 32 chunks per sequence: the one-wavefront merge; up to 64: two
-    // wavefronts, 32 chunks each (measured faster than the workgroup merge
-    // at 22 and 43 chunks, neutral at 57; one wavefront for 43 or 57 chunks
-    // measured slower: its serial loads cost more than the barriers save)
-    if (plan.nchunks <= kMerge1Chunks) {
-        if (hd == 64)
-            hipLaunchKernelGGL((k_attn_merge1<64, 1>), dim3(H, m), dim3(kWave), 0, st, b);
-        else
-            hipLaunchKernelGGL((k_attn_merge1<128, 1>), dim3(H, m), dim3(kWave), 0, st, b);
-    } else if (plan.nchunks <= 2 * kMerge1Chunks) {
-        if (hd == 64)
-            hipLaunchKernelGGL((k_attn_merge1<64, 2>), dim3(H, m), dim3(2 * kWave), 0, st, b);
-        else
-            hipLaunchKernelGGL((k_attn_merge1<128, 2>), dim3(H, m), dim3(2 * kWave), 0, st, b);
+    // up to 128 chunks per sequence: one wavefront per 32 chunks (measured
+    // faster than the workgroup merge at 22 and 43 chunks with one and two
+    // wavefronts, neutral at 57, and faster at 86 with three: 4.4 against
+    // 4.9 us at the 7B shape; one wavefront for 43 or 57 chunks measured
+    // slower: its serial loads cost more than the barriers save); beyond,
+    // the workgroup merge
+    const int nwv = (plan.nchunks + kMerge1Chunks - 1) / kMerge1Chunks;
+#define CK_MERGE1(HD_, NWV_) \
+    hipLaunchKernelGGL((k_attn_merge1<HD_, NWV_>), dim3(H, m), dim3(NWV_ * kWave), 0, st, b)
+    if (nwv <= 4) {
+        if (hd == 64) {
+            if (nwv <= 1) CK_MERGE1(64, 1);
+            else if (nwv == 2) CK_MERGE1(64, 2);
+            else if (nwv == 3) CK_MERGE1(64, 3);
+            else CK_MERGE1(64, 4);
+        } else {
+            if (nwv <= 1) CK_MERGE1(128, 1);
+            else if (nwv == 2) CK_MERGE1(128, 2);
+            else if (nwv == 3) CK_MERGE1(128, 3);
+            else CK_MERGE1(128, 4);
+        }
     } else if (hd == 64) {
         hipLaunchKernelGGL(k_attn_merge<64>, dim3(H, m), dim3(kMergeThreads), 0, st, b);
     } else {
         hipLaunchKernelGGL(k_attn_merge<128>, dim3(H, m), dim3(kMergeThreads), 0, st, b);
     }
+#undef CK_MERGE1
     return hipGetLastError();
 }
 

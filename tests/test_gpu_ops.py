@@ -257,13 +257,15 @@ ATTN_CASES = [
     (1, 32, 8, 128, 32769, 0, False),
     (4, 32, 8, 128, 700, 0, True),
     (3, 8, 1, 64, 90, 64, True),
-    # more than 64 chunks per sequence (the workgroup merge), and past its
-    # 16 preloaded chunk slots per thread (128 chunks at hd 128, 256 at hd 64)
+    # 65-128 chunks per sequence (three and four merge wavefronts), more
+    # than 128 (the workgroup merge), and past its 16 preloaded chunk slots
+    # per thread (128 chunks at hd 128, 256 at hd 64)
     (1, 28, 4, 128, 6000, 0, False),       # the automatic plan: 125 chunks of 48
     (1, 28, 4, 128, 9000, 48, False),      # 188 chunks
     (1, 14, 2, 64, 4097, 64, False),       # 65 chunks
     (1, 8, 1, 64, 20000, 64, False),       # 313 chunks
     (4, 32, 8, 128, 5000, 64, True),       # paged, m = 4: up to 79 chunks
+    (1, 32, 8, 128, 6500, 64, False),      # 102 chunks
 ]
 
 

@@ -4,11 +4,12 @@ the oracle.
   * ck_attn_sparse on contiguous, paged and ring caches, one to four
     sequences, selections with duplicates and -1 padding, with and without a
     sink: within 1e-4 x RMS of the oracle per sequence; also with selections
-    split into more than 64 chunks (the workgroup merge, with and without a
-    sink);
+    split into 65-128 chunks (the three- and four-wavefront merges) and more
+    (the workgroup merge), with and without a sink;
   * with a fixed split, padding a selection with -1 (even whole chunks of it)
     changes nothing, bit for bit, and the selection of every token in order
-    without a sink is the dense attention, bit for bit;
+    without a sink is the dense attention (bit for bit where both run the
+    vector kernel, within fp32 rounding against the matrix-core kernel);
   * an entry past its sequence makes that sequence's outputs NaN and leaves
     the others' alone; an all -1 selection gives zeros, with or without a sink;
   * ck_decode_layer_sparse (chain and fused) over a decode loop: out within
@@ -143,19 +144,22 @@ def test_sparse_attention(layout, m, H, KV, hd, pos, topk, R, with_sink):
 
 
 MANY_CHUNK_CASES = [
-    # layout, m, H, KV, hd, positions, topk, chunk, sink: more than 64 chunks
-    # per sequence (the workgroup merge), past its first 16 preloaded slots per
-    # thread (16 x 8 chunks for 128-wide heads, 16 x 16 for 64-wide)
+    # layout, m, H, KV, hd, positions, topk, chunk, sink: more than 128
+    # chunks per sequence (the workgroup merge), past its first 16 preloaded
+    # slots per thread (16 x 8 chunks for 128-wide heads, 16 x 16 for
+    # 64-wide); 65-128 chunks (three and four merge wavefronts)
     ("contig", 1, 28, 4, 128, [9000], 8000, 48, True),
     ("contig", 1, 8, 2, 64, [20000], 18000, 64, True),
     ("paged", 2, 32, 8, 128, [5000, 3000], 4500, 64, False),
+    ("contig", 1, 28, 4, 128, [9000], 4000, 48, True),     # 84 chunks
+    ("contig", 1, 8, 2, 64, [20000], 8000, 64, True),      # 125 chunks
 ]
 
 
 @pytest.mark.parametrize("layout,m,H,KV,hd,pos,topk,chunk,with_sink", MANY_CHUNK_CASES, ids=str)
 def test_sparse_attention_many_chunks(layout, m, H, KV, hd, pos, topk, chunk, with_sink):
-    """Selections split into more chunks than the one- and two-wavefront
-    merges take: the workgroup merge, with and without a sink, against the
+    """Selections split into many chunks: the three- and four-wavefront
+    merges and the workgroup merge, with and without a sink, against the
     oracle within 1e-4."""
     from decode_step_attention_layer_amd import ck
 
