@@ -511,20 +511,21 @@ __device__ __forceinline__ bool attn_item(const AttnArgs &a, int item, int g,
 //   O^T[dim][head]  += sum_t V[t][dim] P[t][head]        (HD/4 instructions)
 // with the group's heads in the 16 columns (heads >= G are zero). Lane l
 // (hl = l % 16, kq = l / 16) holds, by the operand layout of the
-// instruction (checked on the device): for the scores, K of token hl at
-// dims KD*kq .. KD*kq + KD - 1 and q of head hl at the same dims (the k
-// index of step i is dim KD*kq + i: a contraction may visit its index in
-// any order); it receives the scores of tokens 4*kq + r (r < 4) for head
-// hl. For P V, step s (< 4) contracts tokens 4*kq + s, so the lane's own
-// probability p[s] is its B operand, and its A operand is V of that token
-// at dims VD*hl .. VD*hl + VD - 1 for the VD output tiles (tile T covers
-// dims VD*m + T, m < 16): the lane ends holding, for head hl, the contiguous
-// dims 4*VD*kq .. 4*VD*kq + 4*VD - 1. K and V pieces are contiguous per
-// lane; the softmax statistics of a head are reduced over r in the lane and
-// over kq with two cross-lane exchanges. Each wave keeps one online softmax
-// per head; the NW waves' states are combined through LDS as above. A
-// workgroup has one wave per 16-token tile of its chunk (at most 4; longer
-// chunks give a wave every NW-th tile).
+// instruction (checked on the device): for the scores, at step 4j + e, K
+// of token hl and q of head hl at dim 16j + 4kq + e (a contraction may
+// visit its index in any order: this one lets the four lanes of a token
+// read 64 adjacent bytes of its row per load); it receives the scores of
+// tokens 4*kq + r (r < 4) for head hl. For P V, step s (< 4) contracts
+// tokens 4*kq + s, so the lane's own probability p[s] is its B operand, and
+// its A operand is V of that token at dims 64b + 4hl + e for the VD output
+// tiles T = 4b + e (tile T covers dims 64b + 4m + e, m < 16; the 16 lanes
+// of a token read 256 adjacent bytes of its row per load): the lane ends
+// holding, for head hl, dims 64b + 16kq + 4r + e. The softmax statistics of
+// a head are reduced over r in the lane and over kq with two cross-lane
+// exchanges. Each wave keeps one online softmax per head; the NW waves'
+// states are combined through LDS as above. A workgroup has one wave per
+// 16-token tile of its chunk (at most 8; longer chunks give a wave every
+// NW-th tile).
 template <int HD, int G, int NW>
 struct SmemM {
     float ro[NW][G][HD + 4];
@@ -541,7 +542,7 @@ template <int HD, int G, int NW, bool PAGED, bool STREAM, bool COH>
 __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int g,
                                                SmemM<HD, G, NW> &sm) {
     static_assert(HD == 64 || HD == 128, "head size");
-    static_assert(G >= 1 && G <= 16 && NW >= 1 && NW <= 4, "query group, waves");
+    static_assert(G >= 1 && G <= 16 && NW >= 1 && NW <= 8, "query group, waves");
     constexpr int NT = NW * kWave;
     constexpr int KD = HD / 4;      // dims of a K row per lane (one per MFMA step)
     constexpr int VD = HD / 16;     // dims of a V row per lane; output tiles
@@ -572,6 +573,7 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
     }
     __syncthreads();
     const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
+    const int slot0 = (!PAGED && a.c.ring) ? t0 % a.c.capacity : t0;
     bool bad = false;
     auto row_off = [&](int t) -> long long {
         if constexpr (PAGED) {
@@ -587,7 +589,10 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
             if (off < 0) bad = true;
             return off < 0 ? 0 : off;
         } else {
-            const int slot = a.c.ring ? t % a.c.capacity : t;
+            // a chunk's tokens are consecutive and fit in the ring: its first
+            // slot, then at most one wrap
+            int slot = slot0 + (t - t0);
+            if (slot >= a.c.capacity) slot -= a.c.capacity;
             return (long long)(seq_base + (size_t)slot * HD);
         }
     };
@@ -604,21 +609,24 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
     const float *Kc = static_cast<const float *>(a.c.k);
     const float *Vc = static_cast<const float *>(a.c.v);
 
-    // q of head hl (zero for the padding heads), dims KD*kq.., in log2 units
+    // q of head hl at the dims of the lane's K pieces: 16j + 4kq + e for
+    // step 4j + e. The padding heads (hl >= G) repeat head G - 1: their
+    // columns are never read, and stay finite. The scale (with log2 e) is
+    // applied to the scores, so that nothing waits for q before the K/V
+    // loads go out.
     float qr[KD];
     {
-        const float qs = a.scale * kLog2e;
-        const float *qh = a.q + ((size_t)s * a.H + (size_t)g * G + min(hl, G - 1)) * HD + KD * kq;
-        const float z = hl < G ? qs : 0.0f;
+        const float *qh = a.q + ((size_t)s * a.H + (size_t)g * G + min(hl, G - 1)) * HD + 4 * kq;
 #pragma unroll
         for (int i = 0; i < KD; i += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(qh + i);
-            qr[i] = v.x * z;
-            qr[i + 1] = v.y * z;
-            qr[i + 2] = v.z * z;
-            qr[i + 3] = v.w * z;
+            const float4 v = *reinterpret_cast<const float4 *>(qh + 4 * i);
+            qr[i] = v.x;
+            qr[i + 1] = v.y;
+            qr[i + 2] = v.z;
+            qr[i + 3] = v.w;
         }
     }
+    const float qs = a.scale * kLog2e;
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 o[VD];
@@ -628,13 +636,17 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
     for (int tile = wave; tile < ntile; tile += NW) {
         const int tb = t0 + 16 * tile;
         // every load first, unconditional (tokens past the chunk re-read its
-        // last row and are masked)
+        // last row and are masked). K of token tb + hl: the four lanes of a
+        // row read 64 adjacent bytes per instruction (dims 16j + 4kq..), 16
+        // rows per instruction. V of tokens tb + 4kq + sidx: the 16 lanes of
+        // a row read 256 adjacent bytes per instruction (dims 64b + 4hl..),
+        // 4 rows per instruction.
         float kr[KD];
         {
-            const float *kp = Kc + row_off(min(tb + hl, t1 - 1)) + KD * kq;
+            const float *kp = Kc + row_off(min(tb + hl, t1 - 1)) + 4 * kq;
 #pragma unroll
             for (int i = 0; i < KD; i += 4) {
-                const float4 v = ld4(kp + i);
+                const float4 v = ld4(kp + 4 * i);
                 kr[i] = v.x;
                 kr[i + 1] = v.y;
                 kr[i + 2] = v.z;
@@ -644,23 +656,25 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         float vr[4][VD];
 #pragma unroll
         for (int sidx = 0; sidx < 4; sidx++) {
-            const float *vp = Vc + row_off(min(tb + 4 * kq + sidx, t1 - 1)) + VD * hl;
+            const float *vp = Vc + row_off(min(tb + 4 * kq + sidx, t1 - 1)) + 4 * hl;
 #pragma unroll
             for (int T = 0; T < VD; T += 4) {
-                const float4 v = ld4(vp + T);
+                const float4 v = ld4(vp + 16 * T);
                 vr[sidx][T] = v.x;
                 vr[sidx][T + 1] = v.y;
                 vr[sidx][T + 2] = v.z;
                 vr[sidx][T + 3] = v.w;
             }
         }
-        // scores of tokens tb + 4kq + r for head hl
+        // keep the loads together ahead of the arithmetic (left alone, the
+        // scheduler spreads them among the MFMAs and waits for each)
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < KD; i++) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i], qr[i], sc, 0, 0, 0);
         float sv[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) sv[r] = (tb + 4 * kq + r < t1) ? sc[r] : -INFINITY;
+        for (int r = 0; r < 4; r++) sv[r] = (tb + 4 * kq + r < t1) ? sc[r] * qs : -INFINITY;
         float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -694,14 +708,14 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         }
     }
 
-    // the waves' states through LDS: o[T][r] is dim VD*(4kq + r) + T
+    // the waves' states through LDS: o[4b + e][r] is dim 64b + 16kq + 4r + e
     if (bad) sm.bad = 1;
     if (hl < G) {
 #pragma unroll
         for (int r = 0; r < 4; r++)
 #pragma unroll
             for (int T = 0; T < VD; T += 4)
-                *reinterpret_cast<float4 *>(&sm.ro[wave][hl][VD * (4 * kq + r) + T]) =
+                *reinterpret_cast<float4 *>(&sm.ro[wave][hl][16 * T + 16 * kq + 4 * r]) =
                     make_float4(o[T][r], o[T + 1][r], o[T + 2][r], o[T + 3][r]);
         if (kq == 0) {
             sm.rm[wave][hl] = m_run;

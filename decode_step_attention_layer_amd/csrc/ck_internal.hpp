@@ -188,10 +188,10 @@ int attn_step(int G);
 // Whether the attention launch of a query group of G heads runs on the
 // matrix cores: groups over 4 heads attending an fp32 cache with no selection.
 bool attn_matrix_path(int G, int dtype, bool selection);
-// `matrix`: the plan is for that kernel. Its automatic chunks are not doubled
-// (the doubling evens out the vector kernel's load across compute units);
-// callers whose plan another call must reproduce without the cache type (a
-// separate merge) leave it false.
+// `matrix`: the plan is for that kernel, whose automatic split aims at one
+// workgroup per compute unit (the vector kernel's at about two); callers
+// whose plan another call must reproduce without the cache type (a separate
+// merge) leave it false.
 AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req,
                    bool matrix = false);
 int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req);

@@ -32,7 +32,7 @@
 // an fp32 cache (no selection) take the same grid and partials on the fp32
 // matrix cores (k_attn_mfma): per 16-token tile, the scores of the whole
 // group and the value sums are 16x16x4 MFMA contractions, one wave per tile
-// of the chunk (at most four). A second
+// of the chunk (at most eight). A second
 // kernel, one workgroup per (head, sequence) (one wavefront per 32 chunks
 // where a sequence has at most 128), merges the chunks by log-sum-exp with all
 // chunks' loads in flight at once (the sink joins here), writes the attention
@@ -65,26 +65,40 @@ __global__ __launch_bounds__(NW * kWave) void k_attn_mfma(AttnArgs a) {
     attn_item_mfma<HD, G, NW, PAGED, STREAM, false>(a, blockIdx.x, blockIdx.y, sm);
 }
 
-// one wave per 16-token tile of a chunk, at most four
+constexpr int kMfmaMaxWaves = 8;
+
+// One wave per 16-token tile of a chunk, at most eight (longer chunks give a
+// wave every eighth tile). 128-wide heads stream their rows only from chunks
+// of kNtChunk tokens (see launch_t), which take eight waves.
 template <int HD, int G, int NW>
-void launch_mfma_nw(const AttnArgs &a, dim3 grid, bool paged, bool nt, hipStream_t st) {
+void launch_mfma_nw(const AttnArgs &a, dim3 grid, bool paged, hipStream_t st) {
+    constexpr bool NT = HD == 64;
     const dim3 blk(NW * kWave);
-    if (paged) {
-        if (nt) hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, true, true>), grid, blk, 0, st, a);
-        else hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, true, false>), grid, blk, 0, st, a);
-    } else {
-        if (nt) hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, false, true>), grid, blk, 0, st, a);
-        else hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, false, false>), grid, blk, 0, st, a);
-    }
+    if (paged) hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, true, NT>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, false, NT>), grid, blk, 0, st, a);
 }
 
 template <int HD, int G>
 void launch_mfma(const AttnArgs &a, dim3 grid, bool paged, bool nt, hipStream_t st) {
     const int tiles = (a.chunk + 15) / 16;
-    if (tiles <= 1) launch_mfma_nw<HD, G, 1>(a, grid, paged, nt, st);
-    else if (tiles == 2) launch_mfma_nw<HD, G, 2>(a, grid, paged, nt, st);
-    else if (tiles == 3) launch_mfma_nw<HD, G, 3>(a, grid, paged, nt, st);
-    else launch_mfma_nw<HD, G, 4>(a, grid, paged, nt, st);
+    if (HD == 128 && nt) {
+        const dim3 blk(kMfmaMaxWaves * kWave);
+        if (paged)
+            hipLaunchKernelGGL((k_attn_mfma<HD, G, kMfmaMaxWaves, true, true>), grid, blk, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_attn_mfma<HD, G, kMfmaMaxWaves, false, true>), grid, blk, 0, st, a);
+        return;
+    }
+    switch (tiles < kMfmaMaxWaves ? tiles : kMfmaMaxWaves) {
+        case 1: launch_mfma_nw<HD, G, 1>(a, grid, paged, st); break;
+        case 2: launch_mfma_nw<HD, G, 2>(a, grid, paged, st); break;
+        case 3: launch_mfma_nw<HD, G, 3>(a, grid, paged, st); break;
+        case 4: launch_mfma_nw<HD, G, 4>(a, grid, paged, st); break;
+        case 5: launch_mfma_nw<HD, G, 5>(a, grid, paged, st); break;
+        case 6: launch_mfma_nw<HD, G, 6>(a, grid, paged, st); break;
+        case 7: launch_mfma_nw<HD, G, 7>(a, grid, paged, st); break;
+        default: launch_mfma_nw<HD, G, 8>(a, grid, paged, st); break;
+    }
 }
 
 struct MergeArgs {
@@ -434,6 +448,17 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
     const int step = attn_step(G);
     if (chunk_req > 0) {
         p.chunk = (chunk_req + step - 1) / step * step;
+    } else if (matrix) {
+        // the matrix-core kernel: about one workgroup per compute unit over
+        // all (sequence, KV head, chunk) items, a wave per 16-token tile. Its
+        // waves hold one tile each and compute only once their loads have
+        // landed, so a unit holding two workgroups sets the time (measured
+        // at 4097 tokens x 4 KV heads, 128-wide heads: 9.2 us at 80-token
+        // chunks, 208 workgroups, against 10.0 at 48, 344 workgroups)
+        if (total_tokens < max_tokens) total_tokens = max_tokens;
+        const long long cus = cus_of_current_device();
+        const long long c = (total_tokens * KV + cus - 1) / cus;
+        p.chunk = (int)((c + step - 1) / step * step);
     } else {
         // about two workgroups per compute unit over all (sequence, KV head,
         // chunk) items: chunks are sized from the tokens of every sequence,
@@ -445,13 +470,10 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
         // between one and one and a half workgroups per compute unit, the
         // units holding two set the time: twice the chunk gives every busy
         // unit the same work in half the workgroups (and half the partials
-        // to merge). The matrix-core kernel is left as it is: its time per
-        // chunk grows with the chunk's 16-token tiles (measured at 4097
-        // tokens x 4 KV heads, 128-wide heads: 9.97 us at 48-token chunks
-        // against 11.27 at 96, where the vector kernel gains from 96).
+        // to merge)
         const long long items = (total_tokens + p.chunk - 1) / p.chunk * KV;
         const long long cus = cus_of_current_device();
-        if (!matrix && items > cus && 2 * items <= 3 * cus) p.chunk *= 2;
+        if (items > cus && 2 * items <= 3 * cus) p.chunk *= 2;
     }
     if (p.chunk < step) p.chunk = step;
     p.nchunks = (max_tokens + p.chunk - 1) / p.chunk;
@@ -462,7 +484,8 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
 int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req) {
     // the largest nchunks attn_plan returns for any positions with at most
     // max_tokens tokens per sequence: the chunk is at least
-    // max_tokens * KV / (2 CUs), so nchunks <= ceil(2 CUs / KV)
+    // max_tokens * KV / (2 CUs) (the matrix kernel's twice that), so
+    // nchunks <= ceil(2 CUs / KV)
     if (chunk_req > 0) return attn_plan(KV, G, max_tokens, max_tokens, chunk_req).nchunks;
     const int target = 2 * cus_of_current_device();
     const int by_items = (target + KV - 1) / KV;

@@ -84,10 +84,11 @@ def _up256(n):
 def test_layer_attention_plan(ck):
     """The split a layer plans (host-side; with no GPU visible the plan takes
     256 compute units): whole 16-token tiles for query groups over 4 heads,
-    the automatic chunk left undoubled for the matrix-core kernel of the chain
-    and fused layers and doubled where the vector kernel runs (other cache
-    types, the two-launch and persistent layers); every plan covers the
-    longest sequence and fits the attention workspace sized for it."""
+    about one workgroup per compute unit for the matrix-core kernel of the
+    chain and fused layers, about two where the vector kernel runs (other
+    cache types, the two-launch and persistent layers; doubled when between
+    one and one and a half); every plan covers the longest sequence and fits
+    the attention workspace sized for it."""
     V = (ck.CK_VARIANT_CHAIN, ck.CK_VARIANT_FUSED, ck.CK_VARIANT_TWO_LAUNCH,
          ck.CK_VARIANT_PERSISTENT)
     d = lambda v, H=28, KV=4, m=1, chunk=0: ck.layer_desc(H * 128, H, KV, 128, m, variant=v,
@@ -95,9 +96,10 @@ def test_layer_attention_plan(ck):
     c32 = ck.CkKVCache(FAKE, FAKE, 4, 128, 8192, 0, None, 0, 0)
     cbf = ck.CkKVCache(FAKE, FAKE, 4, 128, 8192, 0, None, 0, 0, ck.CK_KV_BF16)
     plan = ck.ck_decode_layer_attn_plan
-    # 4097 tokens x 4 KV heads over 2 x 256 workgroups: 33 tokens, 3 tiles
-    assert plan(d(ck.CK_VARIANT_FUSED), c32, [4096]) == (48, 86)
-    assert plan(d(ck.CK_VARIANT_CHAIN), c32, [4096]) == (48, 86)
+    # 4097 tokens x 4 KV heads over 256 workgroups: 65 tokens, 5 tiles
+    assert plan(d(ck.CK_VARIANT_FUSED), c32, [4096]) == (80, 52)
+    assert plan(d(ck.CK_VARIANT_CHAIN), c32, [4096]) == (80, 52)
+    # over 2 x 256 workgroups: 33 tokens, 3 tiles of 16, doubled
     assert plan(d(ck.CK_VARIANT_TWO_LAUNCH), c32, [4096]) == (96, 43)
     assert plan(d(ck.CK_VARIANT_PERSISTENT), c32, [4096]) == (96, 43)
     assert plan(d(ck.CK_VARIANT_FUSED), cbf, [4096]) == (96, 43)
