@@ -527,11 +527,10 @@ __device__ __forceinline__ bool attn_item(const AttnArgs &a, int item, int g,
 // 16-token tile of its chunk (at most 8; longer chunks give a wave every
 // NW-th tile).
 template <int HD, int G, int NW>
-struct SmemM {
+struct alignas(16) SmemM {
     float ro[NW][G][HD + 4];
     float rm[NW][G];
     float rl[NW][G];
-    float rw[NW][G];
     int pages[kPagesLds];
     int bad;
 };
@@ -723,30 +722,37 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         }
     }
     __syncthreads();
+    // every thread weighs the waves' states of its own output slice (the
+    // same arithmetic for every slice of a head, so no second barrier):
+    // partials of the chunk, and the chunk's (max, sum) from each head's
+    // first slice
     const size_t part = ((size_t)s * KV + g) * a.nchunks + cidx;
-    if (tid < G) {
-        const int j = tid;
+    const bool any_bad = sm.bad != 0;
+    for (int i4 = tid; i4 < G * HD / 4; i4 += NT) {
+        const int j = i4 / (HD / 4), c = 4 * (i4 % (HD / 4));
         float M = sm.rm[0][j];
 #pragma unroll
         for (int w = 1; w < NW; w++) M = fmaxf(M, sm.rm[w][j]);
         const float Mr = M == -INFINITY ? 0.0f : M;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         float ls = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; w++) {
             const float wt = exp2f(sm.rm[w][j] - Mr);
-            sm.rw[w][j] = wt;
             ls = fmaf(sm.rl[w][j], wt, ls);
+            const float4 v = *reinterpret_cast<const float4 *>(&sm.ro[w][j][c]);
+            acc = make_float4(fmaf(v.x, wt, acc.x), fmaf(v.y, wt, acc.y), fmaf(v.z, wt, acc.z),
+                              fmaf(v.w, wt, acc.w));
         }
-        part_store<COH>(&a.pml[(part * G + j) * 2 + 0], M);
-        part_store<COH>(&a.pml[(part * G + j) * 2 + 1], sm.bad ? NAN : ls);
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * HD; idx += NT) {
-        const int j = idx / HD, c = idx % HD;
-        float acc = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; w++) acc = fmaf(sm.ro[w][j][c], sm.rw[w][j], acc);
-        part_store<COH>(&a.po[part * G * HD + idx], acc);
+        float *po = &a.po[part * G * HD + (size_t)j * HD + c];
+        part_store<COH>(po + 0, acc.x);
+        part_store<COH>(po + 1, acc.y);
+        part_store<COH>(po + 2, acc.z);
+        part_store<COH>(po + 3, acc.w);
+        if (c == 0) {
+            part_store<COH>(&a.pml[(part * G + j) * 2 + 0], M);
+            part_store<COH>(&a.pml[(part * G + j) * 2 + 1], any_bad ? NAN : ls);
+        }
     }
     return true;
 }
