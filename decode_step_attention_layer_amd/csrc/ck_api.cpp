@@ -323,9 +323,10 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, attended(mx, c.window),
-                            total_tokens(p, m, c.window), chunk,
-                            attn_matrix_path(H / c.kv_heads, c.dtype, false));
+    const int G = H / c.kv_heads;
+    const bool matrix = attn_matrix_path(G, c.dtype, false);
+    AttnPlan pl = attn_plan(c.kv_heads, G, attended(mx, c.window), total_tokens(p, m, c.window),
+                            chunk, attn_step(G, c.dtype, matrix), matrix);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attention(q, c, p, out, nullptr, m, H, scale, pl, ws, (hipStream_t)stream));
@@ -343,8 +344,10 @@ int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_ho
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
+    // the merge reproduces this plan without the cache type
     AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, attended(mx, c.window),
-                            total_tokens(p, m, c.window), chunk);
+                            total_tokens(p, m, c.window), chunk, attn_step(H / c.kv_heads, -1, false),
+                            false);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attn_partial(q, c, p, m, H, scale, pl, partials, (hipStream_t)stream));
@@ -361,7 +364,8 @@ int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, i
     int mx;
     int rc = read_positions(pos_host, m, 1LL << 30, &p, &mx);
     if (rc) return rc;
-    AttnPlan pl = attn_plan(KV, H / KV, attended(mx, window), total_tokens(p, m, window), chunk);
+    AttnPlan pl = attn_plan(KV, H / KV, attended(mx, window), total_tokens(p, m, window), chunk,
+                            attn_step(H / KV, -1, false), false);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (bytes < attn_partials_bytes(m, H, hd, pl.nchunks)) return CK_ENOSPC;
     return hip_rc(launch_attn_merge(partials, p, window, m, H, KV, hd, pl, out,
@@ -383,7 +387,8 @@ int ck_attn_sparse(const float *q, const ck_kv_cache *kv, const int32_t *pos_hos
     int mx;
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
-    const AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, topk, (long long)m * topk, chunk);
+    const AttnPlan pl = attn_plan(c.kv_heads, H / c.kv_heads, topk, (long long)m * topk, chunk,
+                                  attn_step(H / c.kv_heads, c.dtype, false), false);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
     if (ws_bytes < attn_partials_bytes(m, H, c.head_dim, pl.nchunks)) return CK_ENOSPC;
     const SparseSel sp{sel, topk, sink};
@@ -416,6 +421,13 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
                       const float *x, const float *residual, const PosIn &pin, float *out,
                       void *ws, size_t ws_bytes, void *stream, const SparseSel *sp = nullptr,
                       int phases = 3);
+
+// The attention split of the persistent step: fp32 caches without a window,
+// the vector kernel's step.
+AttnPlan persistent_attn_plan(const ck_layer_desc &d, int mx, long long total) {
+    const int G = d.H / d.KV;
+    return attn_plan(d.KV, G, mx, total, d.attn_chunk, attn_step(G, CK_KV_F32, false), false);
+}
 
 int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
                      int layers, const float *x, const PosIn &pin, float *out, void *ws,
@@ -453,7 +465,7 @@ int decode_step_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const
     rc = resolve_positions(pin, d.m, limit, &p, &mx, &total);
     if (rc) return rc;
     StepWs L = step_layout(desc, layers, mx);
-    const AttnPlan plan = attn_plan(d.KV, d.H / d.KV, mx, total, d.attn_chunk);
+    const AttnPlan plan = persistent_attn_plan(d, mx, total);
     if (ws_bytes < L.total) return CK_ENOSPC;
     hipStream_t st = (hipStream_t)stream;
     uint8_t *base = static_cast<uint8_t *>(ws);
@@ -600,9 +612,10 @@ AttnPlan layer_attn_plan(const ck_layer_desc &d, const CacheView &c, const Posit
     const int amx = sp ? sp->topk : attended(mx, c.window);
     const long long atot = sp ? (long long)d.m * sp->topk
                               : (p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window));
+    const int G = d.H / d.KV;
     const bool matrix = (d.variant == CK_VARIANT_CHAIN || d.variant == CK_VARIANT_FUSED) &&
-                        attn_matrix_path(d.H / d.KV, c.dtype, sp != nullptr);
-    return attn_plan(d.KV, d.H / d.KV, amx, atot, d.attn_chunk, matrix);
+                        attn_matrix_path(G, c.dtype, sp != nullptr);
+    return attn_plan(d.KV, G, amx, atot, d.attn_chunk, attn_step(G, c.dtype, matrix), matrix);
 }
 
 int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, const ck_kv_cache *kv,
@@ -771,7 +784,11 @@ int ck_decode_layer_attn_plan(const ck_layer_desc *desc, const ck_kv_cache *kv,
     rc = cache_view(kv, &c);
     if (rc) return rc;
     if (c.kv_heads != d.KV || c.head_dim != d.head_dim) return CK_EINVAL;
-    if (topk && d.variant == CK_VARIANT_PERSISTENT) return CK_EUNSUPPORTED;
+    // the persistent step takes fp32 caches without window or ring, and no
+    // selection
+    if (d.variant == CK_VARIANT_PERSISTENT &&
+        (topk || c.dtype != CK_KV_F32 || c.window != 0 || c.ring))
+        return CK_EUNSUPPORTED;
     Positions p;
     int mx;
     long long total;
@@ -779,8 +796,7 @@ int ck_decode_layer_attn_plan(const ck_layer_desc *desc, const ck_kv_cache *kv,
     if (rc) return rc;
     AttnPlan pl;
     if (d.variant == CK_VARIANT_PERSISTENT) {
-        // the persistent step plans over every held token (no window)
-        pl = attn_plan(d.KV, d.H / d.KV, mx, total, d.attn_chunk);
+        pl = persistent_attn_plan(d, mx, total);
     } else {
         const SparseSel sp{nullptr, topk, nullptr};
         pl = layer_attn_plan(d, c, p, mx, topk ? &sp : nullptr);

@@ -29,7 +29,7 @@ struct AttnArgs {
     CacheView c;
     Positions pos;
     float scale;
-    int chunk;            // tokens per chunk, a multiple of the kernel's step
+    int chunk;            // tokens per chunk (rows past a chunk are masked)
     int nchunks;
     int H;
     float *po;            // [m][KV][nchunks][G][HD]  unnormalized outputs

@@ -182,18 +182,20 @@ struct AttnPlan {
     int chunk;
     int nchunks;
 };
-// Chunks are whole steps of the attention kernel (attn_step tokens, which
-// depends on the query group size G).
-int attn_step(int G);
+// Tokens per step of the attention kernel that runs a query group of G heads
+// over a cache of type dtype (CK_KV_*), on the matrix cores if `matrix`;
+// dtype < 0: whichever runs (a common multiple of their steps), for plans
+// that another call must reproduce without knowing the cache.
+int attn_step(int G, int dtype, bool matrix);
 // Whether the attention launch of a query group of G heads runs on the
 // matrix cores: groups over 4 heads attending an fp32 cache with no selection.
 bool attn_matrix_path(int G, int dtype, bool selection);
-// `matrix`: the plan is for that kernel, whose automatic split aims at one
-// workgroup per compute unit (the vector kernel's at about two); callers
-// whose plan another call must reproduce without the cache type (a separate
-// merge) leave it false.
-AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req,
-                   bool matrix = false);
+// The split of the attended tokens. An explicit chunk_req is used as given
+// (every kernel masks the rows past a chunk); the automatic chunk is a whole
+// number of `step`s sized for the kernel: with `matrix`, about one
+// workgroup per compute unit, otherwise about two.
+AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req, int step,
+                   bool matrix);
 int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req);
 // Tokens attended over all sequences (host positions), under a window.
 long long total_tokens(const Positions &p, int m, int window);

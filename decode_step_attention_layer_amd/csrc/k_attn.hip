@@ -433,21 +433,25 @@ bool attn_shape_supported(int G, int hd) {
 
 bool attn_chunks_supported(int nchunks) { return nchunks >= 1 && nchunks <= kMaxChunks; }
 
-// Query groups over 4 heads run on the matrix cores in tiles of 16 tokens
-// (fp32 caches; other caches keep the vector kernel, whose 48-token steps
-// then mask the rows past a chunk).
-int attn_step(int G) { return G > 4 ? 16 : AttnShape<1>::step; }
+// The vector kernel's step: 4 waves x load rounds (3 for groups over 4
+// heads) x rows per round (8 for fp8 rows of groups up to 4 heads, held by
+// 8 lanes each; otherwise 4). The matrix-core kernel's: 16-token tiles.
+int attn_step(int G, int dtype, bool matrix) {
+    if (matrix) return 16;
+    const int waves = 4, rounds = G > 4 ? 3 : 4;
+    if (dtype < 0) return waves * rounds * (G > 4 ? 4 : 8);   // 48 or 128: all of them
+    return waves * rounds * ((dtype == CK_KV_FP8_E4M3 && G <= 4) ? 8 : 4);
+}
 
 bool attn_matrix_path(int G, int dtype, bool selection) {
     return G > 4 && dtype == CK_KV_F32 && !selection;
 }
 
-AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req,
+AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int chunk_req, int step,
                    bool matrix) {
     AttnPlan p;
-    const int step = attn_step(G);
     if (chunk_req > 0) {
-        p.chunk = (chunk_req + step - 1) / step * step;
+        p.chunk = chunk_req;
     } else if (matrix) {
         // the matrix-core kernel: about one workgroup per compute unit over
         // all (sequence, KV head, chunk) items, a wave per 16-token tile. Its
@@ -475,7 +479,7 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
         const long long cus = cus_of_current_device();
         if (items > cus && 2 * items <= 3 * cus) p.chunk *= 2;
     }
-    if (p.chunk < step) p.chunk = step;
+    if (chunk_req <= 0 && p.chunk < step) p.chunk = step;
     p.nchunks = (max_tokens + p.chunk - 1) / p.chunk;
     if (p.nchunks < 1) p.nchunks = 1;
     return p;
@@ -483,13 +487,14 @@ AttnPlan attn_plan(int KV, int G, int max_tokens, long long total_tokens, int ch
 
 int attn_max_chunks(int KV, int G, int max_tokens, int chunk_req) {
     // the largest nchunks attn_plan returns for any positions with at most
-    // max_tokens tokens per sequence: the chunk is at least
-    // max_tokens * KV / (2 CUs) (the matrix kernel's twice that), so
-    // nchunks <= ceil(2 CUs / KV)
-    if (chunk_req > 0) return attn_plan(KV, G, max_tokens, max_tokens, chunk_req).nchunks;
+    // max_tokens tokens per sequence: an explicit chunk is used as given;
+    // the automatic chunk is at least max_tokens * KV / (2 CUs) (the matrix
+    // kernel's twice that) and at least the smallest step of a kernel for
+    // this group size, so nchunks <= ceil(2 CUs / KV)
+    if (chunk_req > 0) return (max_tokens + chunk_req - 1) / chunk_req;
     const int target = 2 * cus_of_current_device();
     const int by_items = (target + KV - 1) / KV;
-    const int step = attn_step(G);
+    const int step = G > 4 ? 16 : 64;
     const int by_tile = (max_tokens + step - 1) / step;
     return by_tile < by_items ? by_tile : by_items;
 }

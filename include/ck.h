@@ -209,11 +209,13 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
  * out_q8 is not NULL, also writes the Q8_0 blocks of out (the quantization
  * done before the O projection). Both validate like ck_attn_decode_gqa; the
  * merge must see the same pos_host, m, H, KV, hd and chunk as the partial,
- * and as window the window of the partial's cache (0 = none). The automatic
- * split (chunk 0) of this pair depends on neither the cache type nor the
- * kernel, so it can differ from ck_attn_decode_gqa's, which for query groups
- * over 4 heads on an fp32 cache sizes chunks for its matrix-core kernel:
- * with equal explicit chunks the two give identical bits. */
+ * and as window the window of the partial's cache (0 = none). An explicit
+ * chunk is used as given. The automatic split (chunk 0) of this pair depends
+ * on neither the cache type nor the kernel, so it can differ from
+ * ck_attn_decode_gqa's, which sizes chunks for the kernel that runs (the
+ * matrix-core kernel for query groups over 4 heads on an fp32 cache, whole
+ * steps of the vector kernel otherwise): with equal explicit chunks the two
+ * give identical bits. */
 int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, int m, int H,
                     float scale, int chunk, void *partials, size_t bytes, void *stream);
 int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, int m, int H,
@@ -278,8 +280,9 @@ int ck_decode_layer(const ck_layer_desc *desc, const ck_layer_weights *w,
  * tokens per chunk and *nchunks chunks for the longest sequence. Passing
  * *chunk to ck_attn_partial or ck_attn_decode_gqa runs the attention as the
  * layer does. Host-side only; CK_EINVAL / CK_EUNSUPPORTED as the layer call
- * would for the descriptor, cache and positions (topk with the persistent
- * variant: CK_EUNSUPPORTED). */
+ * would for the descriptor, cache and positions (with the persistent
+ * variant: a selection, or a cache other than fp32 without window or ring,
+ * CK_EUNSUPPORTED). */
 int ck_decode_layer_attn_plan(const ck_layer_desc *desc, const ck_kv_cache *kv,
                               const int32_t *pos_host, int topk, int *chunk, int *nchunks);
 

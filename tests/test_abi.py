@@ -103,14 +103,26 @@ def test_layer_attention_plan(ck):
     assert plan(d(ck.CK_VARIANT_TWO_LAUNCH), c32, [4096]) == (96, 43)
     assert plan(d(ck.CK_VARIANT_PERSISTENT), c32, [4096]) == (96, 43)
     assert plan(d(ck.CK_VARIANT_FUSED), cbf, [4096]) == (96, 43)
-    # an explicit chunk is rounded up to whole steps: 16 tokens for groups of
-    # 7 heads, 64 for groups of 4
-    assert plan(d(ck.CK_VARIANT_FUSED, chunk=40), c32, [4096]) == (48, 86)
+    # an explicit chunk is used as given
+    assert plan(d(ck.CK_VARIANT_FUSED, chunk=40), c32, [4096]) == (40, 103)
     c8 = ck.CkKVCache(FAKE, FAKE, 8, 128, 40000, 0, None, 0, 0)
-    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8, chunk=40), c8, [4096]) == (64, 65)
-    for H, KV, cache in ((28, 4, c32), (28, 4, cbf), (32, 8, c8)):
-        step = 16 if H // KV > 4 else 64
+    c8f8 = ck.CkKVCache(FAKE, FAKE, 8, 128, 40000, 0, None, 0, 0, ck.CK_KV_FP8_E4M3, 1.0, 1.0)
+    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8, chunk=40), c8, [4096]) == (40, 103)
+    # 32769 tokens x 8 KV heads over 2 x 256 workgroups: 513 tokens, whole
+    # steps of the vector kernel: 576 = 9 x 64 (fp32), 640 = 5 x 128 (fp8,
+    # whose rows take 8 lanes, 8 rows a round)
+    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8), c8, [32768]) == (576, 57)
+    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8), c8f8, [32768]) == (640, 52)
+    for H, KV, cache in ((28, 4, c32), (28, 4, cbf), (32, 8, c8), (32, 8, c8f8)):
         for v in V:
+            if v == ck.CK_VARIANT_PERSISTENT and cache.dtype != ck.CK_KV_F32:
+                continue          # fp32 caches only
+            if H // KV > 4:
+                matrix = cache.dtype == ck.CK_KV_F32 and v in (ck.CK_VARIANT_CHAIN,
+                                                               ck.CK_VARIANT_FUSED)
+                step = 16 if matrix else 48
+            else:
+                step = 128 if cache.dtype == ck.CK_KV_FP8_E4M3 else 64
             for pos in ([0], [15], [16], [47], [1023], [4096], [8190], [100, 7000, 3]):
                 if max(pos) >= cache.capacity:
                     continue
@@ -128,6 +140,8 @@ def test_layer_attention_plan(ck):
     pos = (ctypes.c_int32 * 1)(4096)
     assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_PERSISTENT)),
                                        ctypes.byref(c32), pos, 16, out, out) == ck.CK_EUNSUPPORTED
+    assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_PERSISTENT)),
+                                       ctypes.byref(cbf), pos, 0, out, out) == ck.CK_EUNSUPPORTED
     assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_FUSED)), ctypes.byref(c32),
                                        pos, 0, None, out) == ck.CK_EINVAL
     assert L.ck_decode_layer_attn_plan(ctypes.byref(d(ck.CK_VARIANT_FUSED)), ctypes.byref(c32),

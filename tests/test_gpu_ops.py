@@ -326,10 +326,9 @@ def test_attention_split_count_independent():
 
 def test_attention_two_pass_entry_points_match():
     """ck_attn_partial + ck_attn_merge give exactly what ck_attn_decode_gqa
-    gives (same kernels), and the merge's Q8_0 output is the quantizer's.
-    Groups of 4 heads with the automatic split; groups of 8 (the matrix-core
-    kernel, whose automatic split differs between the two) with an explicit
-    one."""
+    gives at the same explicit split (same kernels), and the merge's Q8_0
+    output is the quantizer's. Groups of 4 heads (the vector kernel) and of 8
+    (the matrix-core kernel); the automatic splits of the two may differ."""
     dev = cuda()
     ck = _ck()
     m, KV, hd, L = 3, 8, 128, 900
@@ -338,7 +337,7 @@ def test_attention_two_pass_entry_points_match():
     c, kd, vd, td = _dev_cache(ck, dev, cfg, k, v, table)
     import torch
 
-    for H, chunk in ((32, 0), (64, 64)):
+    for H, chunk in ((32, 192), (64, 64)):
         q = _t(synth.seeded_vector(5, m * H * hd), dev)
         nws = ck.ck_attn_workspace_size(m, H, KV, hd, max(pos) + 1, chunk)
         ws = torch.zeros(nws, dtype=torch.uint8, device=dev)

@@ -162,13 +162,15 @@ def test_window_two_pass_entry_points_match(layout):
     k, v, table, oc, geo = _build(layout, m, KV, hd, pos, W, 512 if layout == "ring" else 0, 6)
     c, keep = _dev(ck, dev, KV, hd, k, v, table, geo)
     q = _t(synth.seeded_vector(5, m * H * hd), dev)
-    nws = ck.ck_attn_workspace_size(m, H, KV, hd, W, 0)
+    # an explicit split: the two automatic ones may differ
+    chunk = 64
+    nws = ck.ck_attn_workspace_size(m, H, KV, hd, W, chunk)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     a = torch.empty(m * H * hd, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
-    ck.ck_attn_decode_gqa(q, c, pos, a, m, H, 1.0 / np.sqrt(hd), 0, ws, nws)
-    ck.ck_attn_partial(q, c, pos, m, H, 1.0 / np.sqrt(hd), 0, ws, nws)
-    ck.ck_attn_merge(ws, nws, pos, m, H, KV, hd, 0, b, window=W)
+    ck.ck_attn_decode_gqa(q, c, pos, a, m, H, 1.0 / np.sqrt(hd), chunk, ws, nws)
+    ck.ck_attn_partial(q, c, pos, m, H, 1.0 / np.sqrt(hd), chunk, ws, nws)
+    ck.ck_attn_merge(ws, nws, pos, m, H, KV, hd, chunk, b, window=W)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
