@@ -184,10 +184,11 @@ struct Smem {
     // the online-softmax state of every row group (NS of them): unnormalized
     // outputs, running max (log2 units), sum of exponentials; then the
     // weight of each state in the combination
-    // rows padded by 4 floats: unpadded, the states of a wave's row groups
-    // (G*HD floats apart, a multiple of the 256 bytes the LDS banks span)
-    // all landed on the same banks (counters: 48% of the LDS cycles in
-    // conflict)
+    // rows padded by 4 floats, so that the states of a wave's row groups do
+    // not start on the same bank (measured neutral: the conflict counter
+    // reads about 48% of the LDS cycles either way, the four row groups of
+    // a store instruction writing a full set of banks each; the combination
+    // is a small part of the kernel)
     float ro[NS][G][HD + 4];
     float rm[NS][G];
     float rl[NS][G];
