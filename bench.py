@@ -159,9 +159,12 @@ def build_stacks(cfg, kv_dtype, keep_host, window=0, ring=False, topk=0):
 def time_steps(stacks, desc, steps, warmup, eager=False):
     """Decode steps of the stacks (rotated) with the given layer descriptor:
     eager warm-up, one HIP graph per replica (checked equal to the eager
-    step), then `steps` replays timed with HIP events on the launch stream,
-    one event between consecutive steps. Returns (per-step times in ms,
-    workspaces)."""
+    step), then `steps` replays timed with one pair of HIP events on the
+    launch stream around them (the headline: an event between consecutive
+    replays puts a barrier between them, measured at about 4 us per step),
+    then a second pass of `steps` replays with an event between consecutive
+    steps for the distribution. Returns (mean ms per step, per-step ms of the
+    second pass, workspaces)."""
     import torch
 
     from decode_step_attention_layer_amd import ck
@@ -212,6 +215,13 @@ def time_steps(stacks, desc, steps, warmup, eager=False):
     for i in range(warmup):
         run_step(i)
     torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        run_step(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    mean = a.elapsed_time(b) / steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
@@ -227,7 +237,7 @@ def time_steps(stacks, desc, steps, warmup, eager=False):
         off = ck.ck_decode_layer_ws_offset(desc, stack.max_ctx, "status")
         for ws in wss:
             assert int(ws[off:off + 4].view(torch.int32).item()) == 0, "a wait timed out"
-    return ms, wss
+    return mean, ms, wss
 
 
 def pct(v, q):
@@ -288,8 +298,7 @@ def main():
                                               args.ring, args.topk)
     stack = stacks[0]
     desc = stack.desc(variant_code(ck, args.variant), args.attn_chunk)
-    ms, wss = time_steps(stacks, desc, args.steps, args.warmup, args.eager)
-    ms_step = sum(ms) / len(ms)
+    ms_step, ms, wss = time_steps(stacks, desc, args.steps, args.warmup, args.eager)
     us_layer = ms_step * 1e3 / stack.nlayers
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.2f} us, {us_layer:.2f} us/layer, {value:.0f} GB/s")
@@ -338,8 +347,13 @@ def main():
         },
         "us_per_layer": round(us_layer, 3),
         "us_per_token": round(ms_step * 1e3 / cfg.m, 3),
-        "step_us": {"mean": round(ms_step * 1e3, 2), "median": round(pct(ms, 50) * 1e3, 2),
-                    "p10": round(pct(ms, 10) * 1e3, 2), "p90": round(pct(ms, 90) * 1e3, 2)},
+        "step_us": {"mean": round(ms_step * 1e3, 2),
+                    "evented": {"median": round(pct(ms, 50) * 1e3, 2),
+                                "p10": round(pct(ms, 10) * 1e3, 2),
+                                "p90": round(pct(ms, 90) * 1e3, 2),
+                                "note": "a second pass of the same steps with an event between "
+                                        "consecutive ones: each adds a barrier between graph "
+                                        "replays (about 4 us per step)"}},
         "bytes_per_step": step_bytes,
         "frac_of_peak": round(value / PEAK_GBS, 4),
         "roofline": roof,
@@ -366,11 +380,10 @@ def extra_records(args, stacks, step_bytes, variant, us_layer):
             var[v] = {"us_per_layer": round(us_layer, 3)}
             continue
         d = stack.desc(variant_code(ck, v), args.attn_chunk)
-        ms, wss = time_steps(stacks, d, steps, warm)
+        m, ms, wss = time_steps(stacks, d, steps, warm)
         del wss
-        m = sum(ms) / len(ms)
         var[v] = {"us_per_layer": round(m * 1e3 / stack.nlayers, 3),
-                  "median_us_per_layer": round(pct(ms, 50) * 1e3 / stack.nlayers, 3),
+                  "median_us_per_layer_evented": round(pct(ms, 50) * 1e3 / stack.nlayers, 3),
                   "GBs": round(step_bytes / (m * 1e-3) / 1e9, 1)}
         log(f"[bench] c3 {v}: {var[v]['us_per_layer']:.2f} us/layer")
     torch.cuda.synchronize()
@@ -381,8 +394,7 @@ def extra_records(args, stacks, step_bytes, variant, us_layer):
     cfg4 = synth.CONFIGS["c4"]
     st4, nb4, sb4 = build_stacks(cfg4, synth.KV_F32, False)
     d4 = st4[0].desc(variant_code(ck, variant), 0)
-    ms4, ws4 = time_steps(st4, d4, max(20, steps), warm)
-    m4 = sum(ms4) / len(ms4)
+    m4, ms4, ws4 = time_steps(st4, d4, max(20, steps), warm)
     g4 = sb4 / (m4 * 1e-3) / 1e9
     class A:   # the roofline's view of the arguments for this workload
         kernel_reps = args.kernel_reps
@@ -391,8 +403,9 @@ def extra_records(args, stacks, step_bytes, variant, us_layer):
     secondary = {"workload": workload_text(A),
                  "variant": variant,
                  "us_per_layer": round(m4 * 1e3, 3),
-                 "median_us_per_layer": round(pct(ms4, 50) * 1e3, 3),
-                 "p10_us": round(pct(ms4, 10) * 1e3, 2), "p90_us": round(pct(ms4, 90) * 1e3, 2),
+                 "evented_steps_us": {"median": round(pct(ms4, 50) * 1e3, 2),
+                                      "p10": round(pct(ms4, 10) * 1e3, 2),
+                                      "p90": round(pct(ms4, 90) * 1e3, 2)},
                  "GBs": round(g4, 1), "frac_of_peak": round(g4 / PEAK_GBS, 4),
                  "bytes_per_layer": sb4,
                  "attention": None if r4 is None else {
