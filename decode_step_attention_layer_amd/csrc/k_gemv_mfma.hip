@@ -17,7 +17,8 @@
 // arithmetic, after the activation blocks) and redistributes them to the MFMA
 // lane layout through its own LDS region, in phases of 4 Q5_0 (2 Q8_0) block
 // pairs; the activations are staged in LDS once per workgroup (codes, scale,
-// code sum) while the weights are in flight, and the 8 partial sums of each
+// code sum; block-major, so one block's token slots sit on distinct banks)
+// while the weights are in flight, and the 8 partial sums of each
 // (token, row) are added through LDS in wave order (deterministic).
 #include "ck_device.hpp"
 #include "ck_gemv_common.hpp"
@@ -179,8 +180,12 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. the activations of all m tokens into LDS (codes, scale, code sum)
-    auto put_x = [&](int b, const uint32_t *w) {
+    // 2. the activations of all m tokens into LDS (codes, scale, code sum),
+    // block-major: the m tokens of a block are consecutive 48-byte records,
+    // so the lanes reading one block's 16 token slots hit distinct banks
+    // (token-major, the slots were nb * 48 bytes apart, all on one bank)
+    auto put_x = [&](int bf, const uint32_t *w) {
+        const int b = bf % nb, tok = bf / nb;     // bf: flat index of the xq block
         XBlock xb;
         xb.d = half_bits_to_float(w[0]);
         int sum = 0;
@@ -191,7 +196,7 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
         }
         xb.sum = sum;
         xb.pad[0] = xb.pad[1] = 0;
-        xs[b] = xb;
+        xs[b * m + tok] = xb;
     };
     if (xpre) {
 #pragma unroll
@@ -227,6 +232,12 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
             if (f < kTileRows * kPh && d < np * St::words) reg[r * St::stride + d] = raw[p][i];
         }
         __builtin_amdgcn_wave_barrier();
+        // every block's MFMA of the phase first (independent, so they
+        // pipeline), then the scaling: a block at a time, each MFMA result
+        // was consumed at once and the chain LDS read -> MFMA -> LDS read ->
+        // FMA ran serially
+        v4i dd[St::pu][2];
+        float dws[St::pu][2];
 #pragma unroll
         for (int k = 0; k < St::pu; k++) {
             if (k < np) {
@@ -235,24 +246,31 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
 #pragma unroll
                 for (int bb = 0; bb < 2; bb++) {
                     const int b = 2 * (pb + k) + bb;
-                    float dw;
-                    const long bop = slice_codes<Q5>(w, bb, ks, dw);
+                    const long bop = slice_codes<Q5>(w, bb, ks, dws[k][bb]);
                     long aop = 0;
                     if (a_valid) {
-                        const int2 c = *reinterpret_cast<const int2 *>(&xs[j * nb + b].c[2 * ks]);
+                        const int2 c = *reinterpret_cast<const int2 *>(&xs[b * m + j].c[2 * ks]);
                         aop = (long)((unsigned long)(uint32_t)c.x |
                                      ((unsigned long)(uint32_t)c.y << 32));
                     }
-                    v4i dd = {0, 0, 0, 0};
-                    dd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, dd, 0, 0, 0);
+                    v4i z = {0, 0, 0, 0};
+                    dd[k][bb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, z, 0, 0, 0);
+                }
+            }
+        }
+        // token slots past the batch read the last token's record (their
+        // sums are never written)
+#pragma unroll
+        for (int k = 0; k < St::pu; k++) {
+            if (k < np) {
+#pragma unroll
+                for (int bb = 0; bb < 2; bb++) {
+                    const int b = 2 * (pb + k) + bb;
 #pragma unroll
                     for (int t = 0; t < 4; t++) {
-                        const int tok = 4 * ks + t;
-                        if (tok < m) {
-                            const XBlock &xb = xs[tok * nb + b];
-                            const int sdot = Q5 ? dd[t] - 16 * xb.sum : dd[t];
-                            acc[t] = fmaf((float)sdot, dw * xb.d, acc[t]);
-                        }
+                        const XBlock &xb = xs[b * m + min(4 * ks + t, m - 1)];
+                        const int sdot = Q5 ? dd[k][bb][t] - 16 * xb.sum : dd[k][bb][t];
+                        acc[t] = fmaf((float)sdot, dws[k][bb] * xb.d, acc[t]);
                     }
                 }
             }
