@@ -260,7 +260,8 @@ ATTN_CASES = [
     # 65-128 chunks per sequence (three and four merge wavefronts), more
     # than 128 (the workgroup merge), and past its 16 preloaded chunk slots
     # per thread (128 chunks at hd 128, 256 at hd 64)
-    (1, 28, 4, 128, 6000, 0, False),       # the automatic plan: 125 chunks of 48
+    (1, 28, 4, 128, 6000, 0, False),       # the automatic plan: 63 chunks of 96
+    (1, 28, 4, 128, 6000, 48, False),      # 125 chunks
     (1, 28, 4, 128, 9000, 48, False),      # 188 chunks
     (1, 14, 2, 64, 4097, 64, False),       # 65 chunks
     (1, 8, 1, 64, 20000, 64, False),       # 313 chunks
