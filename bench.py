@@ -491,9 +491,13 @@ def roofline(args, stacks, desc, ws, nbytes):
         attn_us = _time_launches(lambda: ck.ck_attn_partial(
             q, nxt(0).cache, stack.pos, m, H, scale, chunk, part, nws),
             args.kernel_reps)
-        # query groups over 4 heads attending an fp32 cache run on the matrix
-        # cores (a kernel of its own name)
-        attn_name = "k_attn_mfma" if H // KV > 4 and args.kv == "f32" else "k_attn"
+        # query groups over 4 heads attending an fp32 cache, and one sequence
+        # attending a bf16 or fp8 cache, run on the matrix cores (kernels of
+        # their own names)
+        if args.kv == "f32":
+            attn_name = "k_attn_mfma" if H // KV > 4 else "k_attn"
+        else:
+            attn_name = "k_attn_mfma16" if m == 1 else "k_attn"
 
     def o_gemv():
         L = nxt(1)
@@ -543,7 +547,8 @@ def recorded_traffic(kernel: str, workload: str, launches_bytes=None):
     rec = json.loads(mt.group(1))
     csrc = os.path.join(ROOT, "decode_step_attention_layer_amd", "csrc")
     h = hashlib.sha256()
-    src_file = {"k_attn_merge": "k_attn", "k_attn_mfma": "k_attn"}.get(kernel, kernel) + ".hip"
+    src_file = {"k_attn_merge": "k_attn", "k_attn_mfma": "k_attn",
+                "k_attn_mfma16": "k_attn16"}.get(kernel, kernel) + ".hip"
     # the merge runs as k_attn_merge1 (one wavefront) when a sequence has at
     # most 32 chunks: either record stands for it
     names = ("k_attn_merge", "k_attn_merge1") if kernel == "k_attn_merge" else (kernel,)

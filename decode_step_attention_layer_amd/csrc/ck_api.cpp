@@ -324,7 +324,7 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
     rc = read_positions(pos_host, m, cache_tokens(kv), &p, &mx);
     if (rc) return rc;
     const int G = H / c.kv_heads;
-    const bool matrix = attn_matrix_path(G, c.dtype, false);
+    const bool matrix = attn_matrix_path(G, c.dtype, m, false);
     AttnPlan pl = attn_plan(c.kv_heads, G, attended(mx, c.window), total_tokens(p, m, c.window),
                             chunk, attn_step(G, c.dtype, matrix), matrix);
     if (!attn_chunks_supported(pl.nchunks)) return CK_EUNSUPPORTED;
@@ -614,7 +614,7 @@ AttnPlan layer_attn_plan(const ck_layer_desc &d, const CacheView &c, const Posit
                               : (p.dev ? (long long)d.m * amx : total_tokens(p, d.m, c.window));
     const int G = d.H / d.KV;
     const bool matrix = (d.variant == CK_VARIANT_CHAIN || d.variant == CK_VARIANT_FUSED) &&
-                        attn_matrix_path(G, c.dtype, sp != nullptr);
+                        attn_matrix_path(G, c.dtype, d.m, sp != nullptr);
     return attn_plan(d.KV, G, amx, atot, d.attn_chunk, attn_step(G, c.dtype, matrix), matrix);
 }
 

@@ -760,4 +760,9 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
 
 }  // namespace attn
 
+// The attention over a bf16 or fp8 cache on the bf16 matrix cores (no
+// selection): grid and partials as the vector kernel's (k_attn16.hip).
+hipError_t launch_attn_mfma16(const attn::AttnArgs &a, int G, int hd, dim3 grid, bool paged,
+                              hipStream_t st);
+
 }  // namespace ck

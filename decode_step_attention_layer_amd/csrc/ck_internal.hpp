@@ -187,9 +187,11 @@ struct AttnPlan {
 // dtype < 0: whichever runs (a common multiple of their steps), for plans
 // that another call must reproduce without knowing the cache.
 int attn_step(int G, int dtype, bool matrix);
-// Whether the attention launch of a query group of G heads runs on the
-// matrix cores: groups over 4 heads attending an fp32 cache with no selection.
-bool attn_matrix_path(int G, int dtype, bool selection);
+// Whether the attention launch of m sequences with query groups of G heads
+// runs on the matrix cores: with no selection, groups over 4 heads attending
+// an fp32 cache, and every group of a single sequence attending a bf16 or
+// fp8 cache.
+bool attn_matrix_path(int G, int dtype, int m, bool selection);
 // The split of the attended tokens. An explicit chunk_req is used as given
 // (every kernel masks the rows past a chunk); the automatic chunk is a whole
 // number of `step`s sized for the kernel: with `matrix`, about one

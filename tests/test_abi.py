@@ -109,24 +109,33 @@ def test_layer_attention_plan(ck):
     c8f8 = ck.CkKVCache(FAKE, FAKE, 8, 128, 40000, 0, None, 0, 0, ck.CK_KV_FP8_E4M3, 1.0, 1.0)
     assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8, chunk=40), c8, [4096]) == (40, 103)
     # 32769 tokens x 8 KV heads over 2 x 256 workgroups: 513 tokens, whole
-    # steps of the vector kernel: 576 = 9 x 64 (fp32), 640 = 5 x 128 (fp8,
-    # whose rows take 8 lanes, 8 rows a round)
+    # 64-token steps of the vector kernel (fp32); over 256 workgroups for the
+    # bf16 matrix cores (fp8): 1025 tokens, whole 32-token steps; the
+    # two-launch layer keeps the vector kernel: 640 = 5 x 128 (fp8 rows take
+    # 8 lanes, 8 rows a round)
     assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8), c8, [32768]) == (576, 57)
-    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8), c8f8, [32768]) == (640, 52)
+    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8), c8f8, [32768]) == (1056, 32)
+    assert plan(d(ck.CK_VARIANT_TWO_LAUNCH, H=32, KV=8), c8f8, [32768]) == (640, 52)
+    # a batch over a bf16 or fp8 cache keeps the vector kernel: 2 x 32769
+    # tokens x 8 KV heads over 2 x 256 workgroups, whole 128-token steps
+    assert plan(d(ck.CK_VARIANT_FUSED, H=32, KV=8, m=2), c8f8, [32768, 32768]) == (1152, 29)
     for H, KV, cache in ((28, 4, c32), (28, 4, cbf), (32, 8, c8), (32, 8, c8f8)):
         for v in V:
             if v == ck.CK_VARIANT_PERSISTENT and cache.dtype != ck.CK_KV_F32:
                 continue          # fp32 caches only
-            if H // KV > 4:
-                matrix = cache.dtype == ck.CK_KV_F32 and v in (ck.CK_VARIANT_CHAIN,
-                                                               ck.CK_VARIANT_FUSED)
-                step = 16 if matrix else 48
-            else:
-                step = 128 if cache.dtype == ck.CK_KV_FP8_E4M3 else 64
+            launches_attn = v in (ck.CK_VARIANT_CHAIN, ck.CK_VARIANT_FUSED)
             for pos in ([0], [15], [16], [47], [1023], [4096], [8190], [100, 7000, 3]):
                 if max(pos) >= cache.capacity:
                     continue
                 m = len(pos)
+                if launches_attn and cache.dtype != ck.CK_KV_F32 and m == 1:
+                    step = 32                 # the bf16 matrix cores
+                elif launches_attn and cache.dtype == ck.CK_KV_F32 and H // KV > 4:
+                    step = 16                 # the fp32 matrix cores
+                elif H // KV > 4:
+                    step = 48
+                else:
+                    step = 128 if cache.dtype == ck.CK_KV_FP8_E4M3 else 64
                 chunk, n = plan(d(v, H=H, KV=KV, m=m), cache, pos)
                 assert chunk % step == 0 and chunk >= step, (H, v, pos, chunk)
                 assert (n - 1) * chunk < max(pos) + 1 <= n * chunk, (H, v, pos, chunk, n)
