@@ -48,29 +48,51 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Round-to-nearest-even bf16 of an fp32 value (its upper 16 bits).
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// One word of two bf16: the upper (HI) or lower halves of the words lo and
+// hi, lo's in the low half (one byte permute).
+template <bool HI>
+__device__ __forceinline__ uint32_t pack_halves(uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_perm(hi, lo, HI ? 0x07060302u : 0x05040100u);
 }
 
-// x as a high bf16 term and the bf16 of the remainder. A remainder of zero
-// becomes the smallest positive bf16 (2^-133): an infinite cache value times
-// the low term then stays infinite instead of becoming NaN (inf x 0), as in
-// the fp32 arithmetic; against a finite value it adds less than an fp32
-// rounding (a single token's output is still its V exactly).
-__device__ __forceinline__ void bf16_split(float x, uint32_t &hi, uint32_t &lo) {
-    hi = bf16_rne(x);
-    const uint32_t r = bf16_rne(x - __uint_as_float(hi << 16));
-    lo = (r & 0x7FFFu) ? r : 1u;
+// x and y rounded to nearest even bf16 (one conversion), x in the low half.
+__device__ __forceinline__ uint32_t bf16x2_rne(float x, float y) {
+    const f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Two fp8 E4M3 codes (bytes 2*HI, 2*HI + 1 of w) as a pair of bf16 in one
-// word: the fp32 decode is exact in bf16, so its upper halves are the values.
+// x and y as high bf16 terms (hi) and the bf16 of their remainders (lo). With
+// NZ a remainder of zero becomes the smallest positive bf16 (2^-133): an
+// infinite cache value times the low term then stays infinite instead of
+// becoming NaN (inf x 0), as in the fp32 arithmetic; against a finite value
+// it adds less than an fp32 rounding (a single token's output is still its V
+// exactly). fp8 caches hold no infinity and take plain remainders.
+template <bool NZ>
+__device__ __forceinline__ void bf16_split2(float x, float y, uint32_t &hi, uint32_t &lo) {
+    hi = bf16x2_rne(x, y);
+    lo = bf16x2_rne(x - __uint_as_float(hi << 16), y - __uint_as_float(hi & 0xFFFF0000u));
+    if constexpr (NZ) {
+        if (!(lo & 0x7FFFu)) lo = (lo & 0xFFFF0000u) | 1u;
+        if (!(lo & 0x7FFF0000u)) lo = (lo & 0xFFFFu) | 0x10000u;
+    }
+}
+
+// Two fp8 E4M3 codes (bytes 2*HI, 2*HI + 1 of w) decoded to fp32 (exact).
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8_pair(uint32_t w) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+    return f32x2{f[0], f[1]};
+}
+
+// The same codes as a pair of bf16 in one word: an fp8 value is exact in
+// bf16, so the upper halves of its fp32 decode are its bf16 bits.
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8_pair_bf16(uint32_t w) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+    const f32x2 f = fp8_pair<HI>(w);
+    return pack_halves<true>(__float_as_uint(f[0]), __float_as_uint(f[1]));
 }
 
 template <int NB, bool NT>
@@ -166,20 +188,43 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
     const uint8_t *Vc = static_cast<const uint8_t *>(a.c.v);
 
     // a step's loads: K of tokens tb + 16mb + hl (the lane's quarter of the
-    // row), V of tokens tb + 16(e/4) + 4kq + e%4 (the lane's VT dims)
-    auto load_step = [&](int tb, uint32_t (&kw)[2][KW], uint32_t (&vw)[8][VW]) {
+    // row), V of tokens tb + 16(e/4) + 4kq + e%4 (the lane's VT dims). FULL:
+    // all 32 tokens lie in the chunk and in consecutive slots of a
+    // contiguous cache, so every row is the step's first row plus a constant
+    // (one address a step, the rest immediate offsets); otherwise each row
+    // is located on its own, rows past the chunk re-reading its last row.
+    const int k_lane = hl * HD + KQ * kq;       // element offsets from the step's first row
+    const int v_lane = 4 * kq * HD + VT * hl;
+    auto load_step = [&](auto full, int tb, uint32_t (&kw)[2][KW], uint32_t (&vw)[8][VW]) {
+        constexpr bool FULL = decltype(full)::value;
+        if constexpr (FULL && !PAGED) {
+            const long long base = (long long)seq_base + (long long)(slot0 + (tb - t0)) * HD;
+            const uint8_t *kp = Kc + (base + k_lane) * EB;
+            const uint8_t *vp = Vc + (base + v_lane) * EB;
 #pragma unroll
-        for (int mb = 0; mb < 2; mb++) {
-            const uint8_t *kp = Kc + (row_off(min(tb + 16 * mb + hl, t1 - 1)) + KQ * kq) * EB;
+            for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-            for (int i = 0; i < KQ * EB / KLOAD; i++)
-                load_bytes<KLOAD, STREAM>(kp + KLOAD * i, &kw[mb][i * KLOAD / 4]);
-        }
+                for (int i = 0; i < KQ * EB / KLOAD; i++)
+                    load_bytes<KLOAD, STREAM>(kp + 16 * mb * HD * EB + KLOAD * i,
+                                              &kw[mb][i * KLOAD / 4]);
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const int t = tb + 16 * (e >> 2) + 4 * kq + (e & 3);
-            const uint8_t *vp = Vc + (row_off(min(t, t1 - 1)) + VT * hl) * EB;
-            load_bytes<VLOAD, STREAM>(vp, vw[e]);
+            for (int e = 0; e < 8; e++)
+                load_bytes<VLOAD, STREAM>(vp + (16 * (e >> 2) + (e & 3)) * HD * EB, vw[e]);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < 2; mb++) {
+                const uint8_t *kp =
+                    Kc + (row_off(min(tb + 16 * mb + hl, t1 - 1)) + KQ * kq) * EB;
+#pragma unroll
+                for (int i = 0; i < KQ * EB / KLOAD; i++)
+                    load_bytes<KLOAD, STREAM>(kp + KLOAD * i, &kw[mb][i * KLOAD / 4]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int t = tb + 16 * (e >> 2) + 4 * kq + (e & 3);
+                const uint8_t *vp = Vc + (row_off(min(t, t1 - 1)) + VT * hl) * EB;
+                load_bytes<VLOAD, STREAM>(vp, vw[e]);
+            }
         }
     };
 
@@ -198,14 +243,17 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
             qf[i + 3] = v.w;
         }
     }
+    constexpr bool kNZ = DT == CK_KV_BF16;   // see bf16_split2
     const int nstep = (t1 - t0 + 31) / 32;
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 o[VT];
 #pragma unroll
     for (int T = 0; T < VT; T++) o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 qh8[KB], ql8[KB];
-    // One online-softmax step over the 32 tokens at tb.
-    auto compute_step = [&](int tb, uint32_t (&kw)[2][KW], uint32_t (&vw)[8][VW]) {
+    // One online-softmax step over the 32 tokens at tb; FULL: all of them in
+    // the chunk (nothing to mask).
+    auto compute_step = [&](auto full, int tb, uint32_t (&kw)[2][KW], uint32_t (&vw)[8][VW]) {
+        constexpr bool FULL = decltype(full)::value;
         // scores of tokens tb + 16mb + 4kq + r for head hl
         f32x4 sc[2];
 #pragma unroll
@@ -231,7 +279,7 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
         for (int mb = 0; mb < 2; mb++)
 #pragma unroll
             for (int r = 0; r < 4; r++)
-                sv[mb][r] = (tb + 16 * mb + 4 * kq + r < t1) ? sc[mb][r] : -INFINITY;
+                sv[mb][r] = (FULL || tb + 16 * mb + 4 * kq + r < t1) ? sc[mb][r] : -INFINITY;
         float mt = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; mb++)
@@ -255,61 +303,82 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
         m_run = mn;
         uint32_t ph[4], pl[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            uint32_t h0, l0, h1, l1;
-            bf16_split(p[2 * i], h0, l0);
-            bf16_split(p[2 * i + 1], h1, l1);
-            ph[i] = h0 | (h1 << 16);
-            pl[i] = l0 | (l1 << 16);
-        }
+        for (int i = 0; i < 4; i++) bf16_split2<kNZ>(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
         const bf16x8 ph8 = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         const bf16x8 pl8 = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
-        // V of the 8 tokens, two dims at a time: the bf16 pair (dims
-        // VT*hl + T2, + 1) of each row, a row past the chunk zeroed (it may
-        // hold anything, a NaN code included), then the A operands of tiles
-        // T2 and T2 + 1
-        bool ok[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) ok[e] = tb + 16 * (e >> 2) + 4 * kq + (e & 3) < t1;
 #pragma unroll
         for (int T = 0; T < VT; T++) o[T] *= alpha;
+        // V of the 8 tokens, two dims (VT*hl + T2, + 1) at a time: the pair
+        // of each row, then the A operands of tiles T2 and T2 + 1, rows 2d and
+        // 2d + 1 in word d (one byte permute a word). A bf16 row past the
+        // chunk is zeroed (it may hold an infinity, and 0 x inf is NaN); an
+        // fp8 one needs nothing: its probability is exactly zero and its
+        // value finite, or a NaN that the chunk's own last row holds too.
+        bool ok[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) ok[e] = FULL || tb + 16 * (e >> 2) + 4 * kq + (e & 3) < t1;
 #pragma unroll
         for (int T2 = 0; T2 < VT; T2 += 2) {
-            uint32_t pr[8];
+            uint32_t lo[8], hi[8];   // rows' values at dims T2 (lo) and T2 + 1 (hi)
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                uint32_t w;
-                if constexpr (DT == CK_KV_BF16) w = vw[e][T2 >> 1];
-                else if ((T2 >> 1) & 1) w = fp8_pair_bf16<true>(vw[e][T2 >> 2]);
-                else w = fp8_pair_bf16<false>(vw[e][T2 >> 2]);
-                pr[e] = ok[e] ? w : 0u;
+                if constexpr (DT == CK_KV_BF16) {
+                    const uint32_t w = ok[e] ? vw[e][T2 >> 1] : 0u;
+                    lo[e] = w;
+                    hi[e] = w;
+                } else {
+                    const f32x2 f = ((T2 >> 1) & 1) ? fp8_pair<true>(vw[e][T2 >> 2])
+                                                    : fp8_pair<false>(vw[e][T2 >> 2]);
+                    lo[e] = __float_as_uint(f[0]);
+                    hi[e] = __float_as_uint(f[1]);
+                }
             }
 #pragma unroll
             for (int h = 0; h < 2; h++) {
                 uint32_t aw[4];
 #pragma unroll
-                for (int d = 0; d < 4; d++)
-                    aw[d] = h ? ((pr[2 * d] >> 16) | (pr[2 * d + 1] & 0xFFFF0000u))
-                              : ((pr[2 * d] & 0xFFFFu) | (pr[2 * d + 1] << 16));
+                for (int d = 0; d < 4; d++) {
+                    if constexpr (DT == CK_KV_BF16)
+                        aw[d] = h ? pack_halves<true>(hi[2 * d], hi[2 * d + 1])
+                                  : pack_halves<false>(lo[2 * d], lo[2 * d + 1]);
+                    else
+                        aw[d] = h ? pack_halves<true>(hi[2 * d], hi[2 * d + 1])
+                                  : pack_halves<true>(lo[2 * d], lo[2 * d + 1]);
+                }
                 const bf16x8 vop = as_bf16x8(aw[0], aw[1], aw[2], aw[3]);
                 o[T2 + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph8, o[T2 + h], 0, 0, 0);
                 o[T2 + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl8, o[T2 + h], 0, 0, 0);
             }
         }
     };
-    // A wave's steps are wave, wave + NW, .... bf16: the next one's loads go
-    // out before the current one is computed, so that they land meanwhile.
-    // Two register sets take turns (a copy from one to the other would wait
-    // for the loads in flight), and the last steps are peeled off, so that
-    // no load inside the loop is conditional (a conditional one makes the
-    // waits after it wait for every load). fp8 (half the bytes a step, more
-    // decode work) is faster one step at a time.
+    const std::integral_constant<bool, true> kFull;
+    const std::integral_constant<bool, false> kPart;
+    // A wave's steps are wave, wave + NW, .... Only a wave's last step can
+    // be partial (the chunk's last), and the fast addressing needs a
+    // contiguous cache (no pages, no ring); every other step takes the full
+    // path. bf16: the next step's loads go out before the current one is
+    // computed, so that they land meanwhile. Two register sets take turns (a
+    // copy from one to the other would wait for the loads in flight), and
+    // the last steps are peeled off, so that no load inside the loop is
+    // conditional (a conditional one makes the waits after it wait for every
+    // load). fp8 (half the bytes a step, more decode work) measured faster
+    // one step at a time.
     constexpr bool kPrefetch = DT == CK_KV_BF16;
+    const bool fast = !PAGED && !a.c.ring;
     const int n = wave < nstep ? (nstep - 1 - wave) / NW + 1 : 0;
     if (n > 0) {
         auto at = [&](int i) { return t0 + 32 * (wave + i * NW); };
+        // load and compute of a wave's step i: the fast forms for all but the last
+        auto ld = [&](int i, uint32_t (&kw)[2][KW], uint32_t (&vw)[8][VW]) {
+            if (fast && i + 1 < n) load_step(kFull, at(i), kw, vw);
+            else load_step(kPart, at(i), kw, vw);
+        };
+        auto cp = [&](int i, uint32_t (&kw)[2][KW], uint32_t (&vw)[8][VW]) {
+            if (i + 1 < n) compute_step(kFull, at(i), kw, vw);
+            else compute_step(kPart, at(i), kw, vw);
+        };
         uint32_t k0[2][KW], v0[8][VW], k1[2][KW], v1[8][VW];
-        load_step(at(0), k0, v0);
+        ld(0, k0, v0);
         __builtin_amdgcn_sched_barrier(0);
         // q split after the first step's loads are out (its wait is for q only)
         {
@@ -318,13 +387,9 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
             for (int kb = 0; kb < KB; kb++) {
                 uint32_t hw[4], lw[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    uint32_t h0, l0, h1, l1;
-                    bf16_split(qf[8 * kb + 2 * i] * qs, h0, l0);
-                    bf16_split(qf[8 * kb + 2 * i + 1] * qs, h1, l1);
-                    hw[i] = h0 | (h1 << 16);
-                    lw[i] = l0 | (l1 << 16);
-                }
+                for (int i = 0; i < 4; i++)
+                    bf16_split2<kNZ>(qf[8 * kb + 2 * i] * qs, qf[8 * kb + 2 * i + 1] * qs, hw[i],
+                                     lw[i]);
                 qh8[kb] = as_bf16x8(hw[0], hw[1], hw[2], hw[3]);
                 ql8[kb] = as_bf16x8(lw[0], lw[1], lw[2], lw[3]);
             }
@@ -332,27 +397,27 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
         if constexpr (kPrefetch) {
             int i = 0;
             for (; i + 2 < n; i += 2) {
-                load_step(at(i + 1), k1, v1);
+                ld(i + 1, k1, v1);
                 __builtin_amdgcn_sched_barrier(0);
-                compute_step(at(i), k0, v0);
-                load_step(at(i + 2), k0, v0);
+                compute_step(kFull, at(i), k0, v0);
+                ld(i + 2, k0, v0);
                 __builtin_amdgcn_sched_barrier(0);
-                compute_step(at(i + 1), k1, v1);
+                compute_step(kFull, at(i + 1), k1, v1);
             }
             if (i + 1 < n) {
-                load_step(at(i + 1), k1, v1);
+                ld(i + 1, k1, v1);
                 __builtin_amdgcn_sched_barrier(0);
-                compute_step(at(i), k0, v0);
-                compute_step(at(i + 1), k1, v1);
+                compute_step(kFull, at(i), k0, v0);
+                compute_step(kPart, at(i + 1), k1, v1);
             } else {
-                compute_step(at(i), k0, v0);
+                compute_step(kPart, at(i), k0, v0);
             }
         } else {
-            compute_step(at(0), k0, v0);
+            cp(0, k0, v0);
             for (int i = 1; i < n; i++) {
-                load_step(at(i), k0, v0);
+                ld(i, k0, v0);
                 __builtin_amdgcn_sched_barrier(0);
-                compute_step(at(i), k0, v0);
+                cp(i, k0, v0);
             }
         }
     }
