@@ -9,8 +9,8 @@
 // rows, D[token][row] = S. Lane l supplies token slot l%16 and row l%16 for
 // the k-slice 8*(l/16)..+7 and receives D[4*(l/16)+t][l%16], t < 4, so every
 // output a lane scales belongs to the weight row whose block scale it loaded.
-// Q5_0 codes enter unsigned (0..31) and the 16 * sum(x) offset is removed
-// after the integer dot, as in the vector path.
+// Q5_0 codes are unpacked straight to signed bytes (code - 16), so the
+// integer dot is the block's S itself.
 //
 // Workgroup: 8 waves on one tile of 16 rows; wave w takes an eighth of the
 // rows' block pairs, loads them with coalesced dword loads (all before any
@@ -18,8 +18,11 @@
 // lane layout through its own LDS region, in phases of 4 Q5_0 (2 Q8_0) block
 // pairs; the activations are staged in LDS once per workgroup (codes, scale,
 // code sum; block-major, so one block's token slots sit on distinct banks)
-// while the weights are in flight, and the 8 partial sums of each
-// (token, row) are added through LDS in wave order (deterministic).
+// while the weights are in flight (codes block-major, the m tokens of a block
+// consecutive; scales in a separate array padded to 16 token slots, so a
+// lane's four token scales of a block are one 16-byte read), and the 8
+// partial sums of each (token, row) are added through LDS in wave order
+// (deterministic).
 #include "ck_device.hpp"
 #include "ck_gemv_common.hpp"
 #include "ck_internal.hpp"
@@ -85,11 +88,13 @@ __device__ __forceinline__ long slice_codes(const uint32_t *w, int bb, int ks, f
             q0 = w[7];
             q1 = w[8];
         }
+        // code - 16 as a signed byte: the low nibble, with 0xF0 above it
+        // where the fifth bit is clear
         const int sh = ks < 2 ? 0 : 4;
         c0 = (q0 >> sh) & 0x0F0F0F0Fu;
         c1 = (q1 >> sh) & 0x0F0F0F0Fu;
-        c0 |= spread4(__builtin_amdgcn_ubfe(qh, 8 * ks, 4)) << 4;
-        c1 |= spread4(__builtin_amdgcn_ubfe(qh, 8 * ks + 4, 4)) << 4;
+        c0 |= spread4(__builtin_amdgcn_ubfe(~qh, 8 * ks, 4)) * 0xF0u;
+        c1 |= spread4(__builtin_amdgcn_ubfe(~qh, 8 * ks + 4, 4)) * 0xF0u;
     } else {
         if (bb == 0) {
             dw = half_bits_to_float(w[0]);
@@ -121,9 +126,11 @@ struct Stage {
 constexpr int kStageRegion = Stage<true>::region > Stage<false>::region ? Stage<true>::region
                                                                         : Stage<false>::region;
 
+constexpr int kSlots = 16;   // token slots of an MFMA tile
+
 template <bool Q5>
 __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb, int m,
-                          XBlock *xs, uint32_t *wst, float *red) {
+                          uint32_t *xc, float *xd, uint32_t *wst, float *red) {
     using St = Stage<Q5>;
     constexpr int NSW = SliceWords<Q5>::n;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -180,24 +187,20 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. the activations of all m tokens into LDS (codes, scale, code sum),
-    // block-major: the m tokens of a block are consecutive 48-byte records,
-    // so the lanes reading one block's 16 token slots hit distinct banks
-    // (token-major, the slots were nb * 48 bytes apart, all on one bank)
+    // 2. the activations of all m tokens into LDS: codes block-major (the m
+    // tokens of a block are consecutive 32-byte rows, so the lanes reading
+    // one block's token slots spread over the banks), scales [block][16
+    // slots] with the slots past the batch zero (their MFMA rows are zero
+    // codes; a zero scale keeps stale LDS bits out of the sums)
     auto put_x = [&](int bf, const uint32_t *w) {
         const int b = bf % nb, tok = bf / nb;     // bf: flat index of the xq block
-        XBlock xb;
-        xb.d = half_bits_to_float(w[0]);
-        int sum = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            xb.c[i] = (int)w[1 + i];
-            sum = __builtin_amdgcn_sdot4((int)w[1 + i], 0x01010101, sum, false);
-        }
-        xb.sum = sum;
-        xb.pad[0] = xb.pad[1] = 0;
-        xs[b * m + tok] = xb;
+        xd[b * kSlots + tok] = half_bits_to_float(w[0]);
+        uint4 *dst = reinterpret_cast<uint4 *>(xc + (b * m + tok) * 8);
+        dst[0] = make_uint4(w[1], w[2], w[3], w[4]);
+        dst[1] = make_uint4(w[5], w[6], w[7], w[8]);
     };
+    for (int i = tid; i < nb * kSlots; i += kMT)
+        if ((i & (kSlots - 1)) >= m) xd[i] = 0.0f;
     if (xpre) {
 #pragma unroll
         for (int q = 0; q < 2; q++)
@@ -220,6 +223,7 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
     uint32_t *reg = wst + wave * kStageRegion;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const bool a_valid = j < m;
+    const int jr = min(j, m - 1);
 #pragma unroll
     for (int p = 0; p < St::nph; p++) {
         const int pb = u0 + p * St::pu;
@@ -247,31 +251,28 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
                 for (int bb = 0; bb < 2; bb++) {
                     const int b = 2 * (pb + k) + bb;
                     const long bop = slice_codes<Q5>(w, bb, ks, dws[k][bb]);
-                    long aop = 0;
-                    if (a_valid) {
-                        const int2 c = *reinterpret_cast<const int2 *>(&xs[b * m + j].c[2 * ks]);
-                        aop = (long)((unsigned long)(uint32_t)c.x |
-                                     ((unsigned long)(uint32_t)c.y << 32));
-                    }
+                    const uint2 c = *reinterpret_cast<const uint2 *>(&xc[(b * m + jr) * 8 + 2 * ks]);
+                    const long aop = a_valid ? (long)((unsigned long)c.x |
+                                                      ((unsigned long)c.y << 32))
+                                             : 0;
                     v4i z = {0, 0, 0, 0};
                     dd[k][bb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, z, 0, 0, 0);
                 }
             }
         }
-        // token slots past the batch read the last token's record (their
-        // sums are never written)
+        // the lane's token slots 4ks..4ks+3: their scales in one read (zero
+        // past the batch)
 #pragma unroll
         for (int k = 0; k < St::pu; k++) {
             if (k < np) {
 #pragma unroll
                 for (int bb = 0; bb < 2; bb++) {
                     const int b = 2 * (pb + k) + bb;
-#pragma unroll
-                    for (int t = 0; t < 4; t++) {
-                        const XBlock &xb = xs[b * m + min(4 * ks + t, m - 1)];
-                        const int sdot = Q5 ? dd[k][bb][t] - 16 * xb.sum : dd[k][bb][t];
-                        acc[t] = fmaf((float)sdot, dws[k][bb] * xb.d, acc[t]);
-                    }
+                    const float4 dx = *reinterpret_cast<const float4 *>(&xd[b * kSlots + 4 * ks]);
+                    acc[0] = fmaf((float)dd[k][bb][0], dws[k][bb] * dx.x, acc[0]);
+                    acc[1] = fmaf((float)dd[k][bb][1], dws[k][bb] * dx.y, acc[1]);
+                    acc[2] = fmaf((float)dd[k][bb][2], dws[k][bb] * dx.z, acc[2]);
+                    acc[3] = fmaf((float)dd[k][bb][3], dws[k][bb] * dx.w, acc[3]);
                 }
             }
         }
@@ -302,19 +303,20 @@ __global__ __launch_bounds__(kMT) void k_gemv_mfma(GemvArgs a) {
                    : (a.nseg > 1 && wg >= a.seg[1].wg_begin) ? 1 : 0;
     const GemvSeg sg = si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]);
     const int nb = a.K / kQK;
-    // LDS: the staged weights of the 8 waves, then the activations (the final
-    // reduction reuses the activations' space)
+    // LDS: the staged weights of the 8 waves, then the activation codes and
+    // scales (the final reduction reuses their space)
     uint32_t *wst = lds;
-    XBlock *xa = reinterpret_cast<XBlock *>(wst + kMW * kStageRegion);
-    float *red = reinterpret_cast<float *>(xa);
+    uint32_t *xc = wst + kMW * kStageRegion;
+    float *xd = reinterpret_cast<float *>(xc + (size_t)a.m * nb * 8);
+    float *red = reinterpret_cast<float *>(xc);
     if (sg.is_q5)
-        mfma_body<true>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xa, wst, red);
+        mfma_body<true>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red);
     else
-        mfma_body<false>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xa, wst, red);
+        mfma_body<false>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red);
 }
 
 size_t mfma_lds(int m, int nb) {
-    const size_t xs = sizeof(XBlock) * (size_t)m * nb;
+    const size_t xs = sizeof(uint32_t) * 8 * (size_t)m * nb + sizeof(float) * kSlots * (size_t)nb;
     const size_t red = sizeof(float) * kMT * 4;
     return sizeof(uint32_t) * kMW * kStageRegion + (xs > red ? xs : red);
 }
