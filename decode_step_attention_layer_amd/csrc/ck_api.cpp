@@ -708,10 +708,21 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
         g.xq = xq;
         g.K = d.D;
         g.m = d.m;
-        if ((e = gemv_any(g, st)) != hipSuccess) return CK_EHIP;
+        // the fused layer on the matrix cores (no counters to clear): RoPE
+        // and the append (steps 5-6) in the projection's epilogue
+        const bool epi = fused && ncnt == 0 && gemv_mfma_supported(g.K, g.m);
+        if (epi) {
+            const QkvEpi ep{w->rope_cos, w->rope_sin, p, c, d.head_dim};
+            e = launch_gemv_mfma_qkv(g, ep, st);
+        } else {
+            e = gemv_any(g, st);
+        }
+        if (e != hipSuccess) return CK_EHIP;
 
         // steps 5-6: RoPE on q and k, then the append of (k, v) at pos
-        if (fused) {
+        if (epi) {
+            // done in the projection's epilogue
+        } else if (fused) {
             e = launch_rope_append(q, k, v, w->rope_cos, w->rope_sin, c, p, d.m, d.H, st, cnt,
                                    ncnt, zstride);
         } else {

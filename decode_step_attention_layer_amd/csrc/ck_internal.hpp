@@ -166,6 +166,17 @@ hipError_t launch_gemv(const GemvArgs &a, hipStream_t st);
 // tokens; same arguments and results as launch_gemv.
 bool gemv_mfma_supported(int K, int m);
 hipError_t launch_gemv_mfma(GemvArgs a, hipStream_t st);
+// The epilogue of a Q/K/V projection launch whose segments are q, k and v
+// in that order: RoPE of q and k (rotate-half pairs, table row pos), then k
+// and v appended to the cache at pos; a token with an invalid position keeps
+// its unrotated q and k and appends nothing (as launch_rope_append).
+struct QkvEpi {
+    const float *cos_tab, *sin_tab;   // [rows][hd/2]
+    Positions pos;
+    CacheView c;
+    int hd;
+};
+hipError_t launch_gemv_mfma_qkv(GemvArgs a, const QkvEpi &e, hipStream_t st);
 hipError_t launch_rope(float *q, float *k, const float *cos_tab, const float *sin_tab,
                        const Positions &pos, int m, int H, int KV, int hd, hipStream_t st);
 hipError_t launch_kv_append(const CacheView &c, const float *k, const float *v,

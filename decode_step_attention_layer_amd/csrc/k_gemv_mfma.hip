@@ -23,6 +23,13 @@
 // lane's four token scales of a block are one 16-byte read), and the 8
 // partial sums of each (token, row) are added through LDS in wave order
 // (deterministic).
+// The Q/K/V launch of the batched layer can end in RoPE and the KV append
+// (C-Kernel-Engine MAIN KERNEL steps 5-6): its q and k tiles then take their
+// rows in rotation order (tile rows 2p and 2p + 1 are elements i and
+// i + hd/2 of one head), so a row's partner is the neighbouring lane, and
+// each output thread rotates its value and stores it, and k and v into the
+// cache; the positions, table entries and cache rows load before the
+// weights.
 #include "ck_device.hpp"
 #include "ck_gemv_common.hpp"
 #include "ck_internal.hpp"
@@ -128,9 +135,16 @@ constexpr int kStageRegion = Stage<true>::region > Stage<false>::region ? Stage<
 
 constexpr int kSlots = 16;   // token slots of an MFMA tile
 
-template <bool Q5>
-__device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb, int m,
-                          uint32_t *xc, float *xd, uint32_t *wst, float *red) {
+// Physical row of tile row r of a rotated segment: consecutive rows (2p,
+// 2p+1) are elements i and i + hd/2 of the same head.
+__device__ __forceinline__ int rope_row(int r, int hd) {
+    const int half = hd >> 1, p = r >> 1;
+    return (p / half) * hd + (p % half) + (r & 1) * half;
+}
+
+template <bool Q5, bool EPI>
+__device__ void mfma_body(const GemvSeg &sg, int si, int tile, const uint8_t *xq, int nb, int m,
+                          uint32_t *xc, float *xd, uint32_t *wst, float *red, const QkvEpi &e) {
     using St = Stage<Q5>;
     constexpr int NSW = SliceWords<Q5>::n;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -161,10 +175,32 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
         for (int i = 0; i < 8; i++)
             xr[q][1 + i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
     }
+    // with the epilogue the Q5_0 segments are q and k (rows in rotation
+    // order) and the Q8_0 one is v (the launcher checks)
+    constexpr bool rot = EPI && Q5;
+    auto phys = [&](int r) { return rot ? rope_row(r, e.hd) : r; };
     const int otok = tid / kTileRows, orow = row0 + tid % kTileRows;
     const bool writer = tid < m * kTileRows && orow < sg.rows;
-    const float bias_o = (writer && sg.bias) ? sg.bias[orow] : 0.0f;
-    const float res_o = (writer && sg.residual) ? sg.residual[(size_t)otok * sg.rows + orow] : 0.0f;
+    const int prow = phys(min(orow, sg.rows - 1));
+    const float bias_o = (writer && sg.bias) ? sg.bias[prow] : 0.0f;
+    const float res_o = (!EPI && writer && sg.residual)
+                            ? sg.residual[(size_t)otok * sg.rows + orow] : 0.0f;
+    // the epilogue's position, RoPE factors and cache row (an invalid
+    // position reads table row 0 and rotates and appends nothing)
+    int pv = -1;
+    float cs = 1.0f, sn = 0.0f;
+    long long coff = -1;
+    if constexpr (EPI) {
+        const int tk = min(otok, m - 1);
+        pv = e.pos.get(tk);
+        if constexpr (rot) {
+            const int half = e.hd >> 1, pp = max(pv, 0);
+            const int i = (min(orow, sg.rows - 1) >> 1) % half;
+            cs = e.cos_tab[(size_t)pp * half + i];
+            sn = e.sin_tab[(size_t)pp * half + i];
+        }
+        if (si >= 1 && pv >= 0 && writer) coff = cache_row(e.c, tk, prow / e.hd, pv);
+    }
 
     // every phase's weight dwords, coalesced: flat index f over [16 rows]
     // [St::pu block pairs][words] of the phase; rows past the matrix re-read
@@ -180,7 +216,7 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
         for (int i = 0; i < St::per_lane; i++) {
             const int f = min(lane + kWave * i, kTileRows * kPh - 1);
             const int r = f / kPh, d = f - r * kPh;
-            const int row = min(row0 + r, sg.rows - 1);
+            const int row = phys(min(row0 + r, sg.rows - 1));
             const size_t off = min((size_t)pb * pair_bytes + 4 * (size_t)d, row_bytes - 4);
             raw[p][i] = *reinterpret_cast<const uint32_t *>(sg.W + (size_t)row * row_bytes + off);
         }
@@ -285,18 +321,35 @@ __device__ void mfma_body(const GemvSeg &sg, int tile, const uint8_t *xq, int nb
 #pragma unroll
     for (int t = 0; t < 4; t++) red[(wave * kWave + lane) * 4 + t] = acc[t];
     __syncthreads();
+    float o = 0.0f;
     if (writer) {
         const int src_lane = tid % kTileRows + 16 * (otok / 4), t = otok % 4;
         float v = 0.0f;
 #pragma unroll
         for (int wv = 0; wv < kMW; wv++) v += red[(wv * kWave + src_lane) * 4 + t];
-        float o = v + bias_o;
-        if (sg.residual) o = o + res_o;
+        o = v + bias_o;
+        if (!EPI && sg.residual) o = o + res_o;
+    }
+    if constexpr (EPI) {
+        // the partner row (element i + hd/2 for an even tile row, i for an
+        // odd one) is the neighbouring lane's
+        const float other = __shfl_xor(o, 1);
+        if (writer) {
+            float out = o;
+            if (rot && pv >= 0) out = (orow & 1) ? other * sn + o * cs : o * cs - other * sn;
+            sg.y[(size_t)otok * sg.rows + prow] = out;
+            if (coff >= 0) cache_put(e.c, si == 1, coff + prow % e.hd, out);
+        }
+    } else if (writer) {
         sg.y[(size_t)otok * sg.rows + orow] = o;
     }
 }
 
-__global__ __launch_bounds__(kMT) void k_gemv_mfma(GemvArgs a) {
+// four waves per SIMD, two workgroups per compute unit (at most 128
+// registers): a Q/K/V launch
+// has more tiles than compute units
+template <bool EPI>
+__global__ __launch_bounds__(kMT, 4) void k_gemv_mfma(GemvArgs a, QkvEpi e) {
     extern __shared__ __align__(16) uint32_t lds[];   // staged weights, then activations
     const int wg = blockIdx.x;
     const int si = (a.nseg > 2 && wg >= a.seg[2].wg_begin) ? 2
@@ -310,9 +363,9 @@ __global__ __launch_bounds__(kMT) void k_gemv_mfma(GemvArgs a) {
     float *xd = reinterpret_cast<float *>(xc + (size_t)a.m * nb * 8);
     float *red = reinterpret_cast<float *>(xc);
     if (sg.is_q5)
-        mfma_body<true>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red);
+        mfma_body<true, EPI>(sg, si, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red, e);
     else
-        mfma_body<false>(sg, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red);
+        mfma_body<false, EPI>(sg, si, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red, e);
 }
 
 size_t mfma_lds(int m, int nb) {
@@ -332,14 +385,38 @@ bool gemv_mfma_supported(int K, int m) {
            mfma_lds(m, nb) <= 80 * 1024;
 }
 
-hipError_t launch_gemv_mfma(GemvArgs a, hipStream_t st) {
+namespace {
+
+int plan_tiles(GemvArgs &a) {
     int total = 0;
     for (int i = 0; i < a.nseg; i++) {
         a.seg[i].wg_begin = total;
         total += (a.seg[i].rows + kTileRows - 1) / kTileRows;
     }
     for (int i = a.nseg; i < 3; i++) a.seg[i] = a.seg[0], a.seg[i].wg_begin = 1 << 30;
-    hipLaunchKernelGGL(k_gemv_mfma, dim3(total), dim3(kMT), mfma_lds(a.m, a.K / kQK), st, a);
+    return total;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_mfma(GemvArgs a, hipStream_t st) {
+    const int total = plan_tiles(a);
+    const QkvEpi none{};
+    hipLaunchKernelGGL(k_gemv_mfma<false>, dim3(total), dim3(kMT), mfma_lds(a.m, a.K / kQK), st, a,
+                       none);
+    return hipGetLastError();
+}
+
+// Segments q and k (Q5_0) and v (Q8_0), no residual, row counts multiples of
+// the head size (the caller checks the sizes; the weight formats are checked
+// here).
+hipError_t launch_gemv_mfma_qkv(GemvArgs a, const QkvEpi &e, hipStream_t st) {
+    if (a.nseg != 3 || !a.seg[0].is_q5 || !a.seg[1].is_q5 || a.seg[2].is_q5 || a.seg[0].residual ||
+        a.seg[1].residual || a.seg[2].residual)
+        return hipErrorInvalidValue;
+    const int total = plan_tiles(a);
+    hipLaunchKernelGGL(k_gemv_mfma<true>, dim3(total), dim3(kMT), mfma_lds(a.m, a.K / kQK), st, a,
+                       e);
     return hipGetLastError();
 }
 
