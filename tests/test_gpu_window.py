@@ -5,6 +5,10 @@
     the window: within 1e-4 x RMS of the oracle per sequence. Every token
     outside the window holds NaN (paged: pages wholly before the window are
     unmapped), so a read outside the window cannot go unnoticed.
+  * One sequence over a bf16 or fp8 cache (the bf16 matrix-core kernel), for
+    query groups of 1 to 8 heads, both head sizes, contiguous, paged, windowed
+    and ring caches and a chunk that is not a whole number of steps: within
+    1e-4 x RMS of the oracle on the same cache codes.
   * A window that covers the sequence gives the unwindowed result bit for bit;
     the two-pass entry points with the window give what the one-pass call does.
   * ck_kv_append on a ring writes slot pos % capacity and nothing else, bit for
@@ -134,6 +138,54 @@ def test_window_attention(layout, m, H, KV, hd, pos, W, R, chunk):
     for s in range(m):
         ref = oracle.attention(q[s * H * hd:(s + 1) * H * hd], oc, s, pos[s] + 1, H)
         assert_close_rms(got[s], ref, 1e-4, f"{layout} window attention s={s}")
+
+
+REDUCED_CASES = [
+    # layout, H, KV, hd, position, window, ring slots, chunk
+    ("contig", 28, 4, 128, 4096, 0, 0, 0),       # query groups of 7, 128-wide heads
+    ("contig", 14, 2, 64, 1024, 0, 0, 0),        # groups of 7, 64-wide heads
+    ("contig", 12, 4, 128, 1999, 0, 0, 0),       # groups of 3
+    ("contig", 24, 3, 128, 776, 0, 0, 40),       # groups of 8; partial steps inside the sequence
+    ("paged", 8, 8, 128, 2999, 0, 0, 0),         # paged, groups of 1
+    ("paged", 16, 2, 64, 699, 0, 0, 0),          # paged 64-wide heads, groups of 8
+    ("contig", 28, 4, 128, 4096, 1000, 0, 0),    # a window starting off a step
+    ("paged", 32, 8, 128, 1500, 256, 0, 0),
+    ("ring", 28, 4, 128, 9000, 1000, 1024, 64),  # a ring wrapping inside a step
+    ("ring", 32, 8, 128, 32768, 4096, 4096, 0),
+    ("ring", 4, 2, 64, 10, 1, 1, 0),
+]
+
+
+@pytest.mark.parametrize("layout,H,KV,hd,pos,W,R,chunk", REDUCED_CASES, ids=str)
+@pytest.mark.parametrize("dtype", [synth.KV_BF16, synth.KV_FP8], ids=["bf16", "fp8"])
+def test_reduced_cache_attention_one_sequence(dtype, layout, H, KV, hd, pos, W, R, chunk):
+    """One sequence over a bf16 or fp8 cache (the bf16 matrix-core kernel):
+    query groups of 1 to 8 heads, 64- and 128-wide heads, paged, windowed and
+    ring caches, an explicit chunk that is not a whole number of steps;
+    within 1e-4 x RMS of the oracle on the same cache codes."""
+    dev = cuda()
+    from decode_step_attention_layer_amd import ck
+
+    print(f"reduced-cache attention dtype={dtype} {layout} H={H} KV={KV} hd={hd} pos={pos} "
+          f"W={W} R={R} chunk={chunk}", flush=True)
+    k, v, table, _, geo = _build(layout, 1, KV, hd, [pos], W, R, 11 * H + W)
+    kc = synth.cache_codes(k, dtype, 40 + H, 0, True)
+    vc = synth.cache_codes(v, dtype, 40 + H, 0, False)
+    ks, vs = (synth.FP8_K_SCALE, synth.FP8_V_SCALE) if dtype == synth.KV_FP8 else (1.0, 1.0)
+    if layout == "paged":
+        oc = oracle.Cache(kc, vc, KV, hd, page_size=16, page_table=table,
+                          max_pages_per_seq=geo["max_pages_per_seq"], num_pages=geo["num_pages"],
+                          window=W, dtype=dtype, k_scale=ks, v_scale=vs)
+    else:
+        oc = oracle.Cache(kc, vc, KV, hd, capacity=geo["capacity"], ring=geo.get("ring", False),
+                          window=W, dtype=dtype, k_scale=ks, v_scale=vs)
+    kd, vd = _t(kc, dev), _t(vc, dev)
+    td = _t(table, dev) if table is not None else None
+    c = ck.kv_cache(kd, vd, KV, hd, page_table=td, dtype=dtype, k_scale=ks, v_scale=vs, **geo)
+    q = synth.seeded_vector(W + 5, H * hd)
+    got = _attend(ck, dev, c, q, [pos], 1, H, KV, hd, W, chunk)
+    ref = oracle.attention(q, oc, 0, pos + 1, H)
+    assert_close_rms(got[0], ref, 1e-4, f"{layout} reduced-cache attention")
 
 
 def test_window_covering_the_sequence_is_unwindowed():
