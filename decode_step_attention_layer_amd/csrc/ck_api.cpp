@@ -131,7 +131,7 @@ hipError_t gemv_any(const GemvArgs &g, hipStream_t st) {
 }
 
 struct WsLayout {
-    size_t xn, xq, q, k, v, attn, aq, aqx, cnt, part, total;
+    size_t xn, xq, q, k, v, attn, aq, aqx, xqi, aqi, cnt, part, total;
 };
 
 WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
@@ -149,6 +149,9 @@ WsLayout ws_layout(const ck_layer_desc *d, int max_ctx) {
     // the two-launch variant: the staged Q8_0 blocks of the attention output
     // and the counters of its second launch (the status word last)
     w.aqx = o; o = up256(o + m * (HD / CK_QK) * sizeof(XBlock));
+    // the batched projections' activation images of xq and aq
+    w.xqi = o; o = up256(o + ximage_bytes((int)m, (int)(D / CK_QK)));
+    w.aqi = o; o = up256(o + ximage_bytes((int)m, (int)(HD / CK_QK)));
     w.cnt = o; o = up256(o + sizeof(unsigned) * ato_counter_words(d->m, d->KV));
     const int maxc = attn_max_chunks(d->KV, d->H / d->KV, max_ctx, d->attn_chunk);
     w.part = o; o = up256(o + attn_partials_bytes(d->m, d->H, d->head_dim, maxc));
@@ -675,6 +678,12 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     unsigned *cnt = reinterpret_cast<unsigned *>(base + L.cnt);
     const int ncnt = two ? ato_counters(d.m, d.KV) : 0;
     const int zstride = ato_counter_stride();
+    // the fused batched layer hands its projections activation images (the
+    // two-launch variant's O projection is inside its second launch)
+    const bool img_x = fused && gemv_mfma_supported(d.D, d.m) && ximage_fits(d.m, d.D / CK_QK);
+    const bool img_a = fused && !two && gemv_mfma_supported(HD, d.m) && ximage_fits(d.m, HD / CK_QK);
+    uint32_t *xqi = img_x ? reinterpret_cast<uint32_t *>(base + L.xqi) : nullptr;
+    uint32_t *aqi = img_a ? reinterpret_cast<uint32_t *>(base + L.aqi) : nullptr;
 
     hipError_t e;
     if (!(phases & 1)) {
@@ -690,7 +699,7 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     } else {
         // steps 1-2: RMSNorm and the one Q8_0 quantization shared by Q, K and V
         if (fused) {
-            e = launch_rmsnorm_quant(x, w->gamma, xn, xq, d.m, d.D, d.eps, st);
+            e = launch_rmsnorm_quant(x, w->gamma, xn, xq, d.m, d.D, d.eps, st, xqi);
         } else {
             e = launch_rmsnorm(x, w->gamma, xn, d.m, d.D, d.eps, st);
             if (e == hipSuccess)
@@ -708,9 +717,10 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
         g.xq = xq;
         g.K = d.D;
         g.m = d.m;
+        g.ximg = xqi;
         // the fused layer on the matrix cores (no counters to clear): RoPE
         // and the append (steps 5-6) in the projection's epilogue
-        const bool epi = fused && ncnt == 0 && gemv_mfma_supported(g.K, g.m);
+        const bool epi = fused && ncnt == 0 && xqi;
         if (epi) {
             const QkvEpi ep{w->rope_cos, w->rope_sin, p, c, d.head_dim};
             e = launch_gemv_mfma_qkv(g, ep, st);
@@ -743,7 +753,8 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
 
     // step 7: attention over pos + 1 tokens, or the selection (fused: the
     // merge also quantizes)
-    e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, plan, part, st, sp);
+    e = launch_attention(q, c, p, attn, fused ? aq : nullptr, d.m, d.H, scale, plan, part, st, sp,
+                         aqi);
     if (e != hipSuccess) return CK_EHIP;
     if (!fused) {
         e = launch_quantize_q8_0(attn, aq, (long long)d.m * (HD / CK_QK), st);
@@ -758,6 +769,7 @@ int decode_layer_impl(const ck_layer_desc *desc, const ck_layer_weights *w, cons
     o.xq = aq;
     o.K = HD;
     o.m = d.m;
+    o.ximg = aqi;
     return hip_rc(gemv_any(o, st));
 }
 

@@ -145,14 +145,52 @@ struct GemvArgs {
     const uint8_t *xq;      // [m][K/32] Q8_0 blocks
     int K;
     int m;
+    const uint32_t *ximg;   // nullable: the same blocks as an activation image (below)
 };
+
+// The batched matrix-core GEMV's LDS image of m tokens' Q8_0 activation
+// blocks, written by the kernel that quantizes them so that the GEMV copies
+// it with 16-byte loads instead of unpacking 34-byte blocks: the codes
+// [nb][m][8 words] (block-major), then the scales [nb][16] as fp32 (the
+// fp16 scale's value), zero for the token slots from m to 15. One buffer of
+// ximage_bytes(m, nb) bytes, 16-byte aligned.
+struct XImage {
+    uint32_t *base;         // nullable: no image
+    int m, nb;
+};
+__host__ __device__ __forceinline__ size_t ximage_bytes(int m, int nb) {
+    return (size_t)nb * (32 * (size_t)m + 64);
+}
+// Whether the GEMV takes an image of m tokens x nb blocks (it loads at most
+// five 16-byte pieces per thread of its 512 ahead of the weights).
+__host__ __device__ __forceinline__ bool ximage_fits(int m, int nb) {
+    return (size_t)nb * (2 * m + 4) <= 5 * 512;
+}
+// Element group `sub` (codes 4sub..4sub+3, packed) of block `blk` of token
+// `tok`, and the block's scale on sub 0.
+__device__ __forceinline__ void ximage_put(const XImage &xi, int tok, int blk, int sub,
+                                           uint32_t packed, uint16_t dbits) {
+    xi.base[((size_t)blk * xi.m + tok) * 8 + sub] = packed;
+    if (sub == 0) {
+        float *sc = reinterpret_cast<float *>(xi.base + (size_t)xi.m * xi.nb * 8);
+        sc[blk * 16 + tok] = half_bits_to_float(dbits);
+    }
+}
+// The zero scales of token slots m..15 of blocks [b0, b1), by one
+// workgroup's threads.
+__device__ __forceinline__ void ximage_zero_pads(const XImage &xi, int b0, int b1, int tid,
+                                                 int nthreads) {
+    float *sc = reinterpret_cast<float *>(xi.base + (size_t)xi.m * xi.nb * 8);
+    for (int i = b0 * 16 + tid; i < b1 * 16; i += nthreads)
+        if ((i & 15) >= xi.m) sc[i] = 0.0f;
+}
 
 // Launchers. Each returns hipSuccess or the launch error.
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float *y, int m, int D,
                           float eps, hipStream_t st);
 hipError_t launch_quantize_q8_0(const float *x, uint8_t *y, long long nblocks, hipStream_t st);
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float *xn, uint8_t *xq,
-                                int m, int D, float eps, hipStream_t st);
+                                int m, int D, float eps, hipStream_t st, uint32_t *ximg = nullptr);
 bool gemv_shape_supported(int K);
 bool qkv_shape_supported(int D, int m);
 hipError_t launch_qkv(const float *x, const float *gamma, float eps, int D, int H, int KV, int hd,
@@ -232,12 +270,16 @@ struct SparseSel {
 hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positions &pos, int m,
                                int H, float scale, const AttnPlan &plan, void *partials,
                                hipStream_t st, const SparseSel *sp = nullptr);
+// ximg (nullable, with out_q8): the output's Q8_0 blocks also as an
+// activation image of m tokens x H*hd/32 blocks.
 hipError_t launch_attn_merge(const void *partials, const Positions &pos, int window, int m,
                              int H, int KV, int hd, const AttnPlan &plan, float *out,
-                             uint8_t *out_q8, hipStream_t st, const SparseSel *sp = nullptr);
+                             uint8_t *out_q8, hipStream_t st, const SparseSel *sp = nullptr,
+                             uint32_t *ximg = nullptr);
 hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
-                            void *partials, hipStream_t st, const SparseSel *sp = nullptr);
+                            void *partials, hipStream_t st, const SparseSel *sp = nullptr,
+                            uint32_t *ximg = nullptr);
 
 // Attention + merge + Q8_0 + O projection in one launch (k_ato.hip): the
 // second launch of the two-launch layer. Its counters (ato_counter_words)

@@ -111,7 +111,28 @@ struct MergeArgs {
     const float *sink;   // nullable: [H] logits joining the denominator only
     float *out;          // [m][H][HD]
     uint8_t *out_q8;     // nullable: [m][H*HD/32] Q8_0 blocks
+    XImage xi;           // with out_q8: the blocks also as an activation image
 };
+
+// The Q8_0 of output elements 4*e4.. of (sequence s, head h) (every lane of
+// the block's group of 8 calling), into out_q8 and the image; the image's
+// zero scales of the head's blocks written by its sequence-0 workgroup.
+template <int HD>
+__device__ __forceinline__ void merge_q8_out(const MergeArgs &a, float4 v, int s, int h, int e4) {
+    const size_t oi = ((size_t)s * a.H + h) * HD + 4 * e4;
+    uint32_t packed;
+    uint16_t dbits;
+    quantize_q8_0_x4_codes(v, packed, dbits);
+    uint8_t *blk = a.out_q8 + (oi / kQK) * kQ8Bytes;
+    uint16_t *dst = reinterpret_cast<uint16_t *>(blk + 2 + 4 * (e4 & 7));
+    dst[0] = (uint16_t)(packed & 0xFFFF);
+    dst[1] = (uint16_t)(packed >> 16);
+    if ((e4 & 7) == 0) *reinterpret_cast<uint16_t *>(blk) = dbits;
+    if (a.xi.base) {
+        ximage_put(a.xi, s, (h * HD + 4 * e4) / kQK, e4 & 7, packed, dbits);
+        if (s == 0) ximage_zero_pads(a.xi, h * HD / kQK, (h + 1) * HD / kQK, e4, HD / 4);
+    }
+}
 
 constexpr int kMergeThreads = 256;
 
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
         const float4 v = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
         const size_t oi = ((size_t)s * a.H + h) * HD + 4 * tid;
         *reinterpret_cast<float4 *>(&a.out[oi]) = v;
-        if (a.out_q8) quantize_q8_0_x4(v, a.out_q8 + (oi / kQK) * kQ8Bytes, tid & 7);
+        if (a.out_q8) merge_q8_out<HD>(a, v, s, h, tid);
     }
 }
 
@@ -351,7 +372,7 @@ __global__ __launch_bounds__(kWave * NWV) void k_attn_merge1(MergeArgs a) {
         const float4 v = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
         const size_t oi = ((size_t)s * a.H + h) * HD + 4 * d4;
         *reinterpret_cast<float4 *>(&a.out[oi]) = v;
-        if (a.out_q8) quantize_q8_0_x4(v, a.out_q8 + (oi / kQK) * kQ8Bytes, d4 & 7);
+        if (a.out_q8) merge_q8_out<HD>(a, v, s, h, d4);
     }
 }
 
@@ -558,7 +579,8 @@ hipError_t launch_attn_partial(const float *q, const CacheView &c, const Positio
 
 hipError_t launch_attn_merge(const void *partials, const Positions &pos, int window, int m,
                              int H, int KV, int hd, const AttnPlan &plan, float *out,
-                             uint8_t *out_q8, hipStream_t st, const SparseSel *sp) {
+                             uint8_t *out_q8, hipStream_t st, const SparseSel *sp,
+                             uint32_t *ximg) {
     const uint8_t *base = static_cast<const uint8_t *>(partials);
     MergeArgs b;
     b.po = reinterpret_cast<const float *>(base);
@@ -574,6 +596,7 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
     b.sink = sp ? sp->sink : nullptr;
     b.out = out;
     b.out_q8 = out_q8;
+    b.xi = XImage{out_q8 ? ximg : nullptr, m, H * hd / kQK};
     // up to 128 chunks per sequence: one wavefront per 32 chunks (measured
     // faster than the workgroup merge at 22 and 43 chunks with one and two
     // wavefronts, neutral at 57, and faster at 86 with three: 4.4 against
@@ -606,11 +629,12 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
 
 hipError_t launch_attention(const float *q, const CacheView &c, const Positions &pos, float *out,
                             uint8_t *out_q8, int m, int H, float scale, const AttnPlan &plan,
-                            void *partials, hipStream_t st, const SparseSel *sp) {
+                            void *partials, hipStream_t st, const SparseSel *sp,
+                            uint32_t *ximg) {
     hipError_t e = launch_attn_partial(q, c, pos, m, H, scale, plan, partials, st, sp);
     if (e != hipSuccess) return e;
     return launch_attn_merge(partials, pos, c.window, m, H, c.kv_heads, c.head_dim, plan, out,
-                             out_q8, st, sp);
+                             out_q8, st, sp, ximg);
 }
 
 }  // namespace ck

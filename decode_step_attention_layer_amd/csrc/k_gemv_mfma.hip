@@ -142,9 +142,12 @@ __device__ __forceinline__ int rope_row(int r, int hd) {
     return (p / half) * hd + (p % half) + (r & 1) * half;
 }
 
-template <bool Q5, bool EPI>
-__device__ void mfma_body(const GemvSeg &sg, int si, int tile, const uint8_t *xq, int nb, int m,
-                          uint32_t *xc, float *xd, uint32_t *wst, float *red, const QkvEpi &e) {
+constexpr int kImgPer = 5;   // 16-byte image pieces a thread loads (ximage_fits)
+
+template <bool Q5, bool EPI, bool IMG>
+__device__ void mfma_body(const GemvSeg &sg, int si, int tile, const uint8_t *xq,
+                          const uint32_t *ximg, int nb, int m, uint32_t *xc, float *xd,
+                          uint32_t *wst, float *red, const QkvEpi &e) {
     using St = Stage<Q5>;
     constexpr int NSW = SliceWords<Q5>::n;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -163,17 +166,32 @@ __device__ void mfma_body(const GemvSeg &sg, int si, int tile, const uint8_t *xq
     // load issued before it): the activation blocks of this thread (up to
     // two, when the batch has at most 2 * kMT blocks), the output thread's
     // bias and residual, then every phase's weight dwords.
+    // An activation image goes straight into LDS, no registers: wave w's
+    // i-th load fills pieces [i*512 + 64w, +64) of the LDS image from 64
+    // consecutive 16-byte global pieces; lanes past the image re-read its
+    // last piece and land in the slack after it (mfma_lds).
     const int nxb = m * nb;
     const bool xpre = nxb <= 2 * kMT;
-    uint32_t xr[2][9];
+    const int n16 = nb * (2 * m + 4);
+    uint32_t xr[IMG ? 1 : 2][9];
+    if constexpr (IMG) {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(ximg);
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-        const int b = min(tid + q * kMT, nxb - 1);
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)b * kQ8Bytes);
-        xr[q][0] = src[0];
+        for (int i = 0; i < kImgPer; i++) {
+            const int p0 = i * kMT + wave * kWave;
+            __builtin_amdgcn_global_load_lds(src + (size_t)min(p0 + lane, n16 - 1) * 16,
+                                             xc + (size_t)p0 * 4, 16, 0, 0);
+        }
+    } else {
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            xr[q][1 + i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+        for (int q = 0; q < 2; q++) {
+            const int b = min(tid + q * kMT, nxb - 1);
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(xq + (size_t)b * kQ8Bytes);
+            xr[q][0] = src[0];
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                xr[q][1 + i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+        }
     }
     // with the epilogue the Q5_0 segments are q and k (rows in rotation
     // order) and the Q8_0 one is v (the launcher checks)
@@ -235,6 +253,12 @@ __device__ void mfma_body(const GemvSeg &sg, int si, int tile, const uint8_t *xq
         dst[0] = make_uint4(w[1], w[2], w[3], w[4]);
         dst[1] = make_uint4(w[5], w[6], w[7], w[8]);
     };
+    if constexpr (IMG) {
+        // the image is this LDS layout (codes, then the scales with their
+        // zero slots): every load of this thread has landed, its image
+        // pieces among them, and the barrier below publishes them
+        __builtin_amdgcn_s_waitcnt(0);
+    } else {
     for (int i = tid; i < nb * kSlots; i += kMT)
         if ((i & (kSlots - 1)) >= m) xd[i] = 0.0f;
     if (xpre) {
@@ -251,6 +275,7 @@ __device__ void mfma_body(const GemvSeg &sg, int si, int tile, const uint8_t *xq
                 w[1 + i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
             put_x(b, w);
         }
+    }
     }
     __syncthreads();
 
@@ -348,7 +373,7 @@ __device__ void mfma_body(const GemvSeg &sg, int si, int tile, const uint8_t *xq
 // four waves per SIMD, two workgroups per compute unit (at most 128
 // registers): a Q/K/V launch
 // has more tiles than compute units
-template <bool EPI>
+template <bool EPI, bool IMG>
 __global__ __launch_bounds__(kMT, 4) void k_gemv_mfma(GemvArgs a, QkvEpi e) {
     extern __shared__ __align__(16) uint32_t lds[];   // staged weights, then activations
     const int wg = blockIdx.x;
@@ -363,14 +388,18 @@ __global__ __launch_bounds__(kMT, 4) void k_gemv_mfma(GemvArgs a, QkvEpi e) {
     float *xd = reinterpret_cast<float *>(xc + (size_t)a.m * nb * 8);
     float *red = reinterpret_cast<float *>(xc);
     if (sg.is_q5)
-        mfma_body<true, EPI>(sg, si, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red, e);
+        mfma_body<true, EPI, IMG>(sg, si, wg - sg.wg_begin, a.xq, a.ximg, nb, a.m, xc, xd, wst,
+                                  red, e);
     else
-        mfma_body<false, EPI>(sg, si, wg - sg.wg_begin, a.xq, nb, a.m, xc, xd, wst, red, e);
+        mfma_body<false, EPI, IMG>(sg, si, wg - sg.wg_begin, a.xq, a.ximg, nb, a.m, xc, xd, wst,
+                                   red, e);
 }
 
-size_t mfma_lds(int m, int nb) {
-    const size_t xs = sizeof(uint32_t) * 8 * (size_t)m * nb + sizeof(float) * kSlots * (size_t)nb;
+// img: room for every piece the image loads write (kImgPer per thread)
+size_t mfma_lds(int m, int nb, bool img = false) {
+    size_t xs = sizeof(uint32_t) * 8 * (size_t)m * nb + sizeof(float) * kSlots * (size_t)nb;
     const size_t red = sizeof(float) * kMT * 4;
+    if (img && xs < (size_t)16 * kImgPer * kMT) xs = (size_t)16 * kImgPer * kMT;
     return sizeof(uint32_t) * kMW * kStageRegion + (xs > red ? xs : red);
 }
 
@@ -402,8 +431,13 @@ int plan_tiles(GemvArgs &a) {
 hipError_t launch_gemv_mfma(GemvArgs a, hipStream_t st) {
     const int total = plan_tiles(a);
     const QkvEpi none{};
-    hipLaunchKernelGGL(k_gemv_mfma<false>, dim3(total), dim3(kMT), mfma_lds(a.m, a.K / kQK), st, a,
-                       none);
+    const int nb = a.K / kQK;
+    if (a.ximg && ximage_fits(a.m, nb))
+        hipLaunchKernelGGL((k_gemv_mfma<false, true>), dim3(total), dim3(kMT),
+                           mfma_lds(a.m, nb, true), st, a, none);
+    else
+        hipLaunchKernelGGL((k_gemv_mfma<false, false>), dim3(total), dim3(kMT), mfma_lds(a.m, nb),
+                           st, a, none);
     return hipGetLastError();
 }
 
@@ -412,11 +446,11 @@ hipError_t launch_gemv_mfma(GemvArgs a, hipStream_t st) {
 // here).
 hipError_t launch_gemv_mfma_qkv(GemvArgs a, const QkvEpi &e, hipStream_t st) {
     if (a.nseg != 3 || !a.seg[0].is_q5 || !a.seg[1].is_q5 || a.seg[2].is_q5 || a.seg[0].residual ||
-        a.seg[1].residual || a.seg[2].residual)
+        a.seg[1].residual || a.seg[2].residual || !a.ximg || !ximage_fits(a.m, a.K / kQK))
         return hipErrorInvalidValue;
     const int total = plan_tiles(a);
-    hipLaunchKernelGGL(k_gemv_mfma<true>, dim3(total), dim3(kMT), mfma_lds(a.m, a.K / kQK), st, a,
-                       e);
+    hipLaunchKernelGGL((k_gemv_mfma<true, true>), dim3(total), dim3(kMT),
+                       mfma_lds(a.m, a.K / kQK, true), st, a, e);
     return hipGetLastError();
 }
 

@@ -77,14 +77,17 @@ __global__ __launch_bounds__(256) void k_quantize_q8_0(const float *__restrict__
 // variant when its single-kernel first half does not fit): the normalized row
 // is written to xn and its Q8_0 blocks to xq, with the same row function as
 // the fused first half.
+// With an activation image (xi.base set) the blocks also go there, and
+// workgroup 0 writes its zero scales.
 __global__ __launch_bounds__(kGemvThreads) void k_rmsnorm_quant(const float *__restrict__ x,
                                                                 const float *__restrict__ gamma,
                                                                 float *__restrict__ xn,
                                                                 uint8_t *__restrict__ xq, int D,
-                                                                float eps) {
+                                                                float eps, XImage xi) {
     __shared__ float red[2 * kGemvThreads / kWave];
     const size_t s = blockIdx.x;
     const int nb = D / kQK;
+    if (xi.base && s == 0) ximage_zero_pads(xi, 0, nb, threadIdx.x, kGemvThreads);
     norm_quant_row(x + s * D, gamma, D, eps, red,
                    [&](int c, float4 v, uint32_t packed, uint16_t dbits, int) {
                        reinterpret_cast<float4 *>(xn + s * D)[c] = v;
@@ -93,6 +96,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_rmsnorm_quant(const float *__r
                        dst[0] = (uint16_t)(packed & 0xFFFF);
                        dst[1] = (uint16_t)(packed >> 16);
                        if ((c & 7) == 0) *reinterpret_cast<uint16_t *>(blk) = dbits;
+                       if (xi.base) ximage_put(xi, (int)s, c >> 3, c & 7, packed, dbits);
                    });
 }
 
@@ -111,9 +115,10 @@ hipError_t launch_quantize_q8_0(const float *x, uint8_t *y, long long nblocks, h
 }
 
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float *xn, uint8_t *xq, int m,
-                                int D, float eps, hipStream_t st) {
+                                int D, float eps, hipStream_t st, uint32_t *ximg) {
+    const XImage xi{ximg, m, D / kQK};
     hipLaunchKernelGGL(k_rmsnorm_quant, dim3(m), dim3(kGemvThreads), 0, st, x, gamma, xn, xq, D,
-                       eps);
+                       eps, xi);
     return hipGetLastError();
 }
 
