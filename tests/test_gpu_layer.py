@@ -1,5 +1,6 @@
 """GPU parity of the whole decode layer (ck_decode_layer) against the oracle,
-at the five workloads' full sizes and in the configuration the benchmark times.
+at the five workloads' full sizes and in the configuration the benchmark times,
+and at three more paged batches (4, 5 and 12 tokens).
 
 Per layer (parity.check_layer), with the oracle run on the same input the GPU
 layer received:
@@ -65,7 +66,7 @@ def _run_and_check(name, variant, attn_chunk=0, layers=None):
     from decode_step_attention_layer_amd.workload import DeviceStack
 
     dev = cuda()
-    cfg = synth.CONFIGS[name]
+    cfg = synth.CONFIGS[name] if name in synth.CONFIGS else BATCHES[name]
     stack = DeviceStack(cfg, dev, keep_host=True, spare_pages=4 if cfg.page_size else 0,
                         layers=layers)
     desc = stack.desc(variant, attn_chunk)
@@ -203,3 +204,23 @@ def test_layer_c4(variant):
 @pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
 def test_layer_c5(variant):
     _run_and_check("c5", variant)
+
+
+# Other batches of the paged path: the matrix-core projections from 4 tokens,
+# the activation images' zero token slots from m to 15, the Q/K/V epilogue at
+# other head counts and widths.
+BATCHES = {
+    "b4": synth.Config("b4", 21, 3584, 28, 4, 128, 1e4, layers=1, m=4, page_size=16,
+                       min_ctx=100, max_ctx=900),
+    "b5": synth.Config("b5", 22, 4096, 32, 8, 128, 5e5, layers=1, m=5, page_size=16,
+                       min_ctx=64, max_ctx=700),
+    "b12": synth.Config("b12", 23, 896, 14, 2, 64, 1e4, layers=2, m=12, page_size=16,
+                        min_ctx=30, max_ctx=300),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("name", sorted(BATCHES))
+def test_layer_other_batches(name, variant):
+    _run_and_check(name, variant)
