@@ -17,9 +17,9 @@
 // fp8 E4M3 codes decoded to bf16 (their 3-bit significands fit), the scales
 // applied to q (k_scale) and to the chunk's output (v_scale). q (scaled to
 // log2 units) and the probabilities P enter as two bf16 terms each, a high
-// part and the bf16 of the remainder (never zero, see bf16_split), so each
-// product keeps about 16 bits of significand: two MFMAs per contraction
-// step, fp32 accumulation.
+// part and the bf16 of the remainder (for bf16 caches never zero, see
+// bf16_split2), so each product keeps about 16 bits of significand: two
+// MFMAs per contraction step, fp32 accumulation.
 //
 // Lane (hl = l % 16, kq = l / 16):
 //   scores: for the 16-token half mb of the step, K of token 16mb + hl at
@@ -30,12 +30,15 @@
 //     16(e/4) + 4kq + e%4 (e < 8) at dim VT*hl + T, so that its B operand is
 //     exactly the 8 probabilities it computed (no exchange between lanes);
 //     the 8 rows' VT-dim slices are loaded whole (16 lanes read a full row
-//     per instruction) and regrouped in registers; the lane ends holding,
-//     for head hl, dims VT*(4kq + r) + T.
+//     per instruction) and regrouped in registers, one byte permute per
+//     operand word; the lane ends holding, for head hl, dims
+//     VT*(4kq + r) + T.
 // Every load of a step is issued before its arithmetic (a scheduling
-// barrier keeps them together); tokens past the chunk re-read its last row,
-// their scores masked and their V rows zeroed. The waves' online-softmax
-// states are combined through LDS as in the fp32 matrix-core kernel.
+// barrier keeps them together). Only a wave's last step can reach past the
+// chunk: its tokens there re-read the chunk's last row, their scores masked
+// (bf16: their V rows zeroed too); every other step runs unmasked with one
+// address. The waves' online-softmax states are combined through LDS as in
+// the fp32 matrix-core kernel.
 #include "ck_attn_common.hpp"
 
 namespace ck {

@@ -97,8 +97,10 @@ typedef struct ck_kv_cache {
  * k_scale and one v_scale). FP8 is OCP E4M3 (bias 7, largest finite 448,
  * S.1111.111 the only NaN). A store rounds to nearest, ties to even; an fp8
  * store encodes fp32(x / scale) and saturates at +-448 (NaN -> 0x7F). The
- * attention reads every element back as fp32 (fp8: the product of the code
- * value and the scale, in fp32). */
+ * attention attends the value each element encodes (fp8: the code's value
+ * times the scale). One sequence over a bf16 or fp8 cache is attended on the
+ * bf16 matrix cores: the values exact, q and the probabilities as two bf16
+ * terms each (about 16 significant bits per product), fp32 sums. */
 #define CK_KV_F32 0
 #define CK_KV_BF16 1
 #define CK_KV_FP8_E4M3 2
@@ -213,9 +215,9 @@ int ck_attn_decode_gqa(const float *q, const ck_kv_cache *kv, const int32_t *pos
  * chunk is used as given. The automatic split (chunk 0) of this pair depends
  * on neither the cache type nor the kernel, so it can differ from
  * ck_attn_decode_gqa's, which sizes chunks for the kernel that runs (the
- * matrix-core kernel for query groups over 4 heads on an fp32 cache, whole
- * steps of the vector kernel otherwise): with equal explicit chunks the two
- * give identical bits. */
+ * matrix-core kernels for query groups over 4 heads on an fp32 cache and for
+ * one sequence over a bf16 or fp8 cache, whole steps of the vector kernel
+ * otherwise): with equal explicit chunks the two give identical bits. */
 int ck_attn_partial(const float *q, const ck_kv_cache *kv, const int32_t *pos_host, int m, int H,
                     float scale, int chunk, void *partials, size_t bytes, void *stream);
 int ck_attn_merge(const void *partials, size_t bytes, const int32_t *pos_host, int m, int H,
