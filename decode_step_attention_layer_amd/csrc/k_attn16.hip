@@ -23,9 +23,11 @@
 //
 // Lane (hl = l % 16, kq = l / 16):
 //   scores: for the 16-token half mb of the step, K of token 16mb + hl at
-//     dims KQ*kq + 8kb + e (kq's contiguous quarter of the row; a
-//     contraction may visit its index in any order), q of head hl at the
-//     same dims; the lane receives the scores of tokens 16mb + 4kq + r;
+//     dims 32kb + 8kq + e (bf16: the four lanes of a row read 64 adjacent
+//     bytes per load) or KQ*kq + 8kb + e (fp8: kq's contiguous quarter of
+//     the row; a contraction may visit its index in any order), q of head
+//     hl at the same dims; the lane receives the scores of tokens
+//     16mb + 4kq + r;
 //   value sums: its A operand for output tile T is V of the 8 tokens
 //     16(e/4) + 4kq + e%4 (e < 8) at dim VT*hl + T, so that its B operand is
 //     exactly the 8 probabilities it computed (no exchange between lanes);
@@ -190,13 +192,27 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
     const uint8_t *Kc = static_cast<const uint8_t *>(a.c.k);
     const uint8_t *Vc = static_cast<const uint8_t *>(a.c.v);
 
-    // a step's loads: K of tokens tb + 16mb + hl (the lane's quarter of the
-    // row), V of tokens tb + 16(e/4) + 4kq + e%4 (the lane's VT dims). FULL:
+    // a step's loads: K of tokens tb + 16mb + hl (the lane's K dims), V of
+    // tokens tb + 16(e/4) + 4kq + e%4 (the lane's VT dims). FULL:
     // all 32 tokens lie in the chunk and in consecutive slots of a
     // contiguous cache, so every row is the step's first row plus a constant
     // (one address a step, the rest immediate offsets); otherwise each row
     // is located on its own, rows past the chunk re-reading its last row.
-    const int k_lane = hl * HD + KQ * kq;       // element offsets from the step's first row
+    // The lane's K dims, in 16-byte pieces. bf16: piece i is elements
+    // 32i + 8kq .. + 7 of the row (k-slice i), so that the four lanes of a
+    // row read 64 adjacent bytes per load instruction and consecutive
+    // instructions stay on one 128-byte line (with each lane's quarter of
+    // the row contiguous, every instruction touched both lines of 16 rows,
+    // and streamed lines were fetched again: 8% over the K and V bytes, and
+    // 31.0 against 24.3 us at long context). fp8: the row's kq-th quarter
+    // (its one 128-byte line; interleaved pieces measured the same); q takes
+    // the same dims.
+    constexpr bool KI = DT == CK_KV_BF16;
+    constexpr int NKP = KQ * EB / KLOAD;            // K pieces per row and lane
+    static_assert(KLOAD == 16, "16-byte K pieces");
+    auto kpiece = [&](int i) { return KI ? 32 * i : 16 * i; };   // elements
+    const int k_lane0 = KI ? 8 * kq : KQ * kq;
+    const int k_lane = hl * HD + k_lane0;       // element offsets from the step's first row
     const int v_lane = 4 * kq * HD + VT * hl;
     auto load_step = [&](auto full, int tb, uint32_t (&kw)[2][KW], uint32_t (&vw)[8][VW]) {
         constexpr bool FULL = decltype(full)::value;
@@ -207,8 +223,8 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
 #pragma unroll
             for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-                for (int i = 0; i < KQ * EB / KLOAD; i++)
-                    load_bytes<KLOAD, STREAM>(kp + 16 * mb * HD * EB + KLOAD * i,
+                for (int i = 0; i < NKP; i++)
+                    load_bytes<KLOAD, STREAM>(kp + (16 * mb * HD + kpiece(i)) * EB,
                                               &kw[mb][i * KLOAD / 4]);
 #pragma unroll
             for (int e = 0; e < 8; e++)
@@ -217,10 +233,10 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
 #pragma unroll
             for (int mb = 0; mb < 2; mb++) {
                 const uint8_t *kp =
-                    Kc + (row_off(min(tb + 16 * mb + hl, t1 - 1)) + KQ * kq) * EB;
+                    Kc + (row_off(min(tb + 16 * mb + hl, t1 - 1)) + k_lane0) * EB;
 #pragma unroll
-                for (int i = 0; i < KQ * EB / KLOAD; i++)
-                    load_bytes<KLOAD, STREAM>(kp + KLOAD * i, &kw[mb][i * KLOAD / 4]);
+                for (int i = 0; i < NKP; i++)
+                    load_bytes<KLOAD, STREAM>(kp + kpiece(i) * EB, &kw[mb][i * KLOAD / 4]);
             }
 #pragma unroll
             for (int e = 0; e < 8; e++) {
@@ -236,10 +252,12 @@ __device__ __forceinline__ bool attn_item_mfma16(const AttnArgs &a, int item, in
     // flight); fp8: the K scale folded in
     float qf[KQ];
     {
-        const float *qh = a.q + ((size_t)s * a.H + (size_t)g * G + min(hl, G - 1)) * HD + KQ * kq;
+        // qf[8kb + e] is q at the dim of k-slice kb, element e
+        const float *qh = a.q + ((size_t)s * a.H + (size_t)g * G + min(hl, G - 1)) * HD + k_lane0;
 #pragma unroll
         for (int i = 0; i < KQ; i += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(qh + i);
+            const int d = KI ? 32 * (i >> 3) + (i & 7) : i;
+            const float4 v = *reinterpret_cast<const float4 *>(qh + d);
             qf[i] = v.x;
             qf[i + 1] = v.y;
             qf[i + 2] = v.z;
