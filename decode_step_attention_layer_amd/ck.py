@@ -207,9 +207,13 @@ def ck_rope(q, k, cos_tab, sin_tab, tab_rows, pos, m, H, KV, hd, stream=None):
 def kv_cache(k, v, kv_heads, head_dim, capacity=0, page_size=0, page_table=None,
              max_pages_per_seq=0, num_pages=0, dtype=CK_KV_F32, k_scale=1.0,
              v_scale=1.0, window=0, ring=False) -> CkKVCache:
-    return CkKVCache(_ptr(k), _ptr(v), kv_heads, head_dim, capacity, page_size,
-                     _ptr(page_table), max_pages_per_seq, num_pages, dtype, k_scale, v_scale,
-                     window, int(ring))
+    c = CkKVCache(_ptr(k), _ptr(v), kv_heads, head_dim, capacity, page_size,
+                  _ptr(page_table), max_pages_per_seq, num_pages, dtype, k_scale, v_scale,
+                  window, int(ring))
+    # the struct holds raw device pointers: it keeps the objects they point
+    # into alive as long as it lives
+    c._keep = (k, v, page_table)
+    return c
 
 
 def ck_kv_append(cache: CkKVCache, k, v, pos, m, stream=None):

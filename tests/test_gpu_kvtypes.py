@@ -5,7 +5,9 @@
     exactly the oracle's codes at the appended slot and nothing elsewhere.
   * Load: attention over a single cached token returns that token's V, so
     every fp8 code (and a sweep of bf16 codes) read through the attention
-    kernel equals the oracle's decoded value (times the scale) exactly.
+    kernel equals the oracle's decoded value (times the scale) exactly; and
+    every K code (fp8 but the NaNs; bf16 finite codes with the subnormals)
+    read through the scores gives the oracle's softmax weights.
   * Attention over thousands of cached tokens within 1e-4 x RMS of the
     oracle on the same cache bytes, contiguous and paged.
   * Whole layer (tiny, long-context, batched paged) with fused and chain
@@ -126,7 +128,9 @@ def test_single_token_attention_decodes_every_code(dtype):
     kc = np.zeros(shape, NP_T[dtype])
     vc = np.zeros(shape, NP_T[dtype])
     vc[0, :, 0, :] = codes.reshape(KV, hd)
-    cache = ck.kv_cache(_t(kc, dev), _t(vc, dev), KV, hd, 4, dtype=dtype, k_scale=ks, v_scale=vs)
+    # the cache view holds raw pointers: the tensors must outlive every call
+    kd, vd = _t(kc, dev), _t(vc, dev)
+    cache = ck.kv_cache(kd, vd, KV, hd, 4, dtype=dtype, k_scale=ks, v_scale=vs)
     q = torch.ones(H * hd, dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
     nws = ck.ck_attn_workspace_size(1, H, KV, hd, 1, 0)
@@ -141,6 +145,68 @@ def test_single_token_attention_decodes_every_code(dtype):
     # back as +0); every other value, subnormals and infinities included, exactly
     bad = got[~nan] != want[~nan]
     assert not bad.any(), (codes[~nan][bad], got[~nan][bad], want[~nan][bad])
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=IDS)
+def test_scores_decode_every_k_code(dtype):
+    """The score path reads every K code as the oracle does: one KV head per
+    code (every fp8 code but the NaNs; a sweep of finite bf16 codes with the
+    subnormals and the extremes), two cached tokens per head: token 0's K
+    holds the code at dim 0, token 1's K is zero, and V picks out the two
+    softmax weights. q is scaled per head so that a correctly read code
+    scores exactly 1 against token 1's 0 (within |q| <= 1e30: the smallest
+    bf16 subnormals cannot reach it): a code read as another value (a
+    subnormal flushed to zero, a wrong exponent) moves the weights far
+    beyond the 1e-4 x RMS the output is held to against the oracle."""
+    import torch
+
+    dev = cuda()
+    from decode_step_attention_layer_amd import ck
+
+    hd = 64
+    ks, vs = SCALES[dtype]
+    g = np.random.default_rng(5)
+    if dtype == synth.KV_FP8:
+        codes = g.permutation(np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8))
+    else:
+        fixed = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x00FF, 0x7F7F, 0xFF7F, 0x3F80,
+                 0xBF80, 0x0100, 0x4B00, 0x3400]
+        rnd = g.integers(0, 2**16, size=400).astype(np.uint16)
+        rnd = rnd[(rnd & 0x7F80) != 0x7F80][:240]          # finite only
+        codes = np.concatenate([np.array(fixed, np.uint16), rnd])
+    KV = H = len(codes)
+    kc = np.zeros((1, KV, 2, hd), NP_T[dtype])
+    kc[0, :, 0, 0] = codes
+    one = oracle.encode_cache(np.array([1.0], np.float32), dtype, vs)[0]
+    vc = np.zeros((1, KV, 2, hd), NP_T[dtype])
+    vc[0, :, 0, 0] = one
+    vc[0, :, 1, 1] = one
+    kval = oracle.decode_cache(codes, dtype, ks).astype(np.float64)
+    scale = 1.0 / math.sqrt(hd)
+    q = np.zeros(H * hd, np.float32)
+    nz = kval != 0
+    # |q| within [1e-30, 1e30]: bf16 codes too small (or too large) for a
+    # score of 1 with such a q are read at the nearest bound instead
+    target = 1.0 / (kval[nz] * scale)
+    q[np.arange(H)[nz] * hd] = (np.sign(target) *
+                                np.clip(np.abs(target), 1e-30, 1e30)).astype(np.float32)
+    kd, vd = _t(kc, dev), _t(vc, dev)   # the view holds raw pointers: keep them alive
+    cache = ck.kv_cache(kd, vd, KV, hd, 2, dtype=dtype, k_scale=ks, v_scale=vs)
+    out = torch.empty(H * hd, dtype=torch.float32, device=dev)
+    nws = ck.ck_attn_workspace_size(1, H, KV, hd, 2, 0)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    ck.ck_attn_decode_gqa(_t(q, dev), cache, [1], out, 1, H, scale, 0, ws, nws)
+    torch.cuda.synchronize()
+    got = host(out)
+    oc = oracle.Cache(kc, vc, KV, hd, capacity=2, dtype=dtype, k_scale=ks, v_scale=vs)
+    ref = oracle.attention(q, oc, 0, 2, H)
+    # every head's weight pair, one by one (a correctly read code gives
+    # weights e/(e+1), 1/(e+1)), then the whole output
+    w = got.reshape(H, hd)[:, :2]
+    wr = ref.reshape(H, hd)[:, :2]
+    bad = np.abs(w - wr).max(axis=1) > 1e-4 * np.abs(wr).max(axis=1)
+    assert not bad.any(), ([hex(int(c)) for c in codes[bad]], w[bad], wr[bad])
+    assert_close_rms(got, ref, 1e-4, "per-code scores")
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=IDS)
