@@ -417,11 +417,11 @@ def extra_records(args, stacks, step_bytes, variant, us_layer):
     return {"variants_c3": var, "secondary": secondary, "stream_probe": stream_probe()}
 
 
-def _time_launches(fn, reps):
-    """Average time of one fn() launch: `reps` launches captured in one HIP
-    graph (torch's graph API on the current stream) and replayed, timed with
-    events on that stream, so that the host's launch rate does not pace short
-    kernels."""
+def _time_launches(fn, reps, passes=5):
+    """Time of one fn() launch: `reps` launches captured in one HIP graph
+    (torch's graph API on the current stream), so that the host's launch rate
+    does not pace short kernels, replayed `passes` times, each replay timed
+    with events on that stream; the median replay's average per launch."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -433,12 +433,15 @@ def _time_launches(fn, reps):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    g.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / reps     # us per launch
+    per = []
+    for _ in range(passes):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / reps)     # us per launch
+    return pct(per, 50)
 
 
 def roofline(args, stacks, desc, ws, nbytes):
