@@ -92,12 +92,12 @@ __device__ __forceinline__ f32x2 fp8_pair(uint32_t w) {
     return f32x2{f[0], f[1]};
 }
 
-// The same codes as a pair of bf16 in one word: an fp8 value is exact in
-// bf16, so the upper halves of its fp32 decode are its bf16 bits.
+// The same codes as a pair of bf16 in one word, in one conversion (an fp8
+// value is exact in bf16, and the conversion's scale is one).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8_pair_bf16(uint32_t w) {
-    const f32x2 f = fp8_pair<HI>(w);
-    return pack_halves<true>(__float_as_uint(f[0]), __float_as_uint(f[1]));
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 
 template <int NB, bool NT>
