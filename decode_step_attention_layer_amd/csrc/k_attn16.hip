@@ -14,7 +14,8 @@
 //   O^T[dim][head]  += sum_t V[t][dim] P[t][head]        (2 x HD/16 per 32 tokens)
 // with the group's heads in the 16 columns (padding columns repeat the last
 // head and are never read). K and V enter exactly: bf16 values as stored,
-// fp8 E4M3 codes decoded to bf16 (their 3-bit significands fit), the scales
+// fp8 E4M3 codes decoded to bf16 (their 3-bit significands fit; K codes by
+// the hardware's fp8-to-bf16 pair conversion, V codes through fp32), the scales
 // applied to q (k_scale) and to the chunk's output (v_scale). q (scaled to
 // log2 units) and the probabilities P enter as two bf16 terms each, a high
 // part and the bf16 of the remainder (for bf16 caches never zero, see
