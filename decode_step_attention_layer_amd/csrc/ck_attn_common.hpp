@@ -527,25 +527,35 @@ __device__ __forceinline__ bool attn_item(const AttnArgs &a, int item, int g,
 // states are combined through LDS as above. A workgroup has one wave per
 // 16-token tile of its chunk (at most 8; longer chunks give a wave every
 // NW-th tile).
-template <int HD, int G, int NW>
+template <int HD, int G, int NW, int HF = 1>
 struct alignas(16) SmemM {
     float ro[NW][G][HD + 4];
     float rm[NW][G];
     float rl[NW][G];
+    alignas(16) float sx[HF == 2 ? NW : 1][HF][kWave][4];   // HF = 2: the halves' partial scores
     int pages[kPagesLds];
     int bad;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int HD, int G, int NW, bool PAGED, bool STREAM, bool COH>
+//
+// HF = 2 (128-wide heads, chunks of at most NW tiles): two waves per tile,
+// wave hf contracting head dims [64hf, 64hf + 64) for the scores (the two
+// partial score tiles are added through LDS, in the same order in both
+// waves) and producing those output dims of P V, so each wave issues half
+// the MFMAs after its loads land. Every wave takes exactly one tile (a
+// tile past the chunk is fully masked), so the exchange's barrier is
+// reached by all.
+template <int HD, int G, int NW, bool PAGED, bool STREAM, bool COH, int HF = 1>
 __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int g,
-                                               SmemM<HD, G, NW> &sm) {
+                                               SmemM<HD, G, NW, HF> &sm) {
     static_assert(HD == 64 || HD == 128, "head size");
     static_assert(G >= 1 && G <= 16 && NW >= 1 && NW <= 8, "query group, waves");
-    constexpr int NT = NW * kWave;
-    constexpr int KD = HD / 4;      // dims of a K row per lane (one per MFMA step)
-    constexpr int VD = HD / 16;     // dims of a V row per lane; output tiles
+    static_assert(HF == 1 || (HF == 2 && HD == 128), "dim halves");
+    constexpr int NT = NW * HF * kWave;
+    constexpr int KD = HD / 4 / HF;   // dims of a K row per lane (one per MFMA step)
+    constexpr int VD = HD / 16 / HF;  // dims of a V row per lane; output tiles
     int s = 0;
     while (s + 1 < a.m && item >= a.first[s + 1]) s++;
     const int cidx = item - a.first[s];
@@ -555,7 +565,8 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
     const int t1 = min(L, t0 + a.chunk);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wid % NW, hf = wid / NW;    // tile wave, dim half
     const int hl = lane & 15, kq = lane >> 4;
     const int KV = a.c.kv_heads;
 
@@ -573,6 +584,7 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
     }
     __syncthreads();
     const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
+    const int d0 = hf * (HD / HF);               // the half's first head dim
     const int slot0 = (!PAGED && a.c.ring) ? t0 % a.c.capacity : t0;
     bool bad = false;
     auto row_off = [&](int t) -> long long {
@@ -616,7 +628,7 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
     // loads go out.
     float qr[KD];
     {
-        const float *qh = a.q + ((size_t)s * a.H + (size_t)g * G + min(hl, G - 1)) * HD + 4 * kq;
+        const float *qh = a.q + ((size_t)s * a.H + (size_t)g * G + min(hl, G - 1)) * HD + d0 + 4 * kq;
 #pragma unroll
         for (int i = 0; i < KD; i += 4) {
             const float4 v = *reinterpret_cast<const float4 *>(qh + 4 * i);
@@ -633,7 +645,9 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
 #pragma unroll
     for (int T = 0; T < VD; T++) o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int ntile = (t1 - t0 + 15) / 16;
-    for (int tile = wave; tile < ntile; tile += NW) {
+    // HF = 2: one pass for every wave (the launcher keeps a chunk within NW
+    // tiles; a tile past the chunk reads its last row, fully masked)
+    for (int tile = wave; HF == 2 ? tile == wave : tile < ntile; tile += NW) {
         const int tb = t0 + 16 * tile;
         // every load first, unconditional (tokens past the chunk re-read its
         // last row and are masked). K of token tb + hl: the four lanes of a
@@ -643,7 +657,7 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         // 4 rows per instruction.
         float kr[KD];
         {
-            const float *kp = Kc + row_off(min(tb + hl, t1 - 1)) + 4 * kq;
+            const float *kp = Kc + row_off(min(tb + hl, t1 - 1)) + d0 + 4 * kq;
 #pragma unroll
             for (int i = 0; i < KD; i += 4) {
                 const float4 v = ld4(kp + 4 * i);
@@ -656,7 +670,7 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         float vr[4][VD];
 #pragma unroll
         for (int sidx = 0; sidx < 4; sidx++) {
-            const float *vp = Vc + row_off(min(tb + 4 * kq + sidx, t1 - 1)) + 4 * hl;
+            const float *vp = Vc + row_off(min(tb + 4 * kq + sidx, t1 - 1)) + d0 + 4 * hl;
 #pragma unroll
             for (int T = 0; T < VD; T += 4) {
                 const float4 v = ld4(vp + 16 * T);
@@ -672,6 +686,14 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < KD; i++) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i], qr[i], sc, 0, 0, 0);
+        if constexpr (HF == 2) {
+            // the whole dot: half 0's partial plus half 1's, in both waves
+            *reinterpret_cast<f32x4 *>(sm.sx[wave][hf][lane]) = sc;
+            __syncthreads();
+            const f32x4 p0 = *reinterpret_cast<const f32x4 *>(sm.sx[wave][0][lane]);
+            const f32x4 p1 = *reinterpret_cast<const f32x4 *>(sm.sx[wave][1][lane]);
+            sc = p0 + p1;
+        }
         float sv[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) sv[r] = (tb + 4 * kq + r < t1) ? sc[r] * qs : -INFINITY;
@@ -715,9 +737,9 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         for (int r = 0; r < 4; r++)
 #pragma unroll
             for (int T = 0; T < VD; T += 4)
-                *reinterpret_cast<float4 *>(&sm.ro[wave][hl][16 * T + 16 * kq + 4 * r]) =
+                *reinterpret_cast<float4 *>(&sm.ro[wave][hl][d0 + 16 * T + 16 * kq + 4 * r]) =
                     make_float4(o[T][r], o[T + 1][r], o[T + 2][r], o[T + 3][r]);
-        if (kq == 0) {
+        if (kq == 0 && hf == 0) {
             sm.rm[wave][hl] = m_run;
             sm.rl[wave][hl] = l_run;
         }

@@ -59,23 +59,25 @@ __global__ __launch_bounds__(AttnShape<G>::threads) void k_attn(AttnArgs a) {
 
 // The same on the fp32 matrix cores (query groups of 5 to 8 heads, fp32
 // cache, no selection): same grid, same partials.
-template <int HD, int G, int NW, bool PAGED, bool STREAM>
-__global__ __launch_bounds__(NW * kWave) void k_attn_mfma(AttnArgs a) {
-    __shared__ SmemM<HD, G, NW> sm;
-    attn_item_mfma<HD, G, NW, PAGED, STREAM, false>(a, blockIdx.x, blockIdx.y, sm);
+template <int HD, int G, int NW, bool PAGED, bool STREAM, int HF>
+__global__ __launch_bounds__(NW * HF * kWave) void k_attn_mfma(AttnArgs a) {
+    __shared__ SmemM<HD, G, NW, HF> sm;
+    attn_item_mfma<HD, G, NW, PAGED, STREAM, false, HF>(a, blockIdx.x, blockIdx.y, sm);
 }
 
 constexpr int kMfmaMaxWaves = 8;
 
 // One wave per 16-token tile of a chunk, at most eight (longer chunks give a
-// wave every eighth tile). 128-wide heads stream their rows only from chunks
-// of kNtChunk tokens (see launch_t), which take eight waves.
-template <int HD, int G, int NW>
+// wave every eighth tile); 128-wide heads in chunks of at most eight tiles
+// take two waves per tile, one per half of the head dims. 128-wide heads
+// stream their rows only from chunks of kNtChunk tokens (see launch_t),
+// which take eight waves.
+template <int HD, int G, int NW, int HF = (HD == 128 ? 2 : 1)>
 void launch_mfma_nw(const AttnArgs &a, dim3 grid, bool paged, hipStream_t st) {
     constexpr bool NT = HD == 64;
-    const dim3 blk(NW * kWave);
-    if (paged) hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, true, NT>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, false, NT>), grid, blk, 0, st, a);
+    const dim3 blk(NW * HF * kWave);
+    if (paged) hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, true, NT, HF>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<HD, G, NW, false, NT, HF>), grid, blk, 0, st, a);
 }
 
 template <int HD, int G>
@@ -84,9 +86,11 @@ void launch_mfma(const AttnArgs &a, dim3 grid, bool paged, bool nt, hipStream_t 
     if (HD == 128 && nt) {
         const dim3 blk(kMfmaMaxWaves * kWave);
         if (paged)
-            hipLaunchKernelGGL((k_attn_mfma<HD, G, kMfmaMaxWaves, true, true>), grid, blk, 0, st, a);
+            hipLaunchKernelGGL((k_attn_mfma<HD, G, kMfmaMaxWaves, true, true, 1>), grid, blk, 0, st,
+                               a);
         else
-            hipLaunchKernelGGL((k_attn_mfma<HD, G, kMfmaMaxWaves, false, true>), grid, blk, 0, st, a);
+            hipLaunchKernelGGL((k_attn_mfma<HD, G, kMfmaMaxWaves, false, true, 1>), grid, blk, 0,
+                               st, a);
         return;
     }
     switch (tiles < kMfmaMaxWaves ? tiles : kMfmaMaxWaves) {
@@ -97,7 +101,11 @@ void launch_mfma(const AttnArgs &a, dim3 grid, bool paged, bool nt, hipStream_t 
         case 5: launch_mfma_nw<HD, G, 5>(a, grid, paged, st); break;
         case 6: launch_mfma_nw<HD, G, 6>(a, grid, paged, st); break;
         case 7: launch_mfma_nw<HD, G, 7>(a, grid, paged, st); break;
-        default: launch_mfma_nw<HD, G, 8>(a, grid, paged, st); break;
+        default:
+            // over eight tiles a wave takes several: one wave per tile
+            if (tiles > kMfmaMaxWaves) launch_mfma_nw<HD, G, 8, 1>(a, grid, paged, st);
+            else launch_mfma_nw<HD, G, 8>(a, grid, paged, st);
+            break;
     }
 }
 
