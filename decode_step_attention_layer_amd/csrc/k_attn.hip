@@ -124,9 +124,11 @@ struct MergeArgs {
 
 // The Q8_0 of output elements 4*e4.. of (sequence s, head h) (every lane of
 // the block's group of 8 calling), into out_q8 and the image; the image's
-// zero scales of the head's blocks written by its sequence-0 workgroup.
+// zero scales of blocks [pb0, pb1) written by the sequence-0 workgroup's
+// lanes (lane ptid of pn).
 template <int HD>
-__device__ __forceinline__ void merge_q8_out(const MergeArgs &a, float4 v, int s, int h, int e4) {
+__device__ __forceinline__ void merge_q8_out(const MergeArgs &a, float4 v, int s, int h, int e4,
+                                             int pb0, int pb1, int ptid, int pn) {
     const size_t oi = ((size_t)s * a.H + h) * HD + 4 * e4;
     uint32_t packed;
     uint16_t dbits;
@@ -138,7 +140,7 @@ __device__ __forceinline__ void merge_q8_out(const MergeArgs &a, float4 v, int s
     if ((e4 & 7) == 0) *reinterpret_cast<uint16_t *>(blk) = dbits;
     if (a.xi.base) {
         ximage_put(a.xi, s, (h * HD + 4 * e4) / kQK, e4 & 7, packed, dbits);
-        if (s == 0) ximage_zero_pads(a.xi, h * HD / kQK, (h + 1) * HD / kQK, e4, HD / 4);
+        if (s == 0) ximage_zero_pads(a.xi, pb0, pb1, ptid, pn);
     }
 }
 
@@ -266,30 +268,37 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(MergeArgs a) {
         const float4 v = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
         const size_t oi = ((size_t)s * a.H + h) * HD + 4 * tid;
         *reinterpret_cast<float4 *>(&a.out[oi]) = v;
-        if (a.out_q8) merge_q8_out<HD>(a, v, s, h, tid);
+        if (a.out_q8)
+            merge_q8_out<HD>(a, v, s, h, tid, h * HD / kQK, (h + 1) * HD / kQK, tid, HD / 4);
     }
 }
 
-// The merge for sequences of at most kMerge1Chunks chunks: one wavefront per
-// (head, sequence), no LDS and no barrier. A chunk's output row is held by
-// HD/4 lanes (4 values each); the chunks are dealt round-robin to the
-// 64 / (HD/4) lane groups. Every load goes out at once and none is
-// conditional (a slot past the last chunk re-reads the last one and is not
-// used): lane c's chunk (max, sum) pair, then the lane's output slices. The
-// global max and the denominator are wave reductions; each chunk's weight
-// is computed by lane c and read from it into scalar registers; the lane
-// groups' sums are combined with cross-lane exchanges.
+// The merge for sequences of at most kMerge1Chunks chunks per wavefront: a
+// workgroup per (head, sequence, DQ output dims), no barrier with one
+// wavefront. A chunk's DQ dims are held by DQ/4 lanes (4 values each); the
+// chunks are dealt round-robin to the 64 / (DQ/4) lane groups. Every load
+// goes out at once and none is conditional (a slot past the last chunk
+// re-reads the last one and is not used): lane c's chunk (max, sum) pair,
+// then (DQ = 32) the pairs of the lane's own slots, then the lane's output
+// slices. The global max and the denominator are wave reductions; with DQ
+// = 32 each lane weighs its own 4 slots, with whole heads (DQ = HD, where
+// the grid already fills the GPU) each chunk's weight is computed by lane c
+// and read from it into scalar registers; the lane groups' sums are
+// combined with cross-lane exchanges.
 constexpr int kMerge1Chunks = 32;   // chunks per wavefront
 
 // NWV wavefronts: wave w merges chunks [32w, 32w + 32) as above into its own
 // (max, denominator, weighted sum); with two waves the states are combined by
 // log-sum-exp through LDS after one barrier.
-template <int HD, int NWV>
+template <int HD, int NWV, int DQ>
 __global__ __launch_bounds__(kWave * NWV) void k_attn_merge1(MergeArgs a) {
-    constexpr int LG = HD / 4;                 // lanes per chunk group
+    static_assert(DQ == 32 || DQ == HD, "output dims per workgroup");
+    constexpr bool SPLIT = DQ < HD;            // each lane weighs its own slots
+    constexpr int LG = DQ / 4;                 // lanes per chunk group
     constexpr int NGRP = kWave / LG;           // chunk groups
     constexpr int PER = kMerge1Chunks / NGRP;  // chunk slots per lane
     const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x & (kWave - 1);
+    const int dq = blockIdx.z * DQ;            // this workgroup's first output dim
     const int wave = NWV > 1 ? (int)(threadIdx.x >> 6) : 0;
     const int G = a.H / a.KV, g = h / G, j = h % G;
     const int L = a.pos.get(s) + 1;
@@ -304,11 +313,19 @@ __global__ __launch_bounds__(kWave * NWV) void k_attn_merge1(MergeArgs a) {
 
     const float2 ml =
         *reinterpret_cast<const float2 *>(&a.pml[((base + min(c0 + lane, ncl)) * G + j) * 2]);
+    float2 mls[SPLIT ? PER : 1];
     float4 ov[PER];
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int c = min(c0 + grp + NGRP * i, ncl);
+            mls[i] = *reinterpret_cast<const float2 *>(&a.pml[((base + c) * G + j) * 2]);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < PER; i++) {
         const int c = min(c0 + grp + NGRP * i, ncl);
-        ov[i] = *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + 4 * d4]);
+        ov[i] = *reinterpret_cast<const float4 *>(&a.po[((base + c) * G + j) * HD + dq + 4 * d4]);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -325,13 +342,19 @@ __global__ __launch_bounds__(kWave * NWV) void k_attn_merge1(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; i++) {
         const int c = grp + NGRP * i;
-        // chunk c's weight: read from lane c into a scalar register (the
-        // lane index is a constant per group), no wait on a permute
-        float wc = readlane_f(w, NGRP * i);
+        float wc;
+        if constexpr (SPLIT) {
+            // the slot's weight, as lane c computed it for the denominator
+            wc = exp2f(mls[i].x - Mr);
+        } else {
+            // chunk c's weight: read from lane c into a scalar register (the
+            // lane index is a constant per group), no wait on a permute
+            wc = readlane_f(w, NGRP * i);
 #pragma unroll
-        for (int q = 1; q < NGRP; q++) {
-            const float t = readlane_f(w, NGRP * i + q);
-            wc = grp == q ? t : wc;
+            for (int q = 1; q < NGRP; q++) {
+                const float t = readlane_f(w, NGRP * i + q);
+                wc = grp == q ? t : wc;
+            }
         }
         if (c < nc)
             acc = make_float4(fmaf(wc, ov[i].x, acc.x), fmaf(wc, ov[i].y, acc.y),
@@ -378,9 +401,11 @@ __global__ __launch_bounds__(kWave * NWV) void k_attn_merge1(MergeArgs a) {
         // (a chunk that read an unmapped or unheld row) stays NaN
         const float inv = D == 0.0f ? 0.0f : 1.0f / D;
         const float4 v = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-        const size_t oi = ((size_t)s * a.H + h) * HD + 4 * d4;
+        const size_t oi = ((size_t)s * a.H + h) * HD + dq + 4 * d4;
         *reinterpret_cast<float4 *>(&a.out[oi]) = v;
-        if (a.out_q8) merge_q8_out<HD>(a, v, s, h, d4);
+        if (a.out_q8)
+            merge_q8_out<HD>(a, v, s, h, dq / 4 + d4, (h * HD + dq) / kQK,
+                             (h * HD + dq + DQ) / kQK, d4, LG);
     }
 }
 
@@ -612,8 +637,19 @@ hipError_t launch_attn_merge(const void *partials, const Positions &pos, int win
     // slower: its serial loads cost more than the barriers save); beyond,
     // the workgroup merge
     const int nwv = (plan.nchunks + kMerge1Chunks - 1) / kMerge1Chunks;
+    // a workgroup per 32 output dims while that keeps within one per CU (7B
+    // shape: 24.87 against 25.29 us per layer; a batch of 8, whose heads
+    // already fill the GPU, measured slower split)
+    const bool split = (long long)H * m * (hd / 32) <= cus_of_current_device();
 #define CK_MERGE1(HD_, NWV_) \
-    hipLaunchKernelGGL((k_attn_merge1<HD_, NWV_>), dim3(H, m), dim3(NWV_ * kWave), 0, st, b)
+    do {                                                                                        \
+        if (split)                                                                              \
+            hipLaunchKernelGGL((k_attn_merge1<HD_, NWV_, 32>), dim3(H, m, HD_ / 32),            \
+                               dim3(NWV_ * kWave), 0, st, b);                                   \
+        else                                                                                    \
+            hipLaunchKernelGGL((k_attn_merge1<HD_, NWV_, HD_>), dim3(H, m), dim3(NWV_ * kWave), \
+                               0, st, b);                                                       \
+    } while (0)
     if (nwv <= 4) {
         if (hd == 64) {
             if (nwv <= 1) CK_MERGE1(64, 1);

@@ -208,7 +208,9 @@ def test_layer_c5(variant):
 
 # Other batches of the paged path: the matrix-core projections from 4 tokens,
 # the activation images' zero token slots from m to 15, the Q/K/V epilogue at
-# other head counts and widths.
+# other head counts and widths; b4s is small enough (heads x tokens x 32-dim
+# parts within the compute units) for the merge to split heads over 32-dim
+# workgroups while it writes the O projection's activation image.
 BATCHES = {
     "b4": synth.Config("b4", 21, 3584, 28, 4, 128, 1e4, layers=1, m=4, page_size=16,
                        min_ctx=100, max_ctx=900),
@@ -216,6 +218,8 @@ BATCHES = {
                        min_ctx=64, max_ctx=700),
     "b12": synth.Config("b12", 23, 896, 14, 2, 64, 1e4, layers=2, m=12, page_size=16,
                         min_ctx=30, max_ctx=300),
+    "b4s": synth.Config("b4s", 24, 512, 8, 2, 64, 1e4, layers=2, m=4, page_size=16,
+                        min_ctx=20, max_ctx=200),
 }
 
 
