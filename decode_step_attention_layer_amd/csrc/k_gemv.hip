@@ -235,11 +235,13 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
     }
 }
 
-constexpr int kRowsIter = 2;
-
-template <int LPR, int UPL, bool PAIRED>
+// Rows per wave and iteration: 2, or 1 where 2 would leave compute units
+// without a workgroup (the Qwen2-0.5B-shaped O projection, 28 workgroups
+// against 56: 15.6 against 16.1 us per layer; at the 7B and long-context
+// shapes, 448 and 512 workgroups, one row measured the same or slower).
+template <int LPR, int UPL, bool PAIRED, int R>
 hipError_t launch_t(GemvArgs a, hipStream_t st) {
-    const int rows_per_wg = kGemvWaves * (kWave / LPR) * kRowsIter;
+    const int rows_per_wg = kGemvWaves * (kWave / LPR) * R;
     int total = 0;
     for (int i = 0; i < a.nseg; i++) {
         a.seg[i].wg_begin = total;
@@ -248,19 +250,28 @@ hipError_t launch_t(GemvArgs a, hipStream_t st) {
     for (int i = a.nseg; i < 3; i++) a.seg[i] = a.seg[0], a.seg[i].wg_begin = 1 << 30;
     const size_t lds = sizeof(XBlock) * (size_t)a.m * (a.K / kQK);
     if (a.m == 1 && a.K / kQK <= kGemvThreads)
-        hipLaunchKernelGGL((k_gemv<LPR, UPL, kRowsIter, PAIRED, true>), dim3(total),
+        hipLaunchKernelGGL((k_gemv<LPR, UPL, R, PAIRED, true>), dim3(total),
                            dim3(kGemvThreads), lds, st, a);
     else
-        hipLaunchKernelGGL((k_gemv<LPR, UPL, kRowsIter, PAIRED, false>), dim3(total),
+        hipLaunchKernelGGL((k_gemv<LPR, UPL, R, PAIRED, false>), dim3(total),
                            dim3(kGemvThreads), lds, st, a);
     return hipGetLastError();
 }
 
+template <int LPR, bool PAIRED, int R>
+hipError_t launch_upl_r(const GemvArgs &a, int upl, hipStream_t st) {
+    if (upl <= 1) return launch_t<LPR, 1, PAIRED, R>(a, st);
+    if (upl <= 2) return launch_t<LPR, 2, PAIRED, R>(a, st);
+    return launch_t<LPR, 4, PAIRED, R>(a, st);
+}
+
 template <int LPR, bool PAIRED>
 hipError_t launch_upl(const GemvArgs &a, int upl, hipStream_t st) {
-    if (upl <= 1) return launch_t<LPR, 1, PAIRED>(a, st);
-    if (upl <= 2) return launch_t<LPR, 2, PAIRED>(a, st);
-    return launch_t<LPR, 4, PAIRED>(a, st);
+    const int rows_per_wg2 = kGemvWaves * (kWave / LPR) * 2;
+    int total2 = 0;
+    for (int i = 0; i < a.nseg; i++) total2 += (a.seg[i].rows + rows_per_wg2 - 1) / rows_per_wg2;
+    if (total2 < num_cus()) return launch_upl_r<LPR, PAIRED, 1>(a, upl, st);
+    return launch_upl_r<LPR, PAIRED, 2>(a, upl, st);
 }
 
 template <bool PAIRED>
