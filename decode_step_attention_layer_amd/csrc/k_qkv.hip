@@ -218,14 +218,27 @@ hipError_t launch_t(QkvArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int LPR, bool PAIRED>
-hipError_t launch_upl(const QkvArgs &a, int upl, hipStream_t st) {
-    // rows per wave: 2 (a RoPE pair), so that the workgroups are small and
-    // many; each CU's share of the weights, not the total, sets the time
-    constexpr int R = 2;
+template <int LPR, bool PAIRED, int R>
+hipError_t launch_upl_r(const QkvArgs &a, int upl, hipStream_t st) {
     if (upl <= 1) return launch_t<LPR, 1, R, PAIRED>(a, st);
     if (upl <= 2) return launch_t<LPR, 2, R, PAIRED>(a, st);
     return launch_t<LPR, 4, R, PAIRED>(a, st);
+}
+
+template <int LPR, bool PAIRED>
+hipError_t launch_upl(const QkvArgs &a, int upl, hipStream_t st) {
+    // rows per wave and iteration: 2 (a RoPE pair when a row spans the
+    // wave), so that the workgroups are small and many, each CU's share of
+    // the weights, not the total, setting the time (four rows measured
+    // slower at the 7B shape); 1 where rows narrower than the wave pair up
+    // across lane groups and 2 would leave compute units without a
+    // workgroup
+    if constexpr (LPR < kWave) {
+        const int per2 = kGemvWaves * (kWave / LPR) * 2;
+        const int total2 = (a.H * a.hd + per2 - 1) / per2 + 2 * ((a.KV * a.hd + per2 - 1) / per2);
+        if (total2 < num_cus()) return launch_upl_r<LPR, PAIRED, 1>(a, upl, st);
+    }
+    return launch_upl_r<LPR, PAIRED, 2>(a, upl, st);
 }
 
 template <bool PAIRED>
