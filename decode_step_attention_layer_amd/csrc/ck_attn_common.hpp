@@ -529,9 +529,12 @@ __device__ __forceinline__ bool attn_item(const AttnArgs &a, int item, int g,
 // NW-th tile).
 template <int HD, int G, int NW, int HF = 1>
 struct alignas(16) SmemM {
-    float ro[NW][G][HD + 4];
-    float rm[NW][G];
-    float rl[NW][G];
+    // wave states: one per tile wave, or per wave where the two waves of a
+    // tile split its tokens (HF = 2 with 64-wide heads)
+    static constexpr int NST = (HF == 2 && HD == 64) ? 2 * NW : NW;
+    float ro[NST][G][HD + 4];
+    float rm[NST][G];
+    float rl[NST][G];
     alignas(16) float sx[HF == 2 ? NW : 1][HF][kWave][4];   // HF = 2: the halves' partial scores
     int pages[kPagesLds];
     int bad;
@@ -540,22 +543,27 @@ struct alignas(16) SmemM {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 //
-// HF = 2 (128-wide heads, chunks of at most NW tiles): two waves per tile,
-// wave hf contracting head dims [64hf, 64hf + 64) for the scores (the two
+// HF = 2 (chunks of at most NW tiles): two waves per tile, wave hf
+// contracting head dims [hf HD/2, (hf + 1) HD/2) for the scores (the two
 // partial score tiles are added through LDS, in the same order in both
-// waves) and producing those output dims of P V, so each wave issues half
-// the MFMAs after its loads land. Every wave takes exactly one tile (a
-// tile past the chunk is fully masked), so the exchange's barrier is
-// reached by all.
+// waves), so each wave issues half the score MFMAs after its loads land.
+// P V: with 128-wide heads wave hf produces those output dims; with 64-wide
+// heads (a single 64-dim output tile group, which 16-byte V loads cannot
+// split) it contracts half of the tile's tokens (steps 2hf, 2hf + 1) and the
+// two waves' sums are added as two states with the same max. Every wave
+// takes exactly one tile (a tile past the chunk is fully masked), so the
+// exchange's barrier is reached by all.
 template <int HD, int G, int NW, bool PAGED, bool STREAM, bool COH, int HF = 1>
 __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int g,
                                                SmemM<HD, G, NW, HF> &sm) {
     static_assert(HD == 64 || HD == 128, "head size");
     static_assert(G >= 1 && G <= 16 && NW >= 1 && NW <= 8, "query group, waves");
-    static_assert(HF == 1 || (HF == 2 && HD == 128), "dim halves");
+    static_assert(HF == 1 || HF == 2, "dim halves");
+    constexpr bool TSPLIT = HF == 2 && HD == 64;   // P V split over tokens
     constexpr int NT = NW * HF * kWave;
     constexpr int KD = HD / 4 / HF;   // dims of a K row per lane (one per MFMA step)
-    constexpr int VD = HD / 16 / HF;  // dims of a V row per lane; output tiles
+    constexpr int VD = TSPLIT ? HD / 16 : HD / 16 / HF;   // V dims per lane; output tiles
+    constexpr int NVR = TSPLIT ? 2 : 4;                   // V rows per lane (P V steps)
     int s = 0;
     while (s + 1 < a.m && item >= a.first[s + 1]) s++;
     const int cidx = item - a.first[s];
@@ -585,6 +593,8 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
     __syncthreads();
     const size_t seq_base = PAGED ? 0 : ((size_t)s * KV + g) * a.c.capacity * HD;
     const int d0 = hf * (HD / HF);               // the half's first head dim
+    const int dv0 = TSPLIT ? 0 : d0;             // its first output dim
+    const int sv0 = TSPLIT ? 2 * hf : 0;         // its first P V step
     const int slot0 = (!PAGED && a.c.ring) ? t0 % a.c.capacity : t0;
     bool bad = false;
     auto row_off = [&](int t) -> long long {
@@ -667,17 +677,18 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
                 kr[i + 3] = v.w;
             }
         }
-        float vr[4][VD];
+        float vr[NVR][VD];
 #pragma unroll
-        for (int sidx = 0; sidx < 4; sidx++) {
-            const float *vp = Vc + row_off(min(tb + 4 * kq + sidx, t1 - 1)) + d0 + 4 * hl;
+        for (int sv = 0; sv < NVR; sv++) {
+            const int sidx = sv0 + sv;
+            const float *vp = Vc + row_off(min(tb + 4 * kq + sidx, t1 - 1)) + dv0 + 4 * hl;
 #pragma unroll
             for (int T = 0; T < VD; T += 4) {
                 const float4 v = ld4(vp + 16 * T);
-                vr[sidx][T] = v.x;
-                vr[sidx][T + 1] = v.y;
-                vr[sidx][T + 2] = v.z;
-                vr[sidx][T + 3] = v.w;
+                vr[sv][T] = v.x;
+                vr[sv][T + 1] = v.y;
+                vr[sv][T + 2] = v.z;
+                vr[sv][T + 3] = v.w;
             }
         }
         // keep the loads together ahead of the arithmetic (left alone, the
@@ -716,32 +727,35 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         // V of a token past the chunk adds nothing (it re-reads a row that
         // may hold anything, an infinity included)
 #pragma unroll
-        for (int sidx = 0; sidx < 4; sidx++) {
-            const bool ok = tb + 4 * kq + sidx < t1;
+        for (int sv = 0; sv < NVR; sv++) {
+            const bool ok = tb + 4 * kq + sv0 + sv < t1;
 #pragma unroll
-            for (int T = 0; T < VD; T++) vr[sidx][T] = ok ? vr[sidx][T] : 0.0f;
+            for (int T = 0; T < VD; T++) vr[sv][T] = ok ? vr[sv][T] : 0.0f;
         }
 #pragma unroll
         for (int T = 0; T < VD; T++) {
             o[T] *= alpha;
 #pragma unroll
-            for (int sidx = 0; sidx < 4; sidx++)
-                o[T] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[sidx][T], p[sidx], o[T], 0, 0, 0);
+            for (int sv = 0; sv < NVR; sv++)
+                o[T] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[sv][T], p[sv0 + sv], o[T], 0, 0, 0);
         }
     }
 
     // the waves' states through LDS: o[4b + e][r] is dim 64b + 16kq + 4r + e
+    // (token halves: each wave its own state, the same max, the sum once)
+    constexpr int NST = SmemM<HD, G, NW, HF>::NST;
+    const int st = TSPLIT ? 2 * wave + hf : wave;
     if (bad) sm.bad = 1;
     if (hl < G) {
 #pragma unroll
         for (int r = 0; r < 4; r++)
 #pragma unroll
             for (int T = 0; T < VD; T += 4)
-                *reinterpret_cast<float4 *>(&sm.ro[wave][hl][d0 + 16 * T + 16 * kq + 4 * r]) =
+                *reinterpret_cast<float4 *>(&sm.ro[st][hl][dv0 + 16 * T + 16 * kq + 4 * r]) =
                     make_float4(o[T][r], o[T + 1][r], o[T + 2][r], o[T + 3][r]);
-        if (kq == 0 && hf == 0) {
-            sm.rm[wave][hl] = m_run;
-            sm.rl[wave][hl] = l_run;
+        if (kq == 0 && (TSPLIT || hf == 0)) {
+            sm.rm[st][hl] = m_run;
+            sm.rl[st][hl] = hf == 0 ? l_run : 0.0f;
         }
     }
     __syncthreads();
@@ -755,12 +769,12 @@ __device__ __forceinline__ bool attn_item_mfma(const AttnArgs &a, int item, int 
         const int j = i4 / (HD / 4), c = 4 * (i4 % (HD / 4));
         float M = sm.rm[0][j];
 #pragma unroll
-        for (int w = 1; w < NW; w++) M = fmaxf(M, sm.rm[w][j]);
+        for (int w = 1; w < NST; w++) M = fmaxf(M, sm.rm[w][j]);
         const float Mr = M == -INFINITY ? 0.0f : M;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         float ls = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; w++) {
+        for (int w = 0; w < NST; w++) {
             const float wt = exp2f(sm.rm[w][j] - Mr);
             ls = fmaf(sm.rl[w][j], wt, ls);
             const float4 v = *reinterpret_cast<const float4 *>(&sm.ro[w][j][c]);

@@ -68,11 +68,11 @@ __global__ __launch_bounds__(NW * HF * kWave) void k_attn_mfma(AttnArgs a) {
 constexpr int kMfmaMaxWaves = 8;
 
 // One wave per 16-token tile of a chunk, at most eight (longer chunks give a
-// wave every eighth tile); 128-wide heads in chunks of at most eight tiles
-// take two waves per tile, one per half of the head dims. 128-wide heads
+// wave every eighth tile); chunks of at most eight tiles take two waves per
+// tile, one per half of the head dims for the scores. 128-wide heads
 // stream their rows only from chunks of kNtChunk tokens (see launch_t),
 // which take eight waves.
-template <int HD, int G, int NW, int HF = (HD == 128 ? 2 : 1)>
+template <int HD, int G, int NW, int HF = 2>
 void launch_mfma_nw(const AttnArgs &a, dim3 grid, bool paged, hipStream_t st) {
     constexpr bool NT = HD == 64;
     const dim3 blk(NW * HF * kWave);
