@@ -32,10 +32,12 @@
 // an fp32 cache (no selection) take the same grid and partials on the fp32
 // matrix cores (k_attn_mfma): per 16-token tile, the scores of the whole
 // group and the value sums are 16x16x4 MFMA contractions, one wave per tile
-// of the chunk (at most eight). A second
-// kernel, one workgroup per (head, sequence) (one wavefront per 32 chunks
-// where a sequence has at most 128), merges the chunks by log-sum-exp with all
-// chunks' loads in flight at once (the sink joins here), writes the attention
+// of the chunk (at most eight; two per tile, each taking half of the work,
+// where the chunk has at most eight tiles). A second kernel, one workgroup
+// per (head, sequence) (one wavefront per 32 chunks where a sequence has at
+// most 128, and then a workgroup per 32 output dims while the grid leaves
+// compute units free), merges the chunks by log-sum-exp with all chunks'
+// loads in flight at once (the sink joins here), writes the attention
 // output and, optionally, its Q8_0 blocks. (Merging inside the first kernel
 // by the last workgroup to finish needs an agent-scope release per
 // workgroup, an L2 write-back on this GPU; measured, it cost more than the
